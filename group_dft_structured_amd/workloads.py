@@ -1,0 +1,78 @@
+"""Seeded synthetic workloads for the p4 EQ-Linear layer.
+
+This module holds the workload shapes and the seeded input generators, and
+nothing of the layer's arithmetic.  It is the one module shared by the oracle
+tests and the HIP path's tests and bench.
+
+The shapes stand in for the linear layers of the equivariant vision models the
+Flash EQ-Linear paper accelerates (gist.science summary, "Livello di Rete":
+Flash EQ-ViT / Flash EQ-Swin).  The paper's own operator shapes are not given,
+so ViT-S-like (64 images x 197 tokens, 384 features) and Swin-like
+(64 images x 56 x 56 tokens, 768 features) layers are used, with C and D
+counted per group element (a row holds C*T input and D*T output features).
+
+Drawing rule: numpy PCG64 seeded with ``seed``, draws in the order x, W, bias,
+dy, each in fp64, then cast to fp32 and, for fp16 runs, from fp32 to fp16 with
+round-to-nearest-even.  The second parameter of every normal distribution is a
+variance: x, dy ~ N(0, 1); W ~ N(0, 1/(C*T)) (fan-in scaling); bias ~ N(0, 0.02).
+"""
+from dataclasses import dataclass
+import numpy as np
+
+T_P4 = 4
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    N: int
+    C: int
+    D: int
+    T: int
+    dtypes: tuple
+    bias: bool
+    passes: tuple  # subset of ("forward", "backward")
+    desc: str
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 64, 8, 8, T_P4, ("f32",), False, ("forward",),
+                     "tiny p4 layer, 32->32 features"),
+    "vit_s_proj": Workload("vit_s_proj", 12608, 96, 96, T_P4, ("f32", "f16"), True, ("forward",),
+                           "ViT-S-like projection, 64 images x 197 tokens, 384->384 features"),
+    "vit_s_mlp": Workload("vit_s_mlp", 12608, 96, 384, T_P4, ("f16",), True, ("forward",),
+                          "ViT-S-like MLP expansion, 64 images x 197 tokens, 384->1536 features"),
+    "swin_stage": Workload("swin_stage", 200704, 192, 768, T_P4, ("f16", "f32"), True, ("forward",),
+                           "Swin-like stage, 64 images x 56x56 tokens, 768->3072 features"),
+    "vit_s_mlp_bwd": Workload("vit_s_mlp_bwd", 12608, 96, 384, T_P4, ("f16",), True, ("backward",),
+                              "backward of the ViT-S-like MLP expansion (dX, dW, dbias)"),
+}
+
+_NP_DTYPE = {"f32": np.float32, "f16": np.float16}
+
+
+def _cast(a, dtype):
+    a32 = a.astype(np.float32)
+    return a32 if dtype == "f32" else a32.astype(np.float16)
+
+
+def make_inputs(C, D, N, T=T_P4, dtype="f32", seed=0, bias=True, dy=False):
+    """Seeded synthetic tensors {x, W, bias, dy} as numpy arrays in ``dtype``.
+
+    x: [N, C, T], W: [D, C, T], bias: [D] or None, dy: [N, D, T] or None.
+    """
+    if dtype not in _NP_DTYPE:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    out = {}
+    out["x"] = _cast(rng.standard_normal((N, C, T)), dtype)
+    out["W"] = _cast(rng.standard_normal((D, C, T)) * np.sqrt(1.0 / (C * T)), dtype)
+    out["bias"] = _cast(rng.standard_normal(D) * np.sqrt(0.02), dtype) if bias else None
+    out["dy"] = _cast(rng.standard_normal((N, D, T)), dtype) if dy else None
+    return out
+
+
+def workload_inputs(name, dtype=None, seed=0):
+    w = WORKLOADS[name]
+    dt = dtype or w.dtypes[0]
+    return make_inputs(w.C, w.D, w.N, w.T, dt, seed, bias=w.bias, dy="backward" in w.passes)

@@ -1,0 +1,21 @@
+"""Plain fp64 CPU oracle for the p4 EQ-Linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this package:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it.  It shares no code with the HIP path (no kernels, headers,
+helpers, tables or constants) and imports nothing from it.
+
+What it computes, and where each piece is defined, is documented per function in
+``oracle/eqlinear_oracle.py``.  Every function has pins in ``tests/`` that tie
+it to the definition on the pages and to mathematics (brute force, closed
+forms, special cases that reduce to library routines, invariants, finite
+differences); none of it is "parity unpinned".
+"""
+from .eqlinear_oracle import (  # noqa: F401
+    unroll_block_circulant,
+    forward,
+    backward_input,
+    backward_weight,
+    mac_counts,
+    param_counts,
+)
