@@ -1,0 +1,120 @@
+// Device-side helpers shared by the libeqlinear kernels (gfx950 / CDNA4).
+//
+// The p4 group DFT used throughout ("Specializzazione per il Gruppo di
+// Rotazione p4", Flash EQ-Linear gist.science summary: the length-4 DFT and
+// its inverse only need additions, subtractions and power-of-two scalings).
+// With omega = exp(-2*pi*i/4) = -i and X[k] = sum_s x[s] omega^(k s):
+//     X0 = (x0 + x2) + (x1 + x3)     X2 = (x0 + x2) - (x1 + x3)
+//     X1 = Xr + i Xi,  Xr = x0 - x2, Xi = x3 - x1,   X3 = conj(X1)
+// and the inverse, written with the kept frequencies only (conjugate
+// symmetry of the real DFT, "Approccio Algoritmico"):
+//     y0 = (Y0 + Y2)/4 + Yr/2        y1 = (Y0 - Y2)/4 - Yi/2
+//     y2 = (Y0 + Y2)/4 - Yr/2        y3 = (Y0 - Y2)/4 + Yi/2
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eql {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Forward length-4 butterfly on one group vector (fp32 arithmetic).
+struct Spec4 {
+  float f0, f2, fr, fi;
+};
+
+__device__ __forceinline__ Spec4 dft4(float x0, float x1, float x2, float x3) {
+  const float s02 = x0 + x2, s13 = x1 + x3;
+  Spec4 s;
+  s.f0 = s02 + s13;
+  s.f2 = s02 - s13;
+  s.fr = x0 - x2;
+  s.fi = x3 - x1;
+  return s;
+}
+
+// Inverse length-4 butterfly, fp32, with the 1/4 and 1/2 scalings (exact).
+__device__ __forceinline__ floatx4 idft4(float Y0, float Y2, float Yr, float Yi) {
+  const float a = 0.25f * (Y0 + Y2), b = 0.25f * (Y0 - Y2);
+  const float r = 0.5f * Yr, i = 0.5f * Yi;
+  floatx4 o;
+  o[0] = a + r;
+  o[1] = b - i;
+  o[2] = a - r;
+  o[3] = b + i;
+  return o;
+}
+
+// ---- element type traits ---------------------------------------------------
+// Loads/stores of one group quad (4 elements of the type) and conversions.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  typedef floatx4 quad;  // 16 B
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+  static __device__ __forceinline__ quad pack(floatx4 v) { return v; }
+  static __device__ __forceinline__ floatx4 unpack(quad q) { return q; }
+};
+
+template <>
+struct Elem<_Float16> {
+  typedef half4 quad;  // 8 B
+  static __device__ __forceinline__ float to_f(_Float16 v) { return (float)v; }
+  static __device__ __forceinline__ _Float16 from_f(float v) { return (_Float16)v; }
+  static __device__ __forceinline__ quad pack(floatx4 v) {
+    quad q;
+    q[0] = (_Float16)v[0];
+    q[1] = (_Float16)v[1];
+    q[2] = (_Float16)v[2];
+    q[3] = (_Float16)v[3];
+    return q;
+  }
+  static __device__ __forceinline__ floatx4 unpack(quad q) {
+    floatx4 v;
+    v[0] = (float)q[0];
+    v[1] = (float)q[1];
+    v[2] = (float)q[2];
+    v[3] = (float)q[3];
+    return v;
+  }
+};
+
+// ---- matrix-core step ------------------------------------------------------
+// One 32x32 output block, fp32 accumulate.  Operand lane layout (checked on
+// gfx950): lane l holds row/column (l % 32) and the k slice owned by lane
+// group h = l / 32; the result register r of lane l is row
+// 8*(r/4) + 4*h + (r%4), column l % 32.
+//   binary16: v_mfma_f32_32x32x16_f16, 8 consecutive k per lane
+//   binary32: v_mfma_f32_32x32x2_f32,  1 k per lane
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<_Float16> {
+  typedef half8 frag;
+  static constexpr int K_PER_LANE = 8;   // k values one lane feeds per step
+  static constexpr int K_STEP = 16;      // k values per instruction
+  static __device__ __forceinline__ floatx16 mma(frag a, frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<float> {
+  typedef float frag;
+  static constexpr int K_PER_LANE = 1;
+  static constexpr int K_STEP = 2;
+  static __device__ __forceinline__ floatx16 mma(frag a, frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+}  // namespace eql

@@ -1,0 +1,59 @@
+// Host-side internals of libeqlinear: the plan object and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/eqlinear.h"
+
+namespace eql {
+
+// Padding of the spectra planes.  A plane used as the matrix-core B operand
+// with "k" = reduction channel and "n" = output channel is stored [n][k] with
+// k contiguous; k is padded to KPAD and n to NPAD with zeros so that the
+// kernels never bounds-check weight reads.
+constexpr int KPAD = 32;
+constexpr int NPAD = 128;
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+struct SpectraLayout {
+  int64_t n_pad;  // padded output-channel count (rows of a plane)
+  int64_t k_pad;  // padded reduction-channel count (contiguous)
+  size_t plane_elems() const { return (size_t)(n_pad * k_pad); }
+};
+
+}  // namespace eql
+
+struct eqlinear_plan {
+  int64_t C, D;
+  eqlinear_dtype_t dtype;
+  size_t esize;  // bytes per element of the plan dtype
+  int device;    // device of the spectra, -1 before the first set_weight
+  bool has_weight;
+  // Forward operand: 4 planes {W0, W2, Wr, Wi}, each [D_pad][C_pad].
+  eql::SpectraLayout fwd;
+  // Backward-input operand: conjugate transpose {W0^T, W2^T, Wr^T, -Wi^T},
+  // each [C_pad][D_pad].
+  eql::SpectraLayout adj;
+  void* spec_fwd;     // device, plan dtype
+  void* spec_adj;     // device, plan dtype
+  float* bias_f32;    // device, [fwd.n_pad], zeros where no bias
+  float* zeros_f32;   // device, [adj.n_pad] zeros (bias of backward_input)
+};
+
+namespace eql {
+
+// Backward-weight split over rows: each work-group reduces ROWS_PER_SPLIT rows.
+int64_t bwd_weight_rows_per_split(const eqlinear_plan* p, int64_t N);
+size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N);
+
+hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
+hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s);
+hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
+                                 hipStream_t s);
+hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
+                                  float* dbias, int64_t N, void* ws, hipStream_t s);
+
+}  // namespace eql

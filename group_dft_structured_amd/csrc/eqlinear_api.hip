@@ -1,0 +1,214 @@
+// C ABI of libeqlinear: argument validation, the plan object and dispatch.
+// Every check that can run without a GPU runs before the first HIP call.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "eql_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char* what, hipError_t e) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest channel count and row count accepted (32-bit index arithmetic in
+// the kernels stays in range below these).
+constexpr int64_t MAX_CHANNELS = 1 << 16;
+constexpr int64_t MAX_ROWS = (int64_t)1 << 30;
+
+eqlinear_status_t check_device(const eqlinear_plan* p) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return EQL_ERR_HIP;
+  }
+  if (p->device >= 0 && cur != p->device) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "plan spectra live on device %d but device %d is current", p->device, cur);
+    return EQL_ERR_INVALID_ARG;
+  }
+  return EQL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* eqlinear_status_string(eqlinear_status_t st) {
+  switch (st) {
+    case EQL_OK: return "ok";
+    case EQL_ERR_INVALID_ARG: return "invalid argument";
+    case EQL_ERR_UNSUPPORTED: return "unsupported group size or dtype";
+    case EQL_ERR_NO_WEIGHT: return "no weight set on the plan";
+    case EQL_ERR_MISALIGNED: return "buffer not 16-byte aligned";
+    case EQL_ERR_WORKSPACE: return "workspace missing or too small";
+    case EQL_ERR_ALLOC: return "device allocation failed";
+    case EQL_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* eqlinear_last_error(void) { return g_last_error; }
+
+eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T, eqlinear_dtype_t dtype,
+                                       eqlinear_plan_t* out) {
+  if (out == nullptr) return EQL_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (T != 4) return EQL_ERR_UNSUPPORTED;
+  if (dtype != EQL_F32 && dtype != EQL_F16) return EQL_ERR_UNSUPPORTED;
+  if (C <= 0 || D <= 0 || C > MAX_CHANNELS || D > MAX_CHANNELS) return EQL_ERR_INVALID_ARG;
+  eqlinear_plan* p = new (std::nothrow) eqlinear_plan;
+  if (p == nullptr) return EQL_ERR_ALLOC;
+  memset(p, 0, sizeof(*p));
+  p->C = C;
+  p->D = D;
+  p->dtype = dtype;
+  p->esize = dtype == EQL_F16 ? 2 : 4;
+  p->device = -1;
+  p->has_weight = false;
+  p->fwd.n_pad = eql::round_up(D, eql::NPAD);
+  p->fwd.k_pad = eql::round_up(C, eql::KPAD);
+  p->adj.n_pad = eql::round_up(C, eql::NPAD);
+  p->adj.k_pad = eql::round_up(D, eql::KPAD);
+  *out = p;
+  return EQL_OK;
+}
+
+eqlinear_status_t eqlinear_plan_destroy(eqlinear_plan_t p) {
+  if (p == nullptr) return EQL_OK;
+  eqlinear_status_t st = EQL_OK;
+  if (p->spec_fwd != nullptr) {
+    int prev = -1;
+    hipGetDevice(&prev);
+    if (prev != p->device) hipSetDevice(p->device);
+    hipError_t e = hipFree(p->spec_fwd);  // one allocation holds every device buffer
+    if (e != hipSuccess) {
+      set_error("hipFree", e);
+      st = EQL_ERR_HIP;
+    }
+    if (prev >= 0 && prev != p->device) hipSetDevice(prev);
+  }
+  delete p;
+  return st;
+}
+
+eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t p, const void* W, const void* bias,
+                                      void* stream) {
+  if (p == nullptr || W == nullptr) return EQL_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(bias)) return EQL_ERR_MISALIGNED;
+  eqlinear_status_t st = check_device(p);
+  if (st != EQL_OK) return st;
+  if (p->spec_fwd == nullptr) {
+    const size_t fwd_bytes = 4 * p->fwd.plane_elems() * p->esize;
+    const size_t adj_bytes = 4 * p->adj.plane_elems() * p->esize;
+    const size_t bias_bytes = (size_t)p->fwd.n_pad * sizeof(float);
+    const size_t zero_bytes = (size_t)p->adj.n_pad * sizeof(float);
+    void* mem = nullptr;
+    hipError_t e = hipMalloc(&mem, fwd_bytes + adj_bytes + bias_bytes + zero_bytes);
+    if (e != hipSuccess) {
+      set_error("hipMalloc(spectra)", e);
+      return EQL_ERR_ALLOC;
+    }
+    int dev = -1;
+    hipGetDevice(&dev);
+    char* base = (char*)mem;
+    p->spec_fwd = base;
+    p->spec_adj = base + fwd_bytes;
+    p->bias_f32 = (float*)(base + fwd_bytes + adj_bytes);
+    p->zeros_f32 = (float*)(base + fwd_bytes + adj_bytes + bias_bytes);
+    p->device = dev;
+  }
+  hipError_t e = eql::launch_spectra(p, W, bias, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("weight spectra launch", e);
+    return EQL_ERR_HIP;
+  }
+  p->has_weight = true;
+  return EQL_OK;
+}
+
+static eqlinear_status_t check_gemm_args(eqlinear_plan_t p, const void* in, const void* out,
+                                         int64_t N) {
+  if (p == nullptr) return EQL_ERR_INVALID_ARG;
+  if (N < 0 || N > MAX_ROWS) return EQL_ERR_INVALID_ARG;
+  if (!p->has_weight) return EQL_ERR_NO_WEIGHT;
+  if (N == 0) return EQL_OK;
+  if (in == nullptr || out == nullptr) return EQL_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(out)) return EQL_ERR_MISALIGNED;
+  return EQL_OK;
+}
+
+eqlinear_status_t eqlinear_forward(eqlinear_plan_t p, const void* x, void* y, int64_t N,
+                                   void* stream) {
+  eqlinear_status_t st = check_gemm_args(p, x, y, N);
+  if (st != EQL_OK || N == 0) return st;
+  st = check_device(p);
+  if (st != EQL_OK) return st;
+  hipError_t e = eql::launch_forward(p, x, y, N, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("forward launch", e);
+    return EQL_ERR_HIP;
+  }
+  return EQL_OK;
+}
+
+eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t p, const void* dy, void* dx, int64_t N,
+                                          void* stream) {
+  eqlinear_status_t st = check_gemm_args(p, dy, dx, N);
+  if (st != EQL_OK || N == 0) return st;
+  st = check_device(p);
+  if (st != EQL_OK) return st;
+  hipError_t e = eql::launch_backward_input(p, dy, dx, N, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("backward_input launch", e);
+    return EQL_ERR_HIP;
+  }
+  return EQL_OK;
+}
+
+size_t eqlinear_backward_weight_workspace(eqlinear_plan_t p, int64_t N) {
+  if (p == nullptr || N < 0 || N > MAX_ROWS) return 0;
+  return eql::bwd_weight_workspace_bytes(p, N);
+}
+
+eqlinear_status_t eqlinear_backward_weight(eqlinear_plan_t p, const void* x, const void* dy,
+                                           float* dW, float* dbias, int64_t N, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (p == nullptr || dW == nullptr) return EQL_ERR_INVALID_ARG;
+  if (N < 0 || N > MAX_ROWS) return EQL_ERR_INVALID_ARG;
+  if (N > 0 && (x == nullptr || dy == nullptr)) return EQL_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dW) || !aligned16(dbias) ||
+      !aligned16(workspace))
+    return EQL_ERR_MISALIGNED;
+  const size_t need = eql::bwd_weight_workspace_bytes(p, N);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return EQL_ERR_WORKSPACE;
+  eqlinear_status_t st = check_device(p);
+  if (st != EQL_OK) return st;
+  hipError_t e = eql::launch_backward_weight(p, x, dy, dW, dbias, N, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("backward_weight launch", e);
+    return EQL_ERR_HIP;
+  }
+  return EQL_OK;
+}
+
+eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t p, int64_t N, int64_t* spectral_macs,
+                                      int64_t* dense_macs) {
+  if (p == nullptr || N < 0) return EQL_ERR_INVALID_ARG;
+  // p4: frequencies 0 and 2 are real (one product each), frequency 1 is
+  // complex (four real products), frequency 3 is its conjugate (free).
+  const int64_t ncd = N * p->C * p->D;
+  if (spectral_macs) *spectral_macs = 6 * ncd;
+  if (dense_macs) *dense_macs = 16 * ncd;
+  return EQL_OK;
+}
+
+}  // extern "C"

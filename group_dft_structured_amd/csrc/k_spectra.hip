@@ -1,0 +1,84 @@
+// Weight-spectrum precompute: the group DFT of every W[d,c,:] (length 4),
+// written once per weight update in the two operand layouts the matrix-core
+// kernels read.
+//
+// Flash EQ-Linear ("Approccio Algoritmico", "Specializzazione per il Gruppo di
+// Rotazione p4"): after the DFT along the group axis the convolution becomes a
+// product per frequency; the weights are real, so frequency 3 is the
+// conjugate of frequency 1 and only {W0, W2, Wr + i Wi} are kept.
+//
+// Forward operand  (reduction over c):  planes {W0, W2, Wr, Wi}, [D_pad][C_pad]
+// Adjoint operand  (reduction over d):  planes {W0, W2, Wr, -Wi} transposed,
+//                                       [C_pad][D_pad]  (conj(W)^T per frequency)
+// Padding entries are written as zeros, so the GEMM kernels read padded planes
+// without bounds checks.
+#include "eql_device.h"
+#include "eql_internal.h"
+
+namespace eql {
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_weight_spectra(
+    const T* __restrict__ W, const T* __restrict__ bias, T* __restrict__ spec_fwd,
+    T* __restrict__ spec_adj, float* __restrict__ bias_f32, float* __restrict__ zeros_f32,
+    int C, int D, int fwd_n, int fwd_k, int adj_n, int adj_k) {
+  const int64_t fwd_elems = (int64_t)fwd_n * fwd_k;
+  const int64_t adj_elems = (int64_t)adj_n * adj_k;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < fwd_elems) {
+    const int d = (int)(i / fwd_k), c = (int)(i % fwd_k);
+    Spec4 s = {0.f, 0.f, 0.f, 0.f};
+    if (d < D && c < C) {
+      const T* w = W + ((int64_t)d * C + c) * 4;
+      s = dft4(Elem<T>::to_f(w[0]), Elem<T>::to_f(w[1]), Elem<T>::to_f(w[2]), Elem<T>::to_f(w[3]));
+    }
+    spec_fwd[0 * fwd_elems + i] = Elem<T>::from_f(s.f0);
+    spec_fwd[1 * fwd_elems + i] = Elem<T>::from_f(s.f2);
+    spec_fwd[2 * fwd_elems + i] = Elem<T>::from_f(s.fr);
+    spec_fwd[3 * fwd_elems + i] = Elem<T>::from_f(s.fi);
+    return;
+  }
+  const int64_t j = i - fwd_elems;
+  if (j < adj_elems) {
+    const int c = (int)(j / adj_k), d = (int)(j % adj_k);
+    Spec4 s = {0.f, 0.f, 0.f, 0.f};
+    if (d < D && c < C) {
+      const T* w = W + ((int64_t)d * C + c) * 4;
+      s = dft4(Elem<T>::to_f(w[0]), Elem<T>::to_f(w[1]), Elem<T>::to_f(w[2]), Elem<T>::to_f(w[3]));
+    }
+    spec_adj[0 * adj_elems + j] = Elem<T>::from_f(s.f0);
+    spec_adj[1 * adj_elems + j] = Elem<T>::from_f(s.f2);
+    spec_adj[2 * adj_elems + j] = Elem<T>::from_f(s.fr);
+    spec_adj[3 * adj_elems + j] = Elem<T>::from_f(-s.fi);
+    return;
+  }
+  const int64_t k = j - adj_elems;
+  if (k < fwd_n) {
+    const int d = (int)k;
+    bias_f32[d] = (bias != nullptr && d < D) ? Elem<T>::to_f(bias[d]) : 0.f;
+    return;
+  }
+  const int64_t z = k - fwd_n;
+  if (z < adj_n) zeros_f32[z] = 0.f;
+}
+
+hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s) {
+  const int64_t total = (int64_t)p->fwd.plane_elems() + (int64_t)p->adj.plane_elems() +
+                        p->fwd.n_pad + p->adj.n_pad;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (p->dtype == EQL_F16) {
+    hipLaunchKernelGGL(k_weight_spectra<_Float16>, dim3((unsigned)blocks), dim3(threads), 0, s,
+                       (const _Float16*)W, (const _Float16*)bias, (_Float16*)p->spec_fwd,
+                       (_Float16*)p->spec_adj, p->bias_f32, p->zeros_f32, (int)p->C, (int)p->D,
+                       (int)p->fwd.n_pad, (int)p->fwd.k_pad, (int)p->adj.n_pad, (int)p->adj.k_pad);
+  } else {
+    hipLaunchKernelGGL(k_weight_spectra<float>, dim3((unsigned)blocks), dim3(threads), 0, s,
+                       (const float*)W, (const float*)bias, (float*)p->spec_fwd,
+                       (float*)p->spec_adj, p->bias_f32, p->zeros_f32, (int)p->C, (int)p->D,
+                       (int)p->fwd.n_pad, (int)p->fwd.k_pad, (int)p->adj.n_pad, (int)p->adj.k_pad);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace eql

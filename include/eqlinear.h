@@ -1,0 +1,143 @@
+/*
+ * eqlinear.h -- C ABI of libeqlinear, the p4 equivariant linear layer
+ * (EQ-Linear, group size T = 4) on AMD MI355X (gfx950).
+ *
+ * The operation.  Flash EQ-Linear: Accelerating Equivariant Linear Layers via
+ * Group-wise Discrete Fourier Transform (gist.science technical summary,
+ * "Intuizione Centrale"; authors' English abstract on the arxivdaily page):
+ * an EQ-Linear layer is a circular convolution along the group axis composed
+ * with a linear map along channels.  With C input and D output channels per
+ * group element,
+ *
+ *     y[n,d,t] = sum_{c<C} sum_{s<4} W[d,c,(t-s) mod 4] * x[n,c,s]  + bias[d]
+ *
+ * It is the dense product with the unrolled group-circulant matrix
+ * ("Problematica"), computed exactly through a real DFT along the group axis
+ * ("Approccio Algoritmico"; "Specializzazione per il Gruppo di Rotazione p4":
+ * adds/subtracts for the transforms and six real matrix products).
+ *
+ * Layouts.  Every tensor is dense, row-major, with the group index fastest:
+ *     x, dx : [N][C][4]      y, dy : [N][D][4]      W, dW : [D][C][4]
+ *     bias, dbias : [D]
+ * x, y, dx, dy, W and bias hold the plan's dtype (EQL_F32 = IEEE binary32,
+ * EQL_F16 = IEEE binary16); dW and dbias are always binary32.  Every pointer
+ * must be 16-byte aligned (EQL_ERR_MISALIGNED otherwise).
+ *
+ * Ownership.  Buffers passed in belong to the caller and are only read or
+ * written during the stream-ordered execution of the call.  The plan owns a
+ * small device copy of the weight spectra (set by eqlinear_set_weight, which
+ * keeps no pointer to W) and frees it in eqlinear_plan_destroy.
+ *
+ * Streams and errors.  Every device call is asynchronous on the given HIP
+ * stream (NULL = the null stream) and never synchronises.  Arguments are
+ * validated on the host before any HIP call, so the validation paths run
+ * without a GPU.  A call returns a status code; it never aborts.  Launch
+ * failures are reported as EQL_ERR_HIP with the HIP message available from
+ * eqlinear_last_error().  Faults inside kernels surface at the caller's next
+ * synchronisation, as with any HIP library.
+ *
+ * Concurrency.  forward, backward_input and backward_weight only read the
+ * plan, so they may run concurrently on different streams.  Ordering
+ * set_weight against calls in flight is the caller's responsibility.
+ */
+#ifndef EQLINEAR_H
+#define EQLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct eqlinear_plan* eqlinear_plan_t; /* opaque */
+
+typedef enum { EQL_F32 = 0, EQL_F16 = 1 } eqlinear_dtype_t;
+
+typedef enum {
+  EQL_OK = 0,
+  EQL_ERR_INVALID_ARG = 1, /* NULL pointer, C/D <= 0, N < 0, size overflow */
+  EQL_ERR_UNSUPPORTED = 2, /* T != 4 or unknown dtype */
+  EQL_ERR_NO_WEIGHT = 3,   /* forward/backward before set_weight */
+  EQL_ERR_MISALIGNED = 4,  /* a buffer is not 16-byte aligned */
+  EQL_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  EQL_ERR_ALLOC = 6,       /* hipMalloc of the plan's spectra failed */
+  EQL_ERR_HIP = 7          /* another HIP runtime error */
+} eqlinear_status_t;
+
+/* Create a plan for C input and D output channels per group element, group
+ * size T, and dtype.  The group DFT method is specialised to the p4 group
+ * ("Limitazioni e Lavoro Futuro": the implementation covers p4 only), so
+ * T != 4 returns EQL_ERR_UNSUPPORTED.  Host-only: allocates no device memory.
+ * On success *out holds a new plan. */
+eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T,
+                                       eqlinear_dtype_t dtype,
+                                       eqlinear_plan_t* out);
+
+/* Destroy a plan and free its device spectra (NULL is a no-op).  The caller
+ * must ensure no call using the plan is still in flight. */
+eqlinear_status_t eqlinear_plan_destroy(eqlinear_plan_t plan);
+
+/* Weight-spectrum precompute (once per weight update).  Reads W[D][C][4] and
+ * bias[D] (NULL = no bias) in the plan dtype and writes the plan's spectra:
+ * the length-4 real DFT of every W[d,c,:] (frequency 0, 2, and the real and
+ * imaginary part of frequency 1; frequency 3 is its conjugate, "Approccio
+ * Algoritmico": conjugate symmetry of the real DFT) in the layouts the
+ * forward and backward kernels read.  On the first call it allocates the
+ * spectra on the current device (EQL_ERR_ALLOC on failure); later calls
+ * must run on the same device. */
+eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t plan, const void* W,
+                                      const void* bias, void* stream);
+
+/* Forward: y[N][D][4] from x[N][C][4] (formula above, with the bias given to
+ * set_weight).  One fused kernel: group DFT of x in registers, six real
+ * products on the matrix cores (fp32 accumulation; binary16 operands for
+ * EQL_F16, binary32 for EQL_F32), inverse DFT, bias and the store.  N = 0 is
+ * a successful no-op. */
+eqlinear_status_t eqlinear_forward(eqlinear_plan_t plan, const void* x, void* y,
+                                   int64_t N, void* stream);
+
+/* Backward with respect to the input ("Implementazione": forward and backward
+ * passes): dx[n,c,s] = sum_{d,t} W[d,c,(t-s) mod 4] * dy[n,d,t], i.e. the
+ * transpose of the forward map, computed with the conjugate weight spectra.
+ * dx has the plan dtype.  N = 0 is a successful no-op. */
+eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t plan, const void* dy,
+                                          void* dx, int64_t N, void* stream);
+
+/* Bytes of device workspace eqlinear_backward_weight needs for N rows
+ * (0 for an invalid plan or N < 0). */
+size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t N);
+
+/* Backward with respect to the weight and bias:
+ *     dW[d,c,r] = sum_{n,t} dy[n,d,t] * x[n,c,(t-r) mod 4]   (binary32)
+ *     dbias[d]  = sum_{n,t} dy[n,d,t]                          (binary32)
+ * i.e. the gradient of every replica of a shared weight summed back onto it.
+ * dW and dbias (NULL = not wanted) are overwritten, not accumulated into.
+ * The reduction over N runs in binary32 in a fixed order (deterministic).
+ * workspace must hold eqlinear_backward_weight_workspace(plan, N) bytes
+ * (EQL_ERR_WORKSPACE otherwise).  N = 0 writes zeros.  Needs no prior
+ * set_weight. */
+eqlinear_status_t eqlinear_backward_weight(eqlinear_plan_t plan, const void* x,
+                                           const void* dy, float* dW, float* dbias,
+                                           int64_t N, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* eqlinear_status_string(eqlinear_status_t st);
+
+/* Message of the last EQL_ERR_HIP / EQL_ERR_ALLOC on the calling thread
+ * ("" if none). */
+const char* eqlinear_last_error(void);
+
+/* Real multiply-accumulates of one forward over N rows as computed by the
+ * library (6*N*C*D for p4) and of the dense unrolled product (16*N*C*D);
+ * the ratio is 2(T-1)/T^2 = 3/8 (authors' abstract).  Either pointer may be
+ * NULL. */
+eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t plan, int64_t N,
+                                      int64_t* spectral_macs, int64_t* dense_macs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQLINEAR_H */

@@ -1,0 +1,120 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side validation behaves as include/eqlinear.h states.  No call here
+reaches a HIP runtime function (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import group_dft_structured_amd as eq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eqlinear.h")
+
+
+def _lib():
+    if not os.path.exists(eq.LIB_PATH):
+        pytest.skip("libeqlinear.so not built (run __graft_entry__.build())")
+    return eq.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eqlinear_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary_calls():
+    names = declared_functions()
+    for n in ("eqlinear_plan_create", "eqlinear_set_weight", "eqlinear_forward",
+              "eqlinear_backward_input", "eqlinear_backward_weight"):
+        assert n in names
+    assert sorted(eq.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _raw_plan(lib, C=8, D=8, T=4, dtype=eq.EQL_F32):
+    h = ctypes.c_void_p()
+    st = lib.eqlinear_plan_create(C, D, T, dtype, ctypes.byref(h))
+    return st, h.value
+
+
+def test_plan_create_validation():
+    lib = _lib()
+    assert _raw_plan(lib, T=8)[0] == 2          # EQL_ERR_UNSUPPORTED: p4 only
+    assert _raw_plan(lib, T=2)[0] == 2
+    assert _raw_plan(lib, dtype=7)[0] == 2
+    assert _raw_plan(lib, C=0)[0] == 1          # EQL_ERR_INVALID_ARG
+    assert _raw_plan(lib, D=-3)[0] == 1
+    assert _raw_plan(lib, C=1 << 20)[0] == 1
+    assert lib.eqlinear_plan_create(8, 8, 4, 0, None) == 1
+    st, h = _raw_plan(lib)
+    assert st == 0 and h
+    assert lib.eqlinear_plan_destroy(h) == 0
+    assert lib.eqlinear_plan_destroy(None) == 0
+
+
+def test_calls_before_set_weight_and_bad_arguments():
+    lib = _lib()
+    st, h = _raw_plan(lib, 96, 384, 4, eq.EQL_F16)
+    assert st == 0
+    try:
+        fake = 0x10000  # never dereferenced: every case below fails validation first
+        assert lib.eqlinear_forward(h, fake, fake, 16, None) == 3        # NO_WEIGHT
+        assert lib.eqlinear_backward_input(h, fake, fake, 16, None) == 3
+        assert lib.eqlinear_forward(h, fake, fake, -1, None) == 1
+        assert lib.eqlinear_forward(None, fake, fake, 16, None) == 1
+        assert lib.eqlinear_set_weight(h, None, None, None) == 1
+        assert lib.eqlinear_set_weight(h, fake + 2, None, None) == 4      # MISALIGNED
+        assert lib.eqlinear_set_weight(h, fake, fake + 8, None) == 4
+        need = lib.eqlinear_backward_weight_workspace(h, 12608)
+        assert need > 0
+        assert lib.eqlinear_backward_weight_workspace(h, -1) == 0
+        assert lib.eqlinear_backward_weight_workspace(None, 10) == 0
+        bw = lib.eqlinear_backward_weight
+        assert bw(h, fake, fake, None, None, 16, fake, need, None) == 1   # dW NULL
+        assert bw(h, None, fake, fake, None, 16, fake, need, None) == 1
+        assert bw(h, fake, fake, fake, None, -5, fake, need, None) == 1
+        assert bw(h, fake + 4, fake, fake, None, 16, fake, need, None) == 4
+        assert bw(h, fake, fake, fake, fake + 4, 16, fake, need, None) == 4
+        need16 = lib.eqlinear_backward_weight_workspace(h, 16)
+        assert bw(h, fake, fake, fake, None, 16, None, need16, None) == 5  # WORKSPACE
+        assert bw(h, fake, fake, fake, None, 16, fake, need16 - 1, None) == 5
+    finally:
+        lib.eqlinear_plan_destroy(h)
+
+
+def test_mac_counts_and_ratio():
+    _lib()
+    p = eq.eqlinear_plan_create(96, 384, 4, eq.EQL_F16)
+    try:
+        s, d = eq.eqlinear_mac_counts(p, 12608)
+        assert s == 6 * 12608 * 96 * 384 and d == 16 * 12608 * 96 * 384
+        assert s * 8 == d * 3   # 2(T-1)/T^2 at T = 4
+    finally:
+        eq.eqlinear_plan_destroy(p)
+
+
+def test_status_strings_and_python_errors():
+    _lib()
+    for code in range(8):
+        assert eq.eqlinear_status_string(code)
+    with pytest.raises(eq.EqlinearError) as ei:
+        eq.eqlinear_plan_create(8, 8, 3, eq.EQL_F32)
+    assert ei.value.name == "EQL_ERR_UNSUPPORTED"
+
+
+def test_workspace_grows_with_rows():
+    _lib()
+    p = eq.eqlinear_plan_create(96, 384, 4, eq.EQL_F16)
+    try:
+        sizes = [eq.eqlinear_backward_weight_workspace(p, n) for n in (0, 1, 600, 12608)]
+        assert sizes[0] == 0 and 0 < sizes[1] <= sizes[2] <= sizes[3]
+    finally:
+        eq.eqlinear_plan_destroy(p)

@@ -1,0 +1,199 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bar: max|gpu - oracle| / max|oracle| <= 1e-5 for binary32 and <= 2e-3 for
+binary16 (fp32 accumulation), per output tensor.  The oracle consumes the
+exact dtype-rounded inputs widened to fp64."""
+import numpy as np
+import pytest
+
+import oracle
+from group_dft_structured_amd import Plan
+from group_dft_structured_amd.workloads import WORKLOADS, make_inputs
+from tests.gpu_helpers import TOL, gpu_available, rel_err, to_dev, to_np64, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+def _sync():
+    torch_mod().cuda.synchronize()
+
+
+def run_forward(C, D, N, dtype, seed=0, bias=True):
+    inp = make_inputs(C, D, N, dtype=dtype, seed=seed, bias=bias)
+    plan = Plan(C, D, dtype)
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    y = plan.forward(to_dev(inp["x"]))
+    _sync()
+    return inp, plan, y
+
+
+def check_forward_full(C, D, N, dtype, seed=0, bias=True):
+    inp, plan, y = run_forward(C, D, N, dtype, seed, bias)
+    ref = oracle.forward(inp["x"], inp["W"], inp["bias"])
+    err = rel_err(to_np64(y), ref)
+    print(f"forward C={C} D={D} N={N} {dtype} bias={bias}: rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype], err
+    return err
+
+
+# ---- workloads at full size ------------------------------------------------
+
+def test_forward_tiny_f32():
+    w = WORKLOADS["tiny"]
+    check_forward_full(w.C, w.D, w.N, "f32", bias=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_forward_vit_s_proj(dtype):
+    w = WORKLOADS["vit_s_proj"]
+    check_forward_full(w.C, w.D, w.N, dtype)
+
+
+def test_forward_vit_s_mlp_f16():
+    w = WORKLOADS["vit_s_mlp"]
+    check_forward_full(w.C, w.D, w.N, "f16")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_forward_swin_stage_sampled(dtype):
+    """Full-size Swin-like stage on the GPU; the oracle checks sampled rows
+    (random rows plus the first and last 64)."""
+    w = WORKLOADS["swin_stage"]
+    inp, plan, y = run_forward(w.C, w.D, w.N, dtype)
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([rng.choice(w.N, 1536, replace=False),
+                                     np.arange(64), np.arange(w.N - 64, w.N)]))
+    ref = oracle.forward(inp["x"][rows], inp["W"], inp["bias"])
+    got = to_np64(y[torch_mod().from_numpy(rows).to("cuda")])
+    err = rel_err(got, ref)
+    print(f"swin_stage {dtype} sampled {len(rows)} rows: rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype], err
+
+
+def _backward_case(C, D, N, dtype, seed=0):
+    inp = make_inputs(C, D, N, dtype=dtype, seed=seed, bias=True, dy=True)
+    plan = Plan(C, D, dtype)
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    x, dy = to_dev(inp["x"]), to_dev(inp["dy"])
+    dx = plan.backward_input(dy)
+    dW, db = plan.backward_weight(x, dy)
+    _sync()
+    ref_dx = oracle.backward_input(inp["dy"], inp["W"])
+    ref_dW, ref_db = oracle.backward_weight(inp["x"], inp["dy"])
+    e = (rel_err(to_np64(dx), ref_dx), rel_err(to_np64(dW), ref_dW), rel_err(to_np64(db), ref_db))
+    print(f"backward C={C} D={D} N={N} {dtype}: dx {e[0]:.3e} dW {e[1]:.3e} dbias {e[2]:.3e}",
+          flush=True)
+    for v in e:
+        assert v <= TOL[dtype], e
+    return plan, x, dy, dx, dW, db
+
+
+def test_backward_vit_s_mlp_f16():
+    w = WORKLOADS["vit_s_mlp_bwd"]
+    _backward_case(w.C, w.D, w.N, "f16")
+
+
+def test_backward_f32_small():
+    _backward_case(96, 384, 3000, "f32")
+
+
+# ---- ragged shapes and edge cases -------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("C,D,N", [(8, 8, 1), (5, 7, 63), (33, 130, 65), (96, 96, 1000),
+                                   (1, 1, 129), (64, 256, 257), (130, 33, 70), (200, 72, 191)])
+def test_forward_ragged(C, D, N, dtype):
+    check_forward_full(C, D, N, dtype, seed=C * 1000 + D)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("C,D,N", [(8, 8, 1), (5, 7, 63), (33, 130, 600), (130, 33, 1100),
+                                   (96, 96, 513)])
+def test_backward_ragged(C, D, N, dtype):
+    _backward_case(C, D, N, dtype, seed=7 + C)
+
+
+def test_no_bias_equals_zero_bias():
+    inp = make_inputs(24, 40, 100, dtype="f32", seed=3, bias=True)
+    plan = Plan(24, 40, "f32")
+    x = to_dev(inp["x"])
+    plan.set_weight(to_dev(inp["W"]), None)
+    y0 = plan.forward(x).clone()
+    plan.set_weight(to_dev(inp["W"]), to_dev(np.zeros(40, np.float32)))
+    y1 = plan.forward(x)
+    _sync()
+    assert torch_mod().equal(y0, y1)
+
+
+def test_zero_rows_is_noop():
+    torch = torch_mod()
+    inp = make_inputs(16, 16, 4, dtype="f16", seed=1)
+    plan = Plan(16, 16, "f16")
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    x = torch.empty((0, 16, 4), dtype=torch.float16, device="cuda")
+    y = plan.forward(x)
+    dx = plan.backward_input(torch.empty((0, 16, 4), dtype=torch.float16, device="cuda"))
+    dW = torch.full((16, 16, 4), 7.0, device="cuda")
+    db = torch.full((16,), 7.0, device="cuda")
+    plan.backward_weight(x, torch.empty((0, 16, 4), dtype=torch.float16, device="cuda"), dW, db)
+    _sync()
+    assert y.shape == (0, 16, 4) and dx.shape == (0, 16, 4)
+    assert float(dW.abs().max()) == 0.0 and float(db.abs().max()) == 0.0
+
+
+# ---- invariants on the GPU ---------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_gpu_equivariance(dtype):
+    """Rolling x along the group axis rolls y ("Contributi Chiave": rotation
+    equivariance is preserved).  The DFT of a rolled quad is a sign/swap of
+    the planes, so the GPU result is rolled exactly up to accumulation order."""
+    torch = torch_mod()
+    inp = make_inputs(96, 96, 2048, dtype=dtype, seed=5)
+    plan = Plan(96, 96, dtype)
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    x = to_dev(inp["x"])
+    y = plan.forward(x)
+    ymax = float(y.abs().max())
+    for r in (1, 2, 3):
+        yr = plan.forward(torch.roll(x, r, dims=2).contiguous())
+        _sync()
+        err = float((yr.float() - torch.roll(y, r, dims=2).float()).abs().max()) / ymax
+        assert err <= TOL[dtype], (r, err)
+
+
+def test_determinism_bitwise():
+    torch = torch_mod()
+    w = WORKLOADS["vit_s_mlp_bwd"]
+    inp = make_inputs(w.C, w.D, w.N, dtype="f16", seed=9, dy=True)
+    plan = Plan(w.C, w.D, "f16")
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    x, dy = to_dev(inp["x"]), to_dev(inp["dy"])
+    outs = []
+    for _ in range(2):
+        y = plan.forward(x)
+        dx = plan.backward_input(dy)
+        dW, db = plan.backward_weight(x, dy)
+        _sync()
+        outs.append((y.clone(), dx.clone(), dW.clone(), db.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_set_weight_twice_replaces_spectra():
+    inp1 = make_inputs(32, 64, 300, dtype="f32", seed=1)
+    inp2 = make_inputs(32, 64, 300, dtype="f32", seed=2)
+    plan = Plan(32, 64, "f32")
+    x = to_dev(inp1["x"])
+    plan.set_weight(to_dev(inp1["W"]), to_dev(inp1["bias"]))
+    plan.set_weight(to_dev(inp2["W"]), to_dev(inp2["bias"]))
+    y = plan.forward(x)
+    _sync()
+    ref = oracle.forward(inp1["x"], inp2["W"], inp2["bias"])
+    assert rel_err(to_np64(y), ref) <= TOL["f32"]
