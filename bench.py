@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the p4 EQ-Linear hot path on one MI355X.
+
+One step = one pass of the whole path over one synthetic batch:
+    set_weight (weight spectra) -> forward -> backward_input -> backward_weight
+on the ViT-S-like MLP expansion layer (N = 12608 rows = 64 images x 197
+tokens, C = 96, D = 384 channels per group element, T = 4, binary16 operands
+with fp32 accumulation).  The step is captured once as a HIP graph and
+replayed, so host launch overhead does not enter the timed region.
+
+Printed: one JSON line.  ``value`` is the metric (forward actual TFLOP/s:
+12*N*C*D flops of the six real products per forward, divided by the
+forward's average duration measured with HIP events on the launch stream);
+``roofline`` reports the kernel that takes the largest share of the step;
+``cpu_baseline`` times the fp64 oracle on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EQ-Linear p4 fwd TFLOP/s (dense-equiv and actual) + % MFMA peak, fp16/fp32"
+PEAK_HBM_GBPS = 8000.0
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "f32": 157.3}
+WORKLOAD = "vit_s_mlp"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--dtype", default=None)
+    ap.add_argument("--kernel-reps", type=int, default=100,
+                    help="launches per captured graph when timing single kernels")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the oracle baseline (0 = skip)")
+    return ap.parse_args()
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "group_dft_structured_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when missing or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic_bytes_per_launch ") or line.startswith("sources_sha256 "):
+                parts = line.split()
+                vals[(parts[0], parts[1])] = parts[2]
+    if vals.get(("sources_sha256", "all")) != src_hash:
+        return None
+    v = vals.get(("traffic_bytes_per_launch", kernel_key))
+    return float(v) if v is not None else None
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import group_dft_structured_amd as eq
+    from group_dft_structured_amd.workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    eq.load_library()  # fails loudly when the HIP library is not built
+
+    w = WORKLOADS[args.workload]
+    dtype = args.dtype or w.dtypes[0]
+    N, C, D, T = w.N, w.C, w.D, w.T
+    esz = 2 if dtype == "f16" else 4
+    dev = torch.device("cuda:0")
+
+    inp = make_inputs(C, D, N, T, dtype=dtype, seed=0, bias=True, dy=True)
+    tens = {k: torch.from_numpy(v).to(dev) for k, v in inp.items() if v is not None}
+    x, W, bias, dy = tens["x"], tens["W"], tens["bias"], tens["dy"]
+    tdt = x.dtype
+    y = torch.empty((N, D, T), dtype=tdt, device=dev)
+    dx = torch.empty((N, C, T), dtype=tdt, device=dev)
+    dW = torch.empty((D, C, T), dtype=torch.float32, device=dev)
+    db = torch.empty((D,), dtype=torch.float32, device=dev)
+    plan = eq.Plan(C, D, dtype)
+    ws_bytes = plan.workspace_bytes(N)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+
+    passes = {
+        "set_weight": lambda: plan.set_weight(W, bias),
+        "forward": lambda: plan.forward(x, y),
+        "backward_input": lambda: plan.backward_input(dy, dx),
+        "backward_weight": lambda: plan.backward_weight(x, dy, dW, db, ws),
+    }
+
+    def step():
+        for fn in passes.values():
+            fn()
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step()  # first set_weight allocates the plan's spectra: outside any capture
+        torch.cuda.synchronize()
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            g_step.replay()
+        torch.cuda.synchronize()
+
+        # ---- timed region: exactly K steps -------------------------------------
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            g_step.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wall_ms = (t1 - t0) * 1e3 / args.steps
+        gpu_ms = ev0.elapsed_time(ev1) / args.steps
+
+        # ---- per-kernel average launch duration (HIP events, same stream) --------
+        per_pass_us = {}
+        for name, fn in passes.items():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(args.kernel_reps):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / args.kernel_reps
+                best = us if best is None else min(best, us)
+            per_pass_us[name] = best
+            del g
+
+    flops = 12.0 * N * C * D  # six real N x C x D products, 2 flops per MAC
+    dense_flops = 32.0 * N * C * D
+    spec_bytes = 4 * C * D * esz
+    bytes_alg = {
+        "set_weight": D * C * T * esz + D * esz + 2 * spec_bytes + 4 * D,
+        "forward": N * T * (C + D) * esz + spec_bytes + 4 * D,
+        "backward_input": N * T * (C + D) * esz + spec_bytes,
+        "backward_weight": N * T * (C + D) * esz + 4 * D * C * T + 4 * D,
+    }
+    flops_pass = {"set_weight": 0.0, "forward": flops, "backward_input": flops,
+                  "backward_weight": flops}
+    kinfo = {}
+    for name, us in per_pass_us.items():
+        gbps = bytes_alg[name] / (us * 1e-6) / 1e9
+        tfl = flops_pass[name] / (us * 1e-6) / 1e12
+        kinfo[name] = {"us": round(us, 3), "alg_bytes": bytes_alg[name],
+                       "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                       "tflops_actual": round(tfl, 2),
+                       "mfma_frac": round(tfl / PEAK_MFMA_TFLOPS[dtype], 4)}
+
+    fwd_us = per_pass_us["forward"]
+    value = flops / (fwd_us * 1e-6) / 1e12
+    dominant = max(per_pass_us, key=per_pass_us.get)
+    src_hash = kernel_sources_hash()
+    dom_ai = flops_pass[dominant] / bytes_alg[dominant]
+    ridge = PEAK_MFMA_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if dom_ai < ridge:
+        roof = {"bound": "hbm", "achieved": kinfo[dominant]["hbm_gbps"], "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": kinfo[dominant]["hbm_frac"]}
+    else:
+        roof = {"bound": "mfma", "achieved": kinfo[dominant]["tflops_actual"],
+                "peak": PEAK_MFMA_TFLOPS[dtype], "unit": "TFLOP/s",
+                "frac": kinfo[dominant]["mfma_frac"]}
+    roof["kernel"] = dominant
+    roof["traffic"] = read_traffic(f"{args.workload}.{dtype}.{dominant}", src_hash)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded normal inputs of the workload's shape)",
+        "config": {"workload": f"{w.name}: {w.desc}; N={N} C={C} D={D} T={T}",
+                   "N": N, "C": C, "D": D, "T": T,
+                   "step": "set_weight + forward + backward_input + backward_weight (HIP graph)"},
+        "fwd_tflops_actual": round(value, 2),
+        "fwd_tflops_dense_equiv": round(dense_flops / (fwd_us * 1e-6) / 1e12, 2),
+        "fwd_mfma_peak_frac": round(value / PEAK_MFMA_TFLOPS[dtype], 4),
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "kernels": kinfo,
+        "roofline": roof,
+        "sources_sha256": src_hash,
+    }
+
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, flops, N, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
+def cpu_baseline(inp, flops_per_forward, N, budget_s):
+    """The fp64 oracle's forward on the full batch, repeated within a time
+    budget, on the host cores (BLAS threads reported)."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"),
+                    default=1)
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(inp["x"], inp["W"], inp["bias"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(flops_per_forward * reps / el / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle.forward (fp64 dense block-circulant, numpy/BLAS) on the full "
+                      f"{N}-row batch, {reps} repetitions in {el:.1f} s; value counts the "
+                      f"method's actual flops (12*N*C*D per forward)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -50,6 +50,13 @@ int64_t bwd_weight_rows_per_split(const eqlinear_plan* p, int64_t N);
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N);
 
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
+// Streaming kernel for reduction widths that fit in LDS; hipErrorNotSupported
+// when the shape is outside its limits.
+hipError_t launch_stream(eqlinear_dtype_t dt, const void* a, const void* spec, const float* bias,
+                         void* out, int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
+// Weight-stationary pipelined kernel (binary16, reduction width <= 192).
+hipError_t launch_coop(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias,
+                       void* y, int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
 hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s);
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s);

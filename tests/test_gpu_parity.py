@@ -105,11 +105,28 @@ def test_backward_f32_small():
 
 # ---- ragged shapes and edge cases -------------------------------------------
 
+@pytest.mark.parametrize("kernel", ["auto", "tiled"])
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("C,D,N", [(8, 8, 1), (5, 7, 63), (33, 130, 65), (96, 96, 1000),
-                                   (1, 1, 129), (64, 256, 257), (130, 33, 70), (200, 72, 191)])
-def test_forward_ragged(C, D, N, dtype):
+                                   (1, 1, 129), (64, 256, 257), (130, 33, 70), (200, 72, 191),
+                                   (96, 384, 3001), (192, 200, 777), (40, 48, 17)])
+def test_forward_ragged(C, D, N, dtype, kernel, monkeypatch):
+    """kernel=auto lets the library pick (streaming kernel where K fits its
+    limits); kernel=tiled forces the tiled LDS kernel for every shape."""
+    if kernel == "tiled":
+        monkeypatch.setenv("EQL_NO_STREAM", "1")
     check_forward_full(C, D, N, dtype, seed=C * 1000 + D)
+
+
+@pytest.mark.parametrize("bn,nw", [(32, 4), (64, 4), (64, 8), (128, 4)])
+def test_forward_stream_variants(bn, nw, monkeypatch):
+    """Every compiled variant of the streaming kernel, on a ragged shape."""
+    monkeypatch.setenv("EQL_STREAM_BN", str(bn))
+    monkeypatch.setenv("EQL_STREAM_NW", str(nw))
+    for dtype in ("f16", "f32"):
+        if dtype == "f32" and bn == 128:
+            continue
+        check_forward_full(96, 200, 1234, dtype, seed=bn + nw)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
