@@ -49,6 +49,11 @@ namespace eql {
 int64_t bwd_weight_rows_per_split(const eqlinear_plan* p, int64_t N);
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N);
 
+// Matrix-core backward-weight path (binary16, even channel counts).
+size_t bwd_weight_mfma_workspace(const eqlinear_plan* p, int64_t N);
+hipError_t launch_bwd_weight_mfma(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
+                                  float* dbias, int64_t N, void* ws, hipStream_t s);
+
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
 // Streaming kernel for reduction widths that fit in LDS; hipErrorNotSupported
 // when the shape is outside its limits.

@@ -263,7 +263,16 @@ static void bw_dims(const eqlinear_plan* p, int64_t N, int64_t* S, int64_t* d_pa
   *c_pad = round_up(p->C, BW_BC);
 }
 
+// The matrix-core path handles binary16 with even channel counts (16-byte
+// loads of column pairs); everything else uses the tiled kernel below.
+static bool use_mfma_path(const eqlinear_plan* p) {
+  const char* v = getenv("EQL_BW_TILED");
+  if (v && *v && atoi(v)) return false;
+  return p->dtype == EQL_F16 && p->C % 2 == 0 && p->D % 2 == 0;
+}
+
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N) {
+  if (use_mfma_path(p)) return bwd_weight_mfma_workspace(p, N);
   int64_t S, dp, cp;
   bw_dims(p, N, &S, &dp, &cp);
   if (S == 0) return 0;
@@ -306,6 +315,7 @@ hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const v
                          (int64_t)p->D);
     return hipGetLastError();
   }
+  if (use_mfma_path(p)) return launch_bwd_weight_mfma(p, x, dy, dW, dbias, N, ws, s);
   if (p->dtype == EQL_F16) return launch_bw_t<_Float16>(p, x, dy, dW, dbias, N, ws, s);
   return launch_bw_t<float>(p, x, dy, dW, dbias, N, ws, s);
 }

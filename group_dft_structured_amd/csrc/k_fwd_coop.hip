@@ -293,10 +293,10 @@ hipError_t launch_coop(eqlinear_dtype_t dt, const void* x, const void* spec, con
   // 32-bit buffer offsets: one tile's bytes, and the spectra planes
   if ((int64_t)n_pad * k_pad * 2 >= (1LL << 31)) return hipErrorNotSupported;
   const int ks = k_pad / 32;
-  const int nw = env_int("EQL_COOP_NW", 4);
-  const int nb = env_int("EQL_COOP_NB", ks <= 3 ? 2 : 1);
+  const int nw = env_int("EQL_COOP_NW", 8);
+  const int nb = env_int("EQL_COOP_NB", 1);
   const int mr = env_int("EQL_COOP_MR", 1);
-  const int wpc = env_int("EQL_COOP_WPC", 2);
+  const int wpc = env_int("EQL_COOP_WPC", 1);
 #define EQL_COOP_CASE(NW_, NB_, KS_, MR_) \
   if (nw == NW_ && nb == NB_ && ks == KS_ && mr == MR_) \
     return launch_coop_t<NW_, NB_, KS_, MR_>(x, spec, bias, y, N, K, n_out, n_pad, k_pad, wpc, s);
