@@ -6,7 +6,9 @@ One step = one pass of the whole path over one synthetic batch:
 on the ViT-S-like MLP expansion layer (N = 12608 rows = 64 images x 197
 tokens, C = 96, D = 384 channels per group element, T = 4, binary16 operands
 with fp32 accumulation).  The step is captured once as a HIP graph and
-replayed, so host launch overhead does not enter the timed region.
+replayed K times (the timed region).  Each pass is then timed on its own as
+a graph of back-to-back launches with HIP events on the launch stream, which
+gives every kernel's average launch duration.
 
 Printed: one JSON line.  ``value`` is the metric (forward actual TFLOP/s:
 12*N*C*D flops of the six real products per forward, divided by the
@@ -37,10 +39,20 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--dtype", default=None)
-    ap.add_argument("--kernel-reps", type=int, default=100,
-                    help="launches per captured graph when timing single kernels")
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="launches per graph when timing each pass")
+    ap.add_argument("--kernel-replays", type=int, default=10,
+                    help="timed replays of each pass graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps eagerly (for counter collection)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs found under DIR")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats run found under DIR")
     return ap.parse_args()
 
 
@@ -74,6 +86,15 @@ def read_traffic(kernel_key, src_hash):
 
 def main():
     args = parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -124,11 +145,20 @@ def main():
     with torch.cuda.stream(stream):
         step()  # first set_weight allocates the plan's spectra: outside any capture
         torch.cuda.synchronize()
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step, stream=stream):
-            step()
+        g_step = None
+        if not args.no_graph:
+            g_step = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_step, stream=stream):
+                step()
+
+        def run_step():
+            if args.no_graph:
+                step()
+            else:
+                g_step.replay()
+
         for _ in range(args.warmup):
-            g_step.replay()
+            run_step()
         torch.cuda.synchronize()
 
         # ---- timed region: exactly K steps -------------------------------------
@@ -137,33 +167,38 @@ def main():
         t0 = time.perf_counter()
         ev0.record(stream)
         for _ in range(args.steps):
-            g_step.replay()
+            run_step()
         ev1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         wall_ms = (t1 - t0) * 1e3 / args.steps
         gpu_ms = ev0.elapsed_time(ev1) / args.steps
 
-        # ---- per-kernel average launch duration (HIP events, same stream) --------
+        # ---- kernel timing: each pass as a graph of back-to-back launches, HIP
+        # events around every replay on the launch stream; mean per launch ----
         per_pass_us = {}
-        for name, fn in passes.items():
+        for name, fn in (() if args.no_graph else passes.items()):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for _ in range(args.kernel_reps):
                     fn()
             g.replay()
             torch.cuda.synchronize()
-            best = None
-            for _ in range(5):
+            tot = 0.0
+            for _ in range(args.kernel_replays):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 g.replay()
                 b.record(stream)
                 torch.cuda.synchronize()
-                us = a.elapsed_time(b) * 1e3 / args.kernel_reps
-                best = us if best is None else min(best, us)
-            per_pass_us[name] = best
+                tot += a.elapsed_time(b) * 1e3
+            per_pass_us[name] = tot / (args.kernel_replays * args.kernel_reps)
             del g
+
+    if args.no_graph:  # counter-collection run: no per-kernel timing, no JSON line
+        print(f"eager steps done: {gpu_ms:.4f} ms/step", flush=True)
+        plan.close()
+        return
 
     flops = 12.0 * N * C * D  # six real N x C x D products, 2 flops per MAC
     dense_flops = 32.0 * N * C * D
@@ -216,7 +251,7 @@ def main():
         "data": "synthetic (seeded normal inputs of the workload's shape)",
         "config": {"workload": f"{w.name}: {w.desc}; N={N} C={C} D={D} T={T}",
                    "N": N, "C": C, "D": D, "T": T,
-                   "step": "set_weight + forward + backward_input + backward_weight (HIP graph)"},
+                   "step": "set_weight + forward + backward_input + backward_weight (one HIP graph)"},
         "fwd_tflops_actual": round(value, 2),
         "fwd_tflops_dense_equiv": round(dense_flops / (fwd_us * 1e-6) / 1e12, 2),
         "fwd_mfma_peak_frac": round(value / PEAK_MFMA_TFLOPS[dtype], 4),
@@ -230,6 +265,100 @@ def main():
         out["cpu_baseline"] = cpu_baseline(inp, flops, N, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     plan.close()
+
+
+COPY_BYTES = 512 << 20  # calibration copy: 512 MiB read + 512 MiB written
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size, three times (torch's copy
+    kernel), so that FETCH_SIZE / WRITE_SIZE can be scaled to bytes."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x3", flush=True)
+
+
+def _kernel_role(name):
+    if "k_weight_spectra" in name:
+        return "set_weight"
+    if "k_fwd_coop" in name or "k_fwd_stream" in name:
+        return "forward"
+    if "k_bwd_weight" in name:
+        return "backward_weight"
+    if "k_spectral_gemm" in name:
+        return "forward_or_backward_input"
+    return None
+
+
+def _counter_rows(root, counter):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append(r)
+    return rows
+
+
+def summarize_counters(root, workload):
+    """Per-kernel HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE runs,
+    each scaled by what the counter reads for the plain copy (calibration)."""
+    import collections
+    out = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = collections.defaultdict(list)
+        for r in _counter_rows(root, counter):
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        copy = [v for k, vs in per.items() if "copy" in k.lower() or "elementwise" in k.lower()
+                for v in vs if v * 1024 > COPY_BYTES * 0.5]
+        if not copy:
+            raise SystemExit(f"no calibration copy found for {counter} under {root}")
+        kib_copy = sorted(copy)[len(copy) // 2]
+        factor = COPY_BYTES / (kib_copy * 1024.0)
+        out[counter] = (factor, kib_copy, {k: sum(v) / len(v) for k, v in per.items()})
+    lines = ["# HBM traffic per kernel launch from rocprofv3 counters (MI355X)",
+             f"sources_sha256 all {kernel_sources_hash()}"]
+    for counter, (factor, kib_copy, _) in out.items():
+        lines.append(f"calibration {counter} copy_of_{COPY_BYTES}_bytes reads {kib_copy:.1f} KiB "
+                     f"-> factor {factor:.4f}")
+    names = sorted(set(out["FETCH_SIZE"][2]) & set(out["WRITE_SIZE"][2]))
+    dtype = WORKLOAD_DTYPE.get(workload, "f16")
+    for k in names:
+        role = _kernel_role(k)
+        if role is None:
+            continue
+        fb = out["FETCH_SIZE"][2][k] * 1024 * out["FETCH_SIZE"][0]
+        wb = out["WRITE_SIZE"][2][k] * 1024 * out["WRITE_SIZE"][0]
+        lines.append(f"kernel {k[:100]} fetch_bytes {fb:.0f} write_bytes {wb:.0f}")
+        if role in ("set_weight", "forward", "backward_weight"):
+            lines.append(f"traffic_bytes_per_launch {workload}.{dtype}.{role} {fb + wb:.0f}")
+        elif "k_spectral_gemm" in k:
+            lines.append(f"traffic_bytes_per_launch {workload}.{dtype}.backward_input {fb + wb:.0f}")
+    print("\n".join(lines))
+
+
+def summarize_trace(root):
+    """Average kernel durations from a rocprofv3 --stats run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {root}")
+    print(f"{'avg_us':>10} {'min_us':>10} {'max_us':>10} {'calls':>6}  kernel")
+    for r in csv.DictReader(open(files[0])):
+        if "at::" in r["Name"] or "rocclr" in r["Name"]:
+            continue
+        print(f"{float(r['AverageNs']) / 1e3:10.3f} {float(r['MinNs']) / 1e3:10.3f} "
+              f"{float(r['MaxNs']) / 1e3:10.3f} {r['Calls']:>6}  {r['Name'][:110]}")
+
+
+WORKLOAD_DTYPE = {"vit_s_mlp": "f16", "vit_s_proj": "f16", "swin_stage": "f16", "tiny": "f32",
+                  "vit_s_mlp_bwd": "f16"}
 
 
 def cpu_baseline(inp, flops_per_forward, N, budget_s):
