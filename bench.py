@@ -51,6 +51,8 @@ def parse_args():
                     help="only run a plain device copy of known size (counter calibration)")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs found under DIR")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time every workload/dtype pass and print one JSON line per pass")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run found under DIR")
     return ap.parse_args()
@@ -94,6 +96,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.all_configs:
+        all_configs(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -267,6 +272,86 @@ def main():
     plan.close()
 
 
+def time_graph(fn, stream, reps, replays):
+    """Mean launch duration (us) of fn, from HIP events around replays of a
+    graph holding `reps` back-to-back launches."""
+    import torch
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b) * 1e3
+    return tot / (replays * reps)
+
+
+def all_configs(args):
+    """Every workload of the layer: forward for each dtype, and the backward
+    pair on the backward workload; one JSON line each, with the roofline
+    fraction against the bound the pass's arithmetic intensity selects."""
+    import torch
+    import group_dft_structured_amd as eq
+    from group_dft_structured_amd.workloads import WORKLOADS, make_inputs
+    eq.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    for w in WORKLOADS.values():
+        for dtype in w.dtypes:
+            N, C, D, T = w.N, w.C, w.D, w.T
+            esz = 2 if dtype == "f16" else 4
+            inp = make_inputs(C, D, N, T, dtype=dtype, seed=0, bias=w.bias,
+                              dy="backward" in w.passes)
+            t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items() if v is not None}
+            plan = eq.Plan(C, D, dtype)
+            plan.set_weight(t["W"], t.get("bias"))
+            flops = 12.0 * N * C * D
+            spec = 4 * C * D * esz
+            passes = {}
+            if "forward" in w.passes:
+                y = torch.empty((N, D, T), dtype=t["x"].dtype, device=dev)
+                passes["forward"] = (lambda: plan.forward(t["x"], y),
+                                     N * T * (C + D) * esz + spec + 4 * D)
+            else:
+                dx = torch.empty((N, C, T), dtype=t["x"].dtype, device=dev)
+                dW = torch.empty((D, C, T), dtype=torch.float32, device=dev)
+                db = torch.empty((D,), dtype=torch.float32, device=dev)
+                ws = torch.empty((max(plan.workspace_bytes(N), 16),), dtype=torch.uint8, device=dev)
+                passes["backward_input"] = (lambda: plan.backward_input(t["dy"], dx),
+                                            N * T * (C + D) * esz + spec)
+                passes["backward_weight"] = (lambda: plan.backward_weight(t["x"], t["dy"], dW, db, ws),
+                                             N * T * (C + D) * esz + 4 * D * C * T + 4 * D)
+            big = N * (C + D) * T * esz > (1 << 30)
+            for name, (fn, nbytes) in passes.items():
+                us = time_graph(fn, stream, 3 if big else 20, 3 if big else 10)
+                tf = flops / (us * 1e-6) / 1e12
+                gbps = nbytes / (us * 1e-6) / 1e9
+                ridge = PEAK_MFMA_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+                bound = "hbm" if flops / nbytes < ridge else "mfma"
+                frac = gbps / PEAK_HBM_GBPS if bound == "hbm" else tf / PEAK_MFMA_TFLOPS[dtype]
+                print(json.dumps({"workload": w.name, "N": N, "C": C, "D": D, "dtype": dtype,
+                                  "pass": name, "us": round(us, 3),
+                                  "tflops_actual": round(tf, 2),
+                                  "tflops_dense_equiv": round(tf * 32.0 / 12.0, 2),
+                                  "mfma_peak_frac": round(tf / PEAK_MFMA_TFLOPS[dtype], 4),
+                                  "hbm_gbps": round(gbps, 1), "alg_bytes": nbytes,
+                                  "roofline": {"bound": bound, "frac": round(frac, 4)}}),
+                      flush=True)
+            plan.close()
+            del t, passes
+            torch.cuda.empty_cache()
+
+
 COPY_BYTES = 512 << 20  # calibration copy: 512 MiB read + 512 MiB written
 
 
@@ -282,15 +367,20 @@ def copy_calibration():
     print(f"copied {COPY_BYTES} bytes x3", flush=True)
 
 
+# Which pass each library kernel belongs to on the benchmark workload.
+KERNEL_ROLES = (
+    ("k_weight_spectra", "set_weight"),
+    ("k_fwd_coop", "forward"),
+    ("k_fwd_stream", "forward"),
+    ("k_gemm_kstream", "backward_input"),
+    ("k_bwd_weight", "backward_weight"),  # partial + finish kernels
+)
+
+
 def _kernel_role(name):
-    if "k_weight_spectra" in name:
-        return "set_weight"
-    if "k_fwd_coop" in name or "k_fwd_stream" in name:
-        return "forward"
-    if "k_bwd_weight" in name:
-        return "backward_weight"
-    if "k_spectral_gemm" in name:
-        return "forward_or_backward_input"
+    for key, role in KERNEL_ROLES:
+        if key in name:
+            return role
     return None
 
 
@@ -328,17 +418,17 @@ def summarize_counters(root, workload):
                      f"-> factor {factor:.4f}")
     names = sorted(set(out["FETCH_SIZE"][2]) & set(out["WRITE_SIZE"][2]))
     dtype = WORKLOAD_DTYPE.get(workload, "f16")
+    per_role = {}
     for k in names:
         role = _kernel_role(k)
         if role is None:
             continue
         fb = out["FETCH_SIZE"][2][k] * 1024 * out["FETCH_SIZE"][0]
         wb = out["WRITE_SIZE"][2][k] * 1024 * out["WRITE_SIZE"][0]
-        lines.append(f"kernel {k[:100]} fetch_bytes {fb:.0f} write_bytes {wb:.0f}")
-        if role in ("set_weight", "forward", "backward_weight"):
-            lines.append(f"traffic_bytes_per_launch {workload}.{dtype}.{role} {fb + wb:.0f}")
-        elif "k_spectral_gemm" in k:
-            lines.append(f"traffic_bytes_per_launch {workload}.{dtype}.backward_input {fb + wb:.0f}")
+        lines.append(f"kernel {role} {k[:100]} fetch_bytes {fb:.0f} write_bytes {wb:.0f}")
+        per_role[role] = per_role.get(role, 0.0) + fb + wb
+    for role, b in sorted(per_role.items()):
+        lines.append(f"traffic_bytes_per_launch {workload}.{dtype}.{role} {b:.0f}")
     print("\n".join(lines))
 
 
