@@ -83,7 +83,11 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_coop_f16(
   constexpr int BUF = 4 * PS;                 // halves per buffer
   constexpr int UNITS = RT * (KP / 2);        // 16-byte loads per tile (2 channels each)
   constexpr int UPT = (UNITS + NT - 1) / NT;  // per thread
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF];
+  // units past the tile (when NT does not divide UNITS) write their
+  // butterfly into a per-thread dummy word after the two buffers, so the
+  // transform has no data-dependent branch
+  constexpr int DUMMY = (UNITS % NT != 0) ? 2 * NT : 0;  // halves
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
@@ -145,11 +149,11 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_coop_f16(
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = k * NT + tid;
-      if (UNITS % NT != 0 && u >= UNITS) break;
       const int row = u % RT, cp = u / RT;
       const int c = 2 * cp;
       const int s = c >> 5, gg = (c & 31) >> 3, jj = c & 7;
       const int mb = row >> 4, r16 = row & 15;
+      const bool real = UNITS % NT == 0 || u < UNITS;
       const half8 w = raw[k];
       const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};  // channel c
       const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};  // channel c + 1
@@ -159,11 +163,14 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_coop_f16(
       const float x2b = __builtin_amdgcn_fdot2(b01, pm, __builtin_amdgcn_fdot2(b23, pm, 0.f, false), false);
       const f16x2 da = a01 - a23, db = b01 - b23;  // (Xr, -Xi) of each channel
       const f16x2 xr = {da[0], db[0]}, xi = {-da[1], -db[1]};
-      _Float16* dst = buf + (s * MR + mb) * FRAG + (gg * 16 + r16) * 8 + jj;
-      *reinterpret_cast<uint32_t*>(dst + 0 * PS) = pack2(x0a, x0b);
-      *reinterpret_cast<uint32_t*>(dst + 1 * PS) = pack2(x2a, x2b);
-      *reinterpret_cast<f16x2*>(dst + 2 * PS) = xr;
-      *reinterpret_cast<f16x2*>(dst + 3 * PS) = xi;
+      // every unit stores unconditionally: units past the tile send their
+      // four words to this thread's dummy slot (a select, not a branch)
+      uint32_t* const dummy = reinterpret_cast<uint32_t*>(xs + 2 * BUF) + tid;
+      _Float16* const dst = buf + (s * MR + mb) * FRAG + (gg * 16 + r16) * 8 + jj;
+      *(real ? reinterpret_cast<uint32_t*>(dst + 0 * PS) : dummy) = pack2(x0a, x0b);
+      *(real ? reinterpret_cast<uint32_t*>(dst + 1 * PS) : dummy) = pack2(x2a, x2b);
+      *(real ? reinterpret_cast<uint32_t*>(dst + 2 * PS) : dummy) = __builtin_bit_cast(uint32_t, xr);
+      *(real ? reinterpret_cast<uint32_t*>(dst + 3 * PS) : dummy) = __builtin_bit_cast(uint32_t, xi);
     }
   };
   // products + epilogue of tile t from LDS buffer `buf`
@@ -220,41 +227,81 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_coop_f16(
   // Software pipeline, x prefetched three tiles ahead in a register ring:
   // iteration i computes tile t_i from LDS, loads t_{i+3} into the ring slot
   // t_i used, and moves t_{i+1} (already in registers) through the butterfly
-  // into the other LDS buffer.  Tiles past the end load as zeros.
+  // into the other LDS buffer.  Tiles past the end load as zeros.  The main
+  // loop runs whole rounds of the three ring slots and the last one or two
+  // tiles follow it, so the loop header is entered only with the same set of
+  // loads in flight (no early exit merges into it; the compiler's wait counts
+  // stay exact instead of falling back to waiting on the newest loads).
+  // Scheduling fences keep the three phases (issue the prefetch, products
+  // and stores, butterfly) in program order: interleaving them lets the
+  // compiler hoist butterfly arithmetic, and its waits on loads, into the
+  // products.
+  const int n_my = q < n_rt ? (n_rt - 1 - q) / Q + 1 : 0;  // tiles of this worker
+  if (n_my == 0) return;
+  // In the loop every tile's loads are followed by one tile's worth of
+  // output stores (2*NB*MR per lane).  The prologue issues the same number
+  // of stores after each prefetched tile, aimed outside an empty range (the
+  // hardware drops them without memory traffic), so that the loop header
+  // sees one pending sequence from either side and the compiler can wait on
+  // a tile's loads without also waiting on the tile loaded after it.
+  constexpr int SPT = 2 * NB * MR;
+  const __amdgpu_buffer_rsrc_t rnull = rsrc(y, 0);
+  auto dummy_stores = [&](uint32_t base) {  // distinct offsets: none is a dead store
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) __builtin_amdgcn_raw_buffer_store_b32(0u, rnull, base + 64u * k, 0, 0);
+  };
   half8 ra[UPT], rb[UPT], rc[UPT];
   int t = q;
   load_tile(ra, t);
   load_tile(rb, t + Q);
+  dummy_stores(0x7FFF0000u);
   load_tile(rc, t + 2 * Q);
+  dummy_stores(0x7FFF8000u);
   // The weight, bias and first-tile loads are all in flight together; wait
-  // until only the two prefetched tiles (2*UPT loads) are outstanding, so the
-  // loop starts with the same pending set every iteration leaves behind.
-  static_assert(2 * UPT <= 15, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt((2 * UPT) | (0x7 << 4) | (0xF << 8));
+  // until only the two prefetched tiles and their stores are outstanding.
+  static_assert(2 * (UPT + SPT) <= 63, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(((2 * (UPT + SPT)) & 15) | (0x7 << 4) | (0xF << 8) |
+                             (((2 * (UPT + SPT)) >> 4) << 14));
   store_tile(ra, xs);
   __syncthreads();
   int cur = 0;
-  while (t < n_rt) {
+  for (int i = 3; i <= n_my; i += 3) {
     load_tile(ra, t + 3 * Q);
+    __builtin_amdgcn_sched_barrier(0);
     compute_tile(t, xs + cur * BUF);
+    __builtin_amdgcn_sched_barrier(0);
     store_tile(rb, xs + (cur ^ 1) * BUF);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     cur ^= 1;
     t += Q;
-    if (t >= n_rt) break;
     load_tile(rb, t + 3 * Q);
+    __builtin_amdgcn_sched_barrier(0);
     compute_tile(t, xs + cur * BUF);
+    __builtin_amdgcn_sched_barrier(0);
     store_tile(rc, xs + (cur ^ 1) * BUF);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     cur ^= 1;
     t += Q;
-    if (t >= n_rt) break;
     load_tile(rc, t + 3 * Q);
+    __builtin_amdgcn_sched_barrier(0);
     compute_tile(t, xs + cur * BUF);
+    __builtin_amdgcn_sched_barrier(0);
     store_tile(ra, xs + (cur ^ 1) * BUF);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     cur ^= 1;
     t += Q;
+  }
+  const int rest = n_my % 3;  // tiles left: t (in LDS) and t + Q (in rb)
+  if (rest > 0) {
+    compute_tile(t, xs + cur * BUF);
+    if (rest > 1) {
+      store_tile(rb, xs + (cur ^ 1) * BUF);
+      __syncthreads();
+      compute_tile(t + Q, xs + (cur ^ 1) * BUF);
+    }
   }
 }
 

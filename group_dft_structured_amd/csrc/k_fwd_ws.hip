@@ -1,0 +1,349 @@
+// Forward of the p4 EQ-Linear layer with producer and consumer waves
+// (binary16, reduction widths up to 192 channels).
+//
+// Arithmetic (Flash EQ-Linear, "Approccio Algoritmico" and "Specializzazione
+// per il Gruppo di Rotazione p4"): with the group DFT of x and of the weight,
+//     Y0 = X0 W0   Y2 = X2 W2   Yr = Xr Wr - Xi Wi   Yi = Xr Wi + Xi Wr
+// six real products, then the inverse length-4 butterfly and the bias.
+//
+// Organisation on CDNA4.  A persistent work-group owns BN = 16*NB*NC output
+// channels and walks 16-row tiles of x.  Its waves have one of two roles:
+//  * NP producer waves stream x: range-checked 16-byte buffer loads three
+//    tiles ahead in a register ring, the length-4 butterfly (X0, X2 exact in
+//    fp32 via v_dot2 with +-1, rounded once to binary16; Xr and Xi from one
+//    correctly rounded packed subtraction) and the write of the four planes
+//    to LDS in matrix-core fragment order (double buffered);
+//  * NC consumer waves keep the weight-spectrum fragments of their 16*NB
+//    channels in VGPRs, multiply the tile from LDS on the matrix cores
+//    (16x16x32 f16, fp32 accumulate), apply the inverse butterfly and the
+//    bias in fp32 and store 32 contiguous bytes per lane.
+// The two roles run separate loops that meet at one work-group barrier per
+// tile, so the butterfly of tile i+1 overlaps the products of tile i, and
+// each role's wait counts only see its own memory operations (loads for the
+// producers, stores for the consumers).  Work-groups that read the same x
+// tiles (different channel ranges) sit on the same XCD and share its L2.
+#include "eql_device.h"
+#include "eql_internal.h"
+
+namespace eql {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma16(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// inverse butterfly of one (row, channel) with its bias, fp32
+__device__ __forceinline__ f32x4 epi4(float Y0, float Y2, float Yr, float Yi, float b) {
+  const float u = __builtin_fmaf(Y0, 0.25f, b);
+  const float p = __builtin_fmaf(Y2, 0.25f, u);   // (Y0 + Y2)/4 + b
+  const float m = __builtin_fmaf(Y2, -0.25f, u);  // (Y0 - Y2)/4 + b
+  f32x4 o;
+  o[0] = __builtin_fmaf(Yr, 0.5f, p);
+  o[1] = __builtin_fmaf(Yi, -0.5f, m);
+  o[2] = __builtin_fmaf(Yr, -0.5f, p);
+  o[3] = __builtin_fmaf(Yi, 0.5f, m);
+  return o;
+}
+
+// Raw buffer resource over [base, base + bytes): out-of-range loads return
+// zeros and out-of-range stores are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache policy of the output stores (instruction cache-policy bits): 0 is
+// the default write-back policy, 2 the non-temporal (streaming) hint.  For
+// outputs that fit in the memory-side cache the streaming hint shortens the
+// write-back of dirty L2 lines after the last wave (several microseconds
+// per launch at a few tens of MB); for outputs of a GB it costs bandwidth.
+constexpr int POLICY_DEFAULT = 0, POLICY_STREAM = 2;
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+}  // namespace
+
+// LDS fragment layout (per buffer): plane p (X0, X2, Xr, Xi) and k-step s
+// hold one 1 KB fragment at (p*KS + s)*512 halves; lane (i16, g) of the B
+// operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
+// channels 32s + 8g .. 32s + 8g + 7.
+template <int NC, int NP, int NB, int KS, int YP>
+__global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
+    const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
+    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
+  constexpr int BN = NC * NB * 16;
+  constexpr int KP = KS * 32;
+  constexpr int FRAG = 512;                   // halves per fragment
+  constexpr int PS = KS * FRAG;               // plane stride (halves)
+  constexpr int BUF = 4 * PS;                 // halves per buffer
+  constexpr int PT = NP * 64;                 // producer threads
+  constexpr int UNITS = 16 * (KP / 2);        // 16-byte loads per tile (row, channel pair)
+  constexpr int UPT = (UNITS + PT - 1) / PT;  // per producer thread
+  constexpr int DUMMY = (UNITS % PT != 0) ? 2 * PT : 0;  // halves
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // work-group -> (channel range j, worker q); equal q share an XCD
+  const int wgid = blockIdx.x, xcd = wgid & 7, slot = wgid >> 3;
+  const int j = slot % n_ct;
+  const int q = (slot / n_ct) * 8 + xcd, Q = Qx * 8;
+  const int n_rt = (N + 15) / 16;
+  const int n_my = q < n_rt ? (n_rt - 1 - q) / Q + 1 : 0;  // tiles of this worker
+  if (n_my == 0) return;  // whole work-group
+
+  if (wave >= NC) {
+    // =========================== producer waves ===========================
+    const int ptid = tid - NC * 64;
+    const int64_t row_elems = (int64_t)K * 4;
+    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+    const f16x2 pm = {(_Float16)1.f, (_Float16)-1.f};
+    // unit u -> (row = u % 16, channel pair cp = u / 16): a wave reads 64
+    // contiguous bytes of each of 16 rows
+    auto load_tile = [&](half8 (&raw)[UPT], int i) {
+      const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
+      const int64_t rows = r0 < N ? (N - r0 < 16 ? N - r0 : 16) : 0;
+      const __amdgpu_buffer_rsrc_t rx = rsrc(x + (r0 < N ? r0 : 0) * row_elems, (uint32_t)(rows * row_elems * 2));
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const int u = k * PT + ptid;
+        const int row = u % 16, cp = u / 16;
+        const uint32_t off = (UNITS % PT == 0 || u < UNITS) ? (uint32_t)(row * row_elems + 8 * cp) * 2
+                                                           : 0x7FFFFFF0u;
+        raw[k] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+      }
+    };
+    auto store_tile = [&](const half8 (&raw)[UPT], _Float16* buf) {
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const int u = k * PT + ptid;
+        const int row = u % 16, cp = u / 16;
+        const int c = 2 * cp;
+        const int s = c >> 5, gg = (c & 31) >> 3, jj = c & 7;
+        const bool real = UNITS % PT == 0 || u < UNITS;
+        const half8 w = raw[k];
+        const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};  // channel c
+        const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};  // channel c + 1
+        const float x0a = __builtin_amdgcn_fdot2(a01, ones, __builtin_amdgcn_fdot2(a23, ones, 0.f, false), false);
+        const float x0b = __builtin_amdgcn_fdot2(b01, ones, __builtin_amdgcn_fdot2(b23, ones, 0.f, false), false);
+        const float x2a = __builtin_amdgcn_fdot2(a01, pm, __builtin_amdgcn_fdot2(a23, pm, 0.f, false), false);
+        const float x2b = __builtin_amdgcn_fdot2(b01, pm, __builtin_amdgcn_fdot2(b23, pm, 0.f, false), false);
+        const f16x2 da = a01 - a23, db = b01 - b23;  // (Xr, -Xi) of each channel
+        const f16x2 xr = {da[0], db[0]}, xi = {-da[1], -db[1]};
+        // units past the tile send their words to this thread's dummy slot
+        uint32_t* const dummy = reinterpret_cast<uint32_t*>(xs + 2 * BUF) + ptid;
+        _Float16* const dst = buf + s * FRAG + (gg * 16 + row) * 8 + jj;
+        *(real ? reinterpret_cast<uint32_t*>(dst + 0 * PS) : dummy) = pack2(x0a, x0b);
+        *(real ? reinterpret_cast<uint32_t*>(dst + 1 * PS) : dummy) = pack2(x2a, x2b);
+        *(real ? reinterpret_cast<uint32_t*>(dst + 2 * PS) : dummy) = __builtin_bit_cast(uint32_t, xr);
+        *(real ? reinterpret_cast<uint32_t*>(dst + 3 * PS) : dummy) = __builtin_bit_cast(uint32_t, xi);
+      }
+    };
+    // Ring: tile i sits in slot i % 3 from its load until its butterfly;
+    // between barriers i and i+1 the producers transform tile i+1 and load
+    // tile i+4 into the slot it frees.  Only loads are in flight here, so
+    // the wait before each transform leaves exactly the two younger tiles
+    // (2*UPT loads) outstanding.  Tiles past the end load as zeros.  The
+    // scheduling fences stop the compiler from hoisting a later transform's
+    // arithmetic (and so its wait on younger loads) above a barrier.
+    half8 ra[UPT], rb[UPT], rc[UPT];
+    load_tile(ra, 0);
+    load_tile(rb, 1);
+    load_tile(rc, 2);
+    store_tile(ra, xs);
+    load_tile(ra, 3);
+    __syncthreads();  // barrier 0: tile 0 is in buffer 0
+    int cur = 1;      // buffer of the next tile
+    int i = 0;        // barriers i .. : tile i+1 goes to buffer cur
+    for (; i + 3 <= n_my - 1; i += 3) {
+      store_tile(rb, xs + cur * BUF);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(rb, i + 4);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      cur ^= 1;
+      store_tile(rc, xs + cur * BUF);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(rc, i + 5);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      cur ^= 1;
+      store_tile(ra, xs + cur * BUF);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(ra, i + 6);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      cur ^= 1;
+    }
+    const int rest = n_my - 1 - i;  // 0, 1 or 2 transforms left
+    if (rest > 0) {
+      store_tile(rb, xs + cur * BUF);
+      __syncthreads();
+      cur ^= 1;
+      if (rest > 1) {
+        store_tile(rc, xs + cur * BUF);
+        __syncthreads();
+      }
+    }
+  } else {
+    // =========================== consumer waves ===========================
+    const int i16 = lane & 15, g = lane >> 4;
+    const int d0 = j * BN + wave * NB * 16;  // this wave's first output channel
+    // weight fragments (A operand): channel d0 + 16nb + i16, reduction
+    // channels 32s + 8g .. 32s + 8g + 7
+    half8 w0[NB][KS], w2[NB][KS], wr[NB][KS], wi[NB][KS];
+    float bc[NB][4];
+    {
+      const uint32_t plane_bytes = (uint32_t)n_pad * KP * 2;
+      const int64_t plane = (int64_t)n_pad * KP;
+      const __amdgpu_buffer_rsrc_t r0 = rsrc(spec, plane_bytes), r2 = rsrc(spec + plane, plane_bytes);
+      const __amdgpu_buffer_rsrc_t rr = rsrc(spec + 2 * plane, plane_bytes);
+      const __amdgpu_buffer_rsrc_t ri = rsrc(spec + 3 * plane, plane_bytes);
+      const __amdgpu_buffer_rsrc_t rb = rsrc(bias, (uint32_t)n_pad * 4);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t off = (uint32_t)((d0 + nb * 16 + i16) * KP + 8 * g) * 2;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          w0[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r0, off + s * 64, 0, 0));
+          w2[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r2, off + s * 64, 0, 0));
+          wr[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rr, off + s * 64, 0, 0));
+          wi[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ri, off + s * 64, 0, 0));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          bc[nb][r] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rb, (d0 + nb * 16 + 4 * g + r) * 4, 0, 0));
+      }
+    }
+    // products + epilogue of the i-th tile of this worker from buffer `buf`
+    auto compute_tile = [&](int i, const _Float16* buf) {
+      const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
+      const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+      const __amdgpu_buffer_rsrc_t ry = rsrc(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 8));
+      f32x4 c0[NB], c2[NB], cr[NB], ci[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) c0[nb] = c2[nb] = cr[nb] = ci[nb] = f32x4{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const _Float16* f = buf + s * FRAG + lane * 8;
+        const half8 x0 = *reinterpret_cast<const half8*>(f + 0 * PS);
+        const half8 x2 = *reinterpret_cast<const half8*>(f + 1 * PS);
+        const half8 xr = *reinterpret_cast<const half8*>(f + 2 * PS);
+        const half8 xi = *reinterpret_cast<const half8*>(f + 3 * PS);
+        const half8 xq = -xi;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          c0[nb] = mma16(w0[nb][s], x0, c0[nb]);
+          cr[nb] = mma16(wr[nb][s], xr, cr[nb]);
+          c2[nb] = mma16(w2[nb][s], x2, c2[nb]);
+          ci[nb] = mma16(wi[nb][s], xr, ci[nb]);
+          cr[nb] = mma16(wi[nb][s], xq, cr[nb]);
+          ci[nb] = mma16(wr[nb][s], xi, ci[nb]);
+        }
+      }
+      // lane holds channels d0 + 16nb + 4g + r of row r0 + i16; rows past N
+      // fall outside the store range and are dropped
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t o[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 v = epi4(c0[nb][r], c2[nb][r], cr[nb][r], ci[nb][r], bc[nb][r]);
+          o[2 * r] = pack2(v[0], v[1]);
+          o[2 * r + 1] = pack2(v[2], v[3]);
+        }
+        // channel groups past n_out (last range) would alias the next row:
+        // give them an offset outside the range so the stores are dropped
+        const int col = d0 + nb * 16 + 4 * g;
+        const uint32_t off = col < n_out ? (uint32_t)((i16 * n_out + col) * 8) : 0x7FFFFFF0u;
+        const u32x4 lo = {o[0], o[1], o[2], o[3]}, hi = {o[4], o[5], o[6], o[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(lo, ry, off, 0, YP);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, ry, off + 16, 0, YP);
+      }
+    };
+    __syncthreads();  // barrier 0
+    int cur = 0;
+    for (int i = 0; i < n_my; ++i) {
+      compute_tile(i, xs + cur * BUF);
+      cur ^= 1;
+      if (i + 1 < n_my) __syncthreads();  // barrier i+1
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+static int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+template <int NC, int NP, int NB, int KS>
+static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias, void* y, int64_t N,
+                              int K, int n_out, int n_pad, int wpc, hipStream_t s) {
+  constexpr int BN = NC * NB * 16;
+  const int n_ct = (n_out + BN - 1) / BN;
+  if ((int64_t)n_ct * BN > n_pad) return hipErrorNotSupported;  // weight reads stay in the planes
+  const int64_t n_rt = (N + 15) / 16;
+  int qx = (256 * wpc) / (8 * n_ct);
+  if (qx < 1) qx = 1;
+  const int64_t max_qx = (n_rt + 7) / 8;
+  if (qx > max_qx) qx = (int)(max_qx < 1 ? 1 : max_qx);
+  qx = env_int("EQL_WS_QX", qx);
+  const unsigned blocks = (unsigned)(8 * n_ct * qx);
+  // streaming stores while the output fits well inside the 256 MB memory-side cache
+  const int64_t y_bytes = N * (int64_t)n_out * 8;
+  const bool stream = env_int("EQL_WS_STREAM", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
+  const dim3 grid(blocks), block((NC + NP) * 64);
+  if (stream)
+    hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_STREAM>), grid, block, 0, s, (const _Float16*)x,
+                       (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, n_pad, n_ct, qx);
+  else
+    hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_DEFAULT>), grid, block, 0, s, (const _Float16*)x,
+                       (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, n_pad, n_ct, qx);
+  return hipGetLastError();
+}
+
+// hipErrorNotSupported when outside this kernel's limits.
+hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
+                     int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
+  if (env_int("EQL_NO_WS", 0) || dt != EQL_F16) return hipErrorNotSupported;
+  // exact 32-channel steps (x rows are read without a channel mask) and whole
+  // 4-channel output groups (32-byte stores)
+  if (K != k_pad || K % 32 != 0 || n_out % 4 != 0) return hipErrorNotSupported;
+  // 32-bit buffer offsets: one tile of x and of y, and the spectra planes
+  if ((int64_t)n_pad * k_pad * 2 >= (1LL << 31) || (int64_t)16 * n_out * 8 >= (1LL << 31))
+    return hipErrorNotSupported;
+  const int ks = k_pad / 32;
+  // measured on MI355X: 4 consumer waves of 32 channels for short reductions,
+  // 8 consumer waves of 16 channels (fewer VGPRs per wave) for long ones
+  const bool wide = ks <= 3;
+  const int nc = env_int("EQL_WS_NC", wide ? 4 : 8);
+  const int np = env_int("EQL_WS_NP", 4);
+  const int nb = env_int("EQL_WS_NB", wide ? 2 : 1);
+  const int wpc = env_int("EQL_WS_WPC", 1);
+#define EQL_WS_CASE(NC_, NP_, NB_, KS_) \
+  if (nc == NC_ && np == NP_ && nb == NB_ && ks == KS_) \
+    return launch_ws_t<NC_, NP_, NB_, KS_>(x, spec, bias, y, N, K, n_out, n_pad, wpc, s);
+  EQL_WS_CASE(4, 4, 2, 1)
+  EQL_WS_CASE(4, 4, 2, 2)
+  EQL_WS_CASE(4, 4, 2, 3)
+  EQL_WS_CASE(8, 4, 1, 4)
+  EQL_WS_CASE(8, 4, 1, 5)
+  EQL_WS_CASE(8, 4, 1, 6)
+  EQL_WS_CASE(8, 4, 1, 1)
+  EQL_WS_CASE(8, 4, 1, 2)
+  EQL_WS_CASE(8, 4, 1, 3)
+  EQL_WS_CASE(8, 2, 1, 3)
+  EQL_WS_CASE(4, 4, 1, 3)
+#undef EQL_WS_CASE
+  return hipErrorNotSupported;
+}
+
+}  // namespace eql

@@ -268,7 +268,10 @@ static int pick_cfg(int64_t n_out) {
 }
 
 hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s) {
-  hipError_t e = launch_coop(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
+  hipError_t e = launch_ws(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
+                           (int)p->D, (int)p->fwd.n_pad, s);
+  if (e != hipErrorNotSupported) return e;
+  e = launch_coop(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
                              (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, s);
   if (e != hipErrorNotSupported) return e;
   e = launch_stream(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,

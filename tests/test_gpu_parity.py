@@ -111,11 +111,49 @@ def test_backward_f32_small():
                                    (1, 1, 129), (64, 256, 257), (130, 33, 70), (200, 72, 191),
                                    (96, 384, 3001), (192, 200, 777), (40, 48, 17)])
 def test_forward_ragged(C, D, N, dtype, kernel, monkeypatch):
-    """kernel=auto lets the library pick (streaming kernel where K fits its
-    limits); kernel=tiled forces the tiled LDS kernel for every shape."""
+    """kernel=auto lets the library pick; kernel=tiled forces the tiled LDS
+    kernel for every shape."""
     if kernel == "tiled":
-        monkeypatch.setenv("EQL_NO_STREAM", "1")
+        for k in ("EQL_NO_WS", "EQL_NO_COOP", "EQL_NO_STREAM"):
+            monkeypatch.setenv(k, "1")
     check_forward_full(C, D, N, dtype, seed=C * 1000 + D)
+
+
+# binary16 forward paths forced one at a time (each falls back to the next
+# one in the library's order where a shape is outside its limits)
+F16_PATHS = {
+    "ws_stream": {"EQL_WS_STREAM": "1"},
+    "ws_default": {"EQL_WS_STREAM": "0"},
+    "ws_8x1": {"EQL_WS_NC": "8", "EQL_WS_NB": "1"},
+    "coop": {"EQL_NO_WS": "1"},
+    "stream": {"EQL_NO_WS": "1", "EQL_NO_COOP": "1"},
+}
+
+
+@pytest.mark.parametrize("path", sorted(F16_PATHS))
+@pytest.mark.parametrize("C,D,N", [(8, 8, 1), (32, 4, 17), (64, 256, 257), (96, 96, 1000),
+                                   (96, 384, 3001), (128, 132, 4001), (160, 36, 255),
+                                   (192, 200, 777), (192, 768, 1531)])
+def test_forward_f16_paths(C, D, N, path, monkeypatch):
+    for k, v in F16_PATHS[path].items():
+        monkeypatch.setenv(k, v)
+    check_forward_full(C, D, N, "f16", seed=C * 1000 + D + 7)
+
+
+# every compiled (consumer waves, producer waves, 16-channel blocks per
+# consumer, 32-channel reduction steps) case of the producer/consumer kernel
+WS_CASES = [(4, 4, 2, 1), (4, 4, 2, 2), (4, 4, 2, 3), (8, 4, 1, 1), (8, 4, 1, 2), (8, 4, 1, 3),
+            (8, 4, 1, 4), (8, 4, 1, 5), (8, 4, 1, 6), (8, 2, 1, 3), (4, 4, 1, 3)]
+
+
+@pytest.mark.parametrize("nc,np_,nb,ks", WS_CASES)
+def test_forward_ws_cases(nc, np_, nb, ks, monkeypatch):
+    monkeypatch.setenv("EQL_WS_NC", str(nc))
+    monkeypatch.setenv("EQL_WS_NP", str(np_))
+    monkeypatch.setenv("EQL_WS_NB", str(nb))
+    for stream in ("0", "1"):
+        monkeypatch.setenv("EQL_WS_STREAM", stream)
+        check_forward_full(32 * ks, 260, 1234 + ks, "f16", seed=nc * 100 + ks)
 
 
 @pytest.mark.parametrize("bn,nw", [(32, 4), (64, 4), (64, 8), (128, 4)])
