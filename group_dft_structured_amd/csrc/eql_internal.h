@@ -54,6 +54,17 @@ size_t bwd_weight_mfma_workspace(const eqlinear_plan* p, int64_t N);
 hipError_t launch_bwd_weight_mfma(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
                                   float* dbias, int64_t N, void* ws, hipStream_t s);
 
+// Fixed-order sum of S fp32 partial planes [S][4][c_pad][d_pad] (+ bias
+// partials [S][d_pad]) and the inverse butterfly into dW [D][C][4], dbias [D].
+hipError_t launch_bwd_weight_finish(const float* part, const float* part_b, float* dW, float* dbias,
+                                    int64_t C, int64_t D, int64_t d_pad, int64_t c_pad, int64_t S,
+                                    hipStream_t s);
+// Producer/consumer backward-weight path (binary16, even channel counts, C <= 96).
+bool bws_supported(const eqlinear_plan* p);
+size_t bws_workspace(const eqlinear_plan* p, int64_t N);
+hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, float* dW, float* dbias,
+                      int64_t N, void* ws, hipStream_t s);
+
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
 // Streaming kernel for reduction widths that fit in LDS; hipErrorNotSupported
 // when the shape is outside its limits.

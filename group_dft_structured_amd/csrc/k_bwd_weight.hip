@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * WAVES_D* WAVES_C) void k_bwd_weight_partial(
   const int r_end = min(N, r_begin + rows_per_split);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h = lane >> 5, i32 = lane & 31;
   const int wd = wave / WAVES_C, wc = wave % WAVES_C;
 
@@ -272,7 +272,7 @@ static bool use_mfma_path(const eqlinear_plan* p) {
 }
 
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N) {
-  if (use_mfma_path(p)) return bwd_weight_mfma_workspace(p, N);
+  if (use_mfma_path(p)) return bws_supported(p) ? bws_workspace(p, N) : bwd_weight_mfma_workspace(p, N);
   int64_t S, dp, cp;
   bw_dims(p, N, &S, &dp, &cp);
   if (S == 0) return 0;
@@ -315,7 +315,9 @@ hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const v
                          (int64_t)p->D);
     return hipGetLastError();
   }
-  if (use_mfma_path(p)) return launch_bwd_weight_mfma(p, x, dy, dW, dbias, N, ws, s);
+  if (use_mfma_path(p))
+    return bws_supported(p) ? launch_bws(p, x, dy, dW, dbias, N, ws, s)
+                            : launch_bwd_weight_mfma(p, x, dy, dW, dbias, N, ws, s);
   if (p->dtype == EQL_F16) return launch_bw_t<_Float16>(p, x, dy, dW, dbias, N, ws, s);
   return launch_bw_t<float>(p, x, dy, dW, dbias, N, ws, s);
 }

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(NWD * NWC * 64) void k_bwd_weight_mfma(
   __shared__ __attribute__((aligned(16))) _Float16 lds[2 * BUF];
   __shared__ float bred[8][BD];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
   const int i16 = lane & 15, g = lane >> 4;
   const int T = n_dt * n_ct;
   const int wgid = blockIdx.x, xcd = wgid & 7, slot = wgid >> 3;
@@ -85,10 +86,13 @@ __global__ __launch_bounds__(NWD * NWC * 64) void k_bwd_weight_mfma(
     const int rows = r0 < r_end ? min(32, r_end - r0) : 0;
     const __amdgpu_buffer_rsrc_t rdy = rsrc_bw(dy + (int64_t)r0 * D * 4, (uint32_t)rows * D * 8);
     const __amdgpu_buffer_rsrc_t rx = rsrc_bw(x + (int64_t)r0 * C * 4, (uint32_t)rows * C * 8);
+    static_assert(DUNITS % 64 == 0, "dy and x units split at a wave boundary");
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = k * NT + tid;
-      const bool is_dy = u < DUNITS;
+      // dy or x is decided per wave (DUNITS is a multiple of 64), so the
+      // buffer descriptor is a scalar select, not a per-lane one
+      const bool is_dy = __builtin_amdgcn_readfirstlane(k * NT + wave * 64) < DUNITS;
       const int v = is_dy ? u : u - DUNITS;
       const int np = is_dy ? BD / 2 : BC / 2;  // column pairs
       const int cp = v % np, quart = v / np;
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(NWD * NWC * 64) void k_bwd_weight_mfma(
     for (int k = 0; k < UPT; ++k) {
       const int u = k * NT + tid;
       if (UNITS % NT != 0 && u >= UNITS) break;
-      const bool is_dy = u < DUNITS;
+      const bool is_dy = __builtin_amdgcn_readfirstlane(k * NT + wave * 64) < DUNITS;
       const int v = is_dy ? u : u - DUNITS;
       const int np = is_dy ? BD / 2 : BC / 2;
       const int cp = v % np, quart = v / np;
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(256) void k_bwd_weight_finish(const float* __restri
                                                            float* __restrict__ dbias, int C, int D,
                                                            int d_pad, int c_pad, int S) {
   __shared__ float red[4][5][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_dchunk = (D + 63) / 64;
   const int c = blockIdx.x / n_dchunk, d = (blockIdx.x % n_dchunk) * 64 + lane;
   const bool bias_block = c == 0 && dbias != nullptr;
@@ -302,6 +306,9 @@ static BwmCfg bwm_cfg(int64_t C) {
     case 1: return {1, 3, 4, 1};   // 64 x 48
     case 2: return {1, 3, 2, 2};   // 32 x 96
     case 3: return {1, 3, 8, 1};   // 128 x 48
+    case 4: return {1, 1, 1, 6};   // 16 x 96
+    case 5: return {1, 1, 2, 6};   // 32 x 96
+    case 6: return {1, 2, 1, 3};   // 16 x 96, 3 waves
     default: return {1, 3, 4, 2};  // 64 x 96
   }
 }
@@ -365,10 +372,22 @@ hipError_t launch_bwd_weight_mfma(const eqlinear_plan* p, const void* x, const v
     e = launch_bwm_t<1, 3, 2, 2>(m, p, x, dy, part, part_b, N, s);
   else if (c.db == 1 && c.cb == 3 && c.nwd == 8 && c.nwc == 1)
     e = launch_bwm_t<1, 3, 8, 1>(m, p, x, dy, part, part_b, N, s);
+  else if (c.db == 1 && c.cb == 1 && c.nwd == 1 && c.nwc == 6)
+    e = launch_bwm_t<1, 1, 1, 6>(m, p, x, dy, part, part_b, N, s);
+  else if (c.db == 1 && c.cb == 1 && c.nwd == 2 && c.nwc == 6)
+    e = launch_bwm_t<1, 1, 2, 6>(m, p, x, dy, part, part_b, N, s);
+  else if (c.db == 1 && c.cb == 2 && c.nwd == 1 && c.nwc == 3)
+    e = launch_bwm_t<1, 2, 1, 3>(m, p, x, dy, part, part_b, N, s);
   if (e != hipSuccess) return e;
-  const unsigned fblocks = (unsigned)(p->C * ((p->D + 63) / 64));
+  return launch_bwd_weight_finish(part, part_b, dW, dbias, p->C, p->D, m.d_pad, m.c_pad, m.S, s);
+}
+
+hipError_t launch_bwd_weight_finish(const float* part, const float* part_b, float* dW, float* dbias,
+                                    int64_t C, int64_t D, int64_t d_pad, int64_t c_pad, int64_t S,
+                                    hipStream_t s) {
+  const unsigned fblocks = (unsigned)(C * ((D + 63) / 64));
   hipLaunchKernelGGL(k_bwd_weight_finish, dim3(fblocks), dim3(256), 0, s, part, part_b, dW, dbias,
-                     (int)p->C, (int)p->D, (int)m.d_pad, (int)m.c_pad, (int)m.S);
+                     (int)C, (int)D, (int)d_pad, (int)c_pad, (int)S);
   return hipGetLastError();
 }
 

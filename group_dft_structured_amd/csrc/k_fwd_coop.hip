@@ -89,7 +89,8 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_coop_f16(
   constexpr int DUMMY = (UNITS % NT != 0) ? 2 * NT : 0;  // halves
   __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
   const int i16 = lane & 15, g = lane >> 4;
   // work-group -> (channel range j, worker q); equal q share an XCD
   const int wgid = blockIdx.x, xcd = wgid & 7, slot = wgid >> 3;

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_stream_f16(
   stage_weights<_Float16, BN, NT>(spec, bias, n_pad, KP, col0, SKB, Bs, bs);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, g = lane >> 4;
   const int n_rt = (N + 15) / 16;
   const _Float16* wbase = Bs + i16 * SKB + 8 * g;
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_stream_f32(
   stage_weights<float, BN, NT>(spec, bias, n_pad, KP, col0, SKB, Bs, bs);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, g = lane >> 4;
   const int n_rt = (N + 15) / 16;
   const float* wbase = Bs + i16 * SKB + g * CPL;

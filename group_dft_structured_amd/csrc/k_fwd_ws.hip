@@ -89,7 +89,8 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
   constexpr int DUMMY = (UNITS % PT != 0) ? 2 * PT : 0;  // halves
   __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
   // work-group -> (channel range j, worker q); equal q share an XCD
   const int wgid = blockIdx.x, xcd = wgid & 7, slot = wgid >> 3;
   const int j = slot % n_ct;

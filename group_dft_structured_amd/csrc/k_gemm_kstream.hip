@@ -54,7 +54,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_kstream_f16(
   constexpr int PL = BN * SKB;
   __shared__ __attribute__((aligned(16))) _Float16 Bs[4 * PL];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
   const int i16 = lane & 15, g = lane >> 4;
   const int wgid = blockIdx.x, xcd = wgid & 7, slot = wgid >> 3;
   const int j = slot % n_ct;

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void k_spectral_gemm(
   const int n0 = col_tile * BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h = lane >> 5, i32 = lane & 31;
   const int wr = wave / WAVES_N, wc = wave % WAVES_N;
   const int64_t plane = (int64_t)n_pad * k_pad;

@@ -174,6 +174,34 @@ def test_backward_ragged(C, D, N, dtype):
     _backward_case(C, D, N, dtype, seed=7 + C)
 
 
+# backward-weight paths forced one at a time (binary16)
+BW_PATHS = {
+    "ws_32x96": {"EQL_BWS_CFG": "0"},
+    "ws_16x96": {"EQL_BWS_CFG": "1"},
+    "ws_32x96_np4": {"EQL_BWS_CFG": "2"},
+    "ws_few_splits": {"EQL_BWS_S": "3"},
+    "mfma_64x96": {"EQL_NO_BWS": "1"},
+    "tiled": {"EQL_BW_TILED": "1"},
+}
+
+
+@pytest.mark.parametrize("path", sorted(BW_PATHS))
+@pytest.mark.parametrize("C,D,N", [(2, 2, 1), (32, 34, 95), (96, 384, 3001), (96, 100, 12608),
+                                   (64, 256, 777)])
+def test_backward_weight_paths(C, D, N, path, monkeypatch):
+    for k, v in BW_PATHS[path].items():
+        monkeypatch.setenv(k, v)
+    inp = make_inputs(C, D, N, dtype="f16", seed=C + D + N, bias=True, dy=True)
+    plan = Plan(C, D, "f16")
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    dW, db = plan.backward_weight(to_dev(inp["x"]), to_dev(inp["dy"]))
+    _sync()
+    ref_dW, ref_db = oracle.backward_weight(inp["x"], inp["dy"])
+    e = (rel_err(to_np64(dW), ref_dW), rel_err(to_np64(db), ref_db))
+    print(f"backward_weight {path} C={C} D={D} N={N}: dW {e[0]:.3e} dbias {e[1]:.3e}", flush=True)
+    assert max(e) <= TOL["f16"], e
+
+
 def test_no_bias_equals_zero_bias():
     inp = make_inputs(24, 40, 100, dtype="f32", seed=3, bias=True)
     plan = Plan(24, 40, "f32")
