@@ -74,7 +74,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // hold one 1 KB fragment at (p*KS + s)*512 halves; lane (i16, g) of the B
 // operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
 // channels 32s + 8g .. 32s + 8g + 7.
-template <int NC, int NP, int NB, int KS, int YP>
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
@@ -84,9 +84,15 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
   constexpr int PS = KS * FRAG;               // plane stride (halves)
   constexpr int BUF = 4 * PS;                 // halves per buffer
   constexpr int PT = NP * 64;                 // producer threads
-  constexpr int UNITS = 16 * (KP / 2);        // 16-byte loads per tile (row, channel pair)
-  constexpr int UPT = (UNITS + PT - 1) / PT;  // per producer thread
-  constexpr int DUMMY = (UNITS % PT != 0) ? 2 * PT : 0;  // halves
+  // producer unit: one row and 8 reduction channels (64 contiguous bytes,
+  // four 16-byte loads; its butterfly fills one 16-byte fragment slot per
+  // plane) when G8, else one row and 2 channels (one 16-byte load)
+  constexpr int CPU = G8 ? 8 : 2;                    // channels per unit
+  constexpr int LPU = G8 ? 4 : 1;                    // 16-byte loads per unit
+  constexpr int UNITS = 16 * (KP / CPU);             // units per tile
+  constexpr int UPT = (UNITS + PT - 1) / PT;         // units per producer thread
+  constexpr int LPT = UPT * LPU;                     // loads per producer thread
+  constexpr int DUMMY = (UNITS % PT != 0) ? (G8 ? 8 : 2) * PT : 0;  // halves
   __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -105,56 +111,104 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
     const int64_t row_elems = (int64_t)K * 4;
     const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
     const f16x2 pm = {(_Float16)1.f, (_Float16)-1.f};
-    // unit u -> (row = u % 16, channel pair cp = u / 16): a wave reads 64
-    // contiguous bytes of each of 16 rows
-    auto load_tile = [&](half8 (&raw)[UPT], int i) {
+    // unit u -> (row = u % 16, channel group u / 16): a wave reads 16 rows
+    auto load_tile = [&](half8 (&raw)[LPT], int i) {
       const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
       const int64_t rows = r0 < N ? (N - r0 < 16 ? N - r0 : 16) : 0;
       const __amdgpu_buffer_rsrc_t rx = rsrc(x + (r0 < N ? r0 : 0) * row_elems, (uint32_t)(rows * row_elems * 2));
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const int u = k * PT + ptid;
-        const int row = u % 16, cp = u / 16;
-        const uint32_t off = (UNITS % PT == 0 || u < UNITS) ? (uint32_t)(row * row_elems + 8 * cp) * 2
-                                                           : 0x7FFFFFF0u;
-        raw[k] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        const int row = u % 16, grp = u / 16;
+        const bool real = UNITS % PT == 0 || u < UNITS;
+        const uint32_t off = (uint32_t)(row * row_elems + 4 * CPU * grp) * 2;
+#pragma unroll
+        for (int e = 0; e < LPU; ++e)
+          raw[k * LPU + e] = __builtin_bit_cast(
+              half8, __builtin_amdgcn_raw_buffer_load_b128(rx, real ? off + 16 * e : 0x7FFFFFF0u, 0, 0));
       }
     };
-    auto store_tile = [&](const half8 (&raw)[UPT], _Float16* buf) {
-#pragma unroll
-      for (int k = 0; k < UPT; ++k) {
-        const int u = k * PT + ptid;
-        const int row = u % 16, cp = u / 16;
-        const int c = 2 * cp;
-        const int s = c >> 5, gg = (c & 31) >> 3, jj = c & 7;
-        const bool real = UNITS % PT == 0 || u < UNITS;
-        const half8 w = raw[k];
-        const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};  // channel c
-        const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};  // channel c + 1
+    // butterfly of one 16-byte word (channels c, c + 1, four group values
+    // each) into packed binary16 pairs (X0, X2, Xr, Xi) of the two channels
+    auto bfly = [&](const half8& w, uint32_t& o0, uint32_t& o2, uint32_t& orr, uint32_t& oi) {
+      const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};  // channel c
+      const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};  // channel c + 1
+      if (PACKED) {
+        // pair sums (x0 + x2, x1 + x3) rounded to binary16, then X0 and X2
+        // as their sum and difference: two roundings, about half the
+        // instructions of the exact form
+        const f16x2 sa = a01 + a23, sb = b01 + b23;
+        const f16x2 p = {sa[0], sb[0]}, q = {sa[1], sb[1]};
+        o0 = __builtin_bit_cast(uint32_t, p + q);
+        o2 = __builtin_bit_cast(uint32_t, p - q);
+        const f16x2 a0n1 = {w[0], -w[1]}, na2a3 = {-w[2], w[3]};
+        const f16x2 b0n1 = {w[4], -w[5]}, nb2b3 = {-w[6], w[7]};
+        const f16x2 ra = a0n1 + na2a3, rb = b0n1 + nb2b3;  // (Xr, Xi) of each channel
+        orr = __builtin_bit_cast(uint32_t, f16x2{ra[0], rb[0]});
+        oi = __builtin_bit_cast(uint32_t, f16x2{ra[1], rb[1]});
+      } else {
         const float x0a = __builtin_amdgcn_fdot2(a01, ones, __builtin_amdgcn_fdot2(a23, ones, 0.f, false), false);
         const float x0b = __builtin_amdgcn_fdot2(b01, ones, __builtin_amdgcn_fdot2(b23, ones, 0.f, false), false);
         const float x2a = __builtin_amdgcn_fdot2(a01, pm, __builtin_amdgcn_fdot2(a23, pm, 0.f, false), false);
         const float x2b = __builtin_amdgcn_fdot2(b01, pm, __builtin_amdgcn_fdot2(b23, pm, 0.f, false), false);
+        o0 = pack2(x0a, x0b);
+        o2 = pack2(x2a, x2b);
         const f16x2 da = a01 - a23, db = b01 - b23;  // (Xr, -Xi) of each channel
-        const f16x2 xr = {da[0], db[0]}, xi = {-da[1], -db[1]};
+        orr = __builtin_bit_cast(uint32_t, f16x2{da[0], db[0]});
+        oi = __builtin_bit_cast(uint32_t, f16x2{-da[1], -db[1]});
+      }
+    };
+    auto store_tile = [&](const half8 (&raw)[LPT], _Float16* buf) {
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const int u = k * PT + ptid;
+        const int row = u % 16, grp = u / 16;
+        const int c = CPU * grp;  // first channel of the unit
+        const int s = c >> 5, gg = (c & 31) >> 3, jj = c & 7;
+        const bool real = UNITS % PT == 0 || u < UNITS;
         // units past the tile send their words to this thread's dummy slot
-        uint32_t* const dummy = reinterpret_cast<uint32_t*>(xs + 2 * BUF) + ptid;
+        _Float16* const dummy = xs + 2 * BUF + ptid * (G8 ? 8 : 2);
         _Float16* const dst = buf + s * FRAG + (gg * 16 + row) * 8 + jj;
-        *(real ? reinterpret_cast<uint32_t*>(dst + 0 * PS) : dummy) = pack2(x0a, x0b);
-        *(real ? reinterpret_cast<uint32_t*>(dst + 1 * PS) : dummy) = pack2(x2a, x2b);
-        *(real ? reinterpret_cast<uint32_t*>(dst + 2 * PS) : dummy) = __builtin_bit_cast(uint32_t, xr);
-        *(real ? reinterpret_cast<uint32_t*>(dst + 3 * PS) : dummy) = __builtin_bit_cast(uint32_t, xi);
+        if (G8) {
+          u32x4 v0, v2, vr, vi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t t0, t2, tr, ti;
+            bfly(raw[k * 4 + e], t0, t2, tr, ti);
+            v0[e] = t0;
+            v2[e] = t2;
+            vr[e] = tr;
+            vi[e] = ti;
+          }
+          *reinterpret_cast<u32x4*>(real ? dst + 0 * PS : dummy) = v0;
+          *reinterpret_cast<u32x4*>(real ? dst + 1 * PS : dummy) = v2;
+          *reinterpret_cast<u32x4*>(real ? dst + 2 * PS : dummy) = vr;
+          *reinterpret_cast<u32x4*>(real ? dst + 3 * PS : dummy) = vi;
+        } else {
+          uint32_t v0, v2, vr, vi;
+          bfly(raw[k], v0, v2, vr, vi);
+          *reinterpret_cast<uint32_t*>(real ? dst + 0 * PS : dummy) = v0;
+          *reinterpret_cast<uint32_t*>(real ? dst + 1 * PS : dummy) = v2;
+          *reinterpret_cast<uint32_t*>(real ? dst + 2 * PS : dummy) = vr;
+          *reinterpret_cast<uint32_t*>(real ? dst + 3 * PS : dummy) = vi;
+        }
       }
     };
     // Ring: tile i sits in slot i % 3 from its load until its butterfly;
     // between barriers i and i+1 the producers transform tile i+1 and load
     // tile i+4 into the slot it frees.  Only loads are in flight here, so
     // the wait before each transform leaves exactly the two younger tiles
-    // (2*UPT loads) outstanding.  Tiles past the end load as zeros.  The
+    // (2*LPT loads) outstanding.  Tiles past the end load as zeros.  The
     // scheduling fences stop the compiler from hoisting a later transform's
     // arithmetic (and so its wait on younger loads) above a barrier.
-    half8 ra[UPT], rb[UPT], rc[UPT];
+    half8 ra[LPT], rb[LPT], rc[LPT];
     load_tile(ra, 0);
+    if (STAGGER) {
+      // every work-group's first tile is requested before any second or
+      // third one, so the first tiles are not queued behind the whole
+      // prefetch burst of the grid
+      __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0xF << 8) | (0x0 << 14));  // vmcnt(0)
+    }
     load_tile(rb, 1);
     load_tile(rc, 2);
     store_tile(ra, xs);
@@ -301,13 +355,40 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   // streaming stores while the output fits well inside the 256 MB memory-side cache
   const int64_t y_bytes = N * (int64_t)n_out * 8;
   const bool stream = env_int("EQL_WS_STREAM", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
+  // 8-channel producer units for long reductions (fewer instructions per
+  // tile); the packed butterfly (two roundings of X0, X2) only on request:
+  // it saves little and its error grows with the reduction width
+  const bool packed = env_int("EQL_WS_PACKED", 0) != 0;
+  const bool g8 = env_int("EQL_WS_G8", KS > 6 ? 1 : 0) != 0;
   const dim3 grid(blocks), block((NC + NP) * 64);
-  if (stream)
-    hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_STREAM>), grid, block, 0, s, (const _Float16*)x,
-                       (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, n_pad, n_ct, qx);
-  else
-    hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_DEFAULT>), grid, block, 0, s, (const _Float16*)x,
-                       (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, n_pad, n_ct, qx);
+#define EQL_WS_LAUNCH(YP_, PK_, G8_, ST_)                                                                 \
+  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, PK_, G8_, ST_>), grid, block, 0, s, (const _Float16*)x, \
+                     (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, n_pad, n_ct, qx)
+  const int v = (stream ? 4 : 0) | (packed ? 2 : 0) | (g8 ? 1 : 0);
+  if (env_int("EQL_WS_STAGGER", 1)) {
+    switch (v) {
+      case 0: EQL_WS_LAUNCH(POLICY_DEFAULT, false, false, true); break;
+      case 1: EQL_WS_LAUNCH(POLICY_DEFAULT, false, true, true); break;
+      case 2: EQL_WS_LAUNCH(POLICY_DEFAULT, true, false, true); break;
+      case 3: EQL_WS_LAUNCH(POLICY_DEFAULT, true, true, true); break;
+      case 4: EQL_WS_LAUNCH(POLICY_STREAM, false, false, true); break;
+      case 5: EQL_WS_LAUNCH(POLICY_STREAM, false, true, true); break;
+      case 6: EQL_WS_LAUNCH(POLICY_STREAM, true, false, true); break;
+      default: EQL_WS_LAUNCH(POLICY_STREAM, true, true, true); break;
+    }
+  } else {
+    switch (v) {
+      case 0: EQL_WS_LAUNCH(POLICY_DEFAULT, false, false, false); break;
+      case 1: EQL_WS_LAUNCH(POLICY_DEFAULT, false, true, false); break;
+      case 2: EQL_WS_LAUNCH(POLICY_DEFAULT, true, false, false); break;
+      case 3: EQL_WS_LAUNCH(POLICY_DEFAULT, true, true, false); break;
+      case 4: EQL_WS_LAUNCH(POLICY_STREAM, false, false, false); break;
+      case 5: EQL_WS_LAUNCH(POLICY_STREAM, false, true, false); break;
+      case 6: EQL_WS_LAUNCH(POLICY_STREAM, true, false, false); break;
+      default: EQL_WS_LAUNCH(POLICY_STREAM, true, true, false); break;
+    }
+  }
+#undef EQL_WS_LAUNCH
   return hipGetLastError();
 }
 
@@ -323,9 +404,14 @@ hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const
     return hipErrorNotSupported;
   const int ks = k_pad / 32;
   // measured on MI355X: 4 consumer waves of 32 channels for short reductions,
-  // 8 consumer waves of 16 channels (fewer VGPRs per wave) for long ones
-  const bool wide = ks <= 3;
-  const int nc = env_int("EQL_WS_NC", wide ? 4 : 8);
+  // 8 consumer waves of 16 channels (fewer VGPRs per wave) up to 192
+  // channels, and 4 consumer waves of 16 channels beyond (the weight
+  // fragments of a wave grow with the reduction width)
+  const bool wide = ks <= 3, deep = ks > 6;
+  // long reductions: 3 or 4 consumer waves, whichever pads the output
+  // channels less (ties go to 4)
+  const int pad3 = (n_out + 47) / 48 * 48 - n_out, pad4 = (n_out + 63) / 64 * 64 - n_out;
+  const int nc = env_int("EQL_WS_NC", wide ? 4 : deep ? (pad3 < pad4 ? 3 : 4) : 8);
   const int np = env_int("EQL_WS_NP", 4);
   const int nb = env_int("EQL_WS_NB", wide ? 2 : 1);
   const int wpc = env_int("EQL_WS_WPC", 1);
@@ -343,6 +429,10 @@ hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const
   EQL_WS_CASE(8, 4, 1, 3)
   EQL_WS_CASE(8, 2, 1, 3)
   EQL_WS_CASE(4, 4, 1, 3)
+  EQL_WS_CASE(4, 4, 1, 8)
+  EQL_WS_CASE(4, 4, 1, 12)
+  EQL_WS_CASE(3, 4, 1, 8)
+  EQL_WS_CASE(3, 4, 1, 12)
 #undef EQL_WS_CASE
   return hipErrorNotSupported;
 }

@@ -84,16 +84,33 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_kstream_f16(
   load_step(rC, t, 2);
 
   // ---- weight spectra of the range into LDS (rows past n_pad read as zeros) ----
+  // A fixed, fully unrolled count of 16-byte units per thread: every load is
+  // in flight before the first LDS store (a load-store-load loop would pay
+  // the memory latency once per unit).
   {
     const uint32_t plane_bytes = (uint32_t)n_pad * k_pad * 2;
     const int64_t plane = (int64_t)n_pad * k_pad;
     const int upr = k_pad / 8;  // 16-byte units per row
-    for (int u = tid; u < 4 * BN * upr; u += NT) {
+    const int total = 4 * BN * upr;
+    constexpr int SU = (4 * BN * (KCAP / 8) + NT - 1) / NT;  // units per thread, at most
+    u32x4 v[SU];
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = i * NT + tid;
       const int p = u / (BN * upr), rem = u % (BN * upr);
       const int c = rem / upr, k = (rem % upr) * 8;
-      const __amdgpu_buffer_rsrc_t rp = rsrc_ks(spec + p * plane, plane_bytes);
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(((col0 + c) * k_pad + k) * 2), 0, 0);
-      *reinterpret_cast<u32x4*>(Bs + p * PL + c * SKB + k) = v;
+      const __amdgpu_buffer_rsrc_t rp = rsrc_ks(spec + (p < 4 ? p : 0) * plane, plane_bytes);
+      const uint32_t off = u < total ? (uint32_t)(((col0 + c) * k_pad + k) * 2) : 0x7FFFFFF0u;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = i * NT + tid;
+      if (u < total) {
+        const int p = u / (BN * upr), rem = u % (BN * upr);
+        const int c = rem / upr, k = (rem % upr) * 8;
+        *reinterpret_cast<u32x4*>(Bs + p * PL + c * SKB + k) = v[i];
+      }
     }
   }
   float bc[NOB][4];

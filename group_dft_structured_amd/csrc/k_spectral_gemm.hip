@@ -288,7 +288,10 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
 
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s) {
-  hipError_t e = launch_kstream(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D,
+  hipError_t e = launch_ws(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad,
+                           (int)p->C, (int)p->adj.n_pad, s);
+  if (e != hipErrorNotSupported) return e;
+  e = launch_kstream(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D,
                                 (int)p->adj.k_pad, (int)p->C, (int)p->adj.n_pad, s);
   if (e != hipErrorNotSupported) return e;
   const int cfg = pick_cfg(p->C);

@@ -143,17 +143,25 @@ def test_forward_f16_paths(C, D, N, path, monkeypatch):
 # every compiled (consumer waves, producer waves, 16-channel blocks per
 # consumer, 32-channel reduction steps) case of the producer/consumer kernel
 WS_CASES = [(4, 4, 2, 1), (4, 4, 2, 2), (4, 4, 2, 3), (8, 4, 1, 1), (8, 4, 1, 2), (8, 4, 1, 3),
-            (8, 4, 1, 4), (8, 4, 1, 5), (8, 4, 1, 6), (8, 2, 1, 3), (4, 4, 1, 3)]
+            (8, 4, 1, 4), (8, 4, 1, 5), (8, 4, 1, 6), (8, 2, 1, 3), (4, 4, 1, 3), (4, 4, 1, 8),
+            (4, 4, 1, 12), (3, 4, 1, 8), (3, 4, 1, 12)]
 
 
 @pytest.mark.parametrize("nc,np_,nb,ks", WS_CASES)
 def test_forward_ws_cases(nc, np_, nb, ks, monkeypatch):
+    """Each case with both store policies, both producer unit shapes, both
+    butterfly forms and both prologue orders (output width 264 is not a
+    multiple of any channel range, so the last range is ragged)."""
     monkeypatch.setenv("EQL_WS_NC", str(nc))
     monkeypatch.setenv("EQL_WS_NP", str(np_))
     monkeypatch.setenv("EQL_WS_NB", str(nb))
-    for stream in ("0", "1"):
+    for stream, g8, packed, stagger in (("0", "0", "0", "1"), ("1", "1", "0", "1"), ("0", "1", "1", "0"),
+                                        ("1", "0", "1", "0")):
         monkeypatch.setenv("EQL_WS_STREAM", stream)
-        check_forward_full(32 * ks, 260, 1234 + ks, "f16", seed=nc * 100 + ks)
+        monkeypatch.setenv("EQL_WS_G8", g8)
+        monkeypatch.setenv("EQL_WS_PACKED", packed)
+        monkeypatch.setenv("EQL_WS_STAGGER", stagger)
+        check_forward_full(32 * ks, 264, 1234 + ks, "f16", seed=nc * 100 + ks)
 
 
 @pytest.mark.parametrize("bn,nw", [(32, 4), (64, 4), (64, 8), (128, 4)])
@@ -172,6 +180,30 @@ def test_forward_stream_variants(bn, nw, monkeypatch):
                                    (96, 96, 513)])
 def test_backward_ragged(C, D, N, dtype):
     _backward_case(C, D, N, dtype, seed=7 + C)
+
+
+# backward-input paths forced one at a time (binary16)
+BI_PATHS = {
+    "ws": {},
+    "kstream": {"EQL_NO_WS": "1"},
+    "tiled": {"EQL_NO_WS": "1", "EQL_NO_KSTREAM": "1"},
+}
+
+
+@pytest.mark.parametrize("path", sorted(BI_PATHS))
+@pytest.mark.parametrize("C,D,N", [(96, 384, 12608), (96, 384, 1001), (32, 256, 333), (100, 96, 777),
+                                   (64, 288, 65)])
+def test_backward_input_paths(C, D, N, path, monkeypatch):
+    for k, v in BI_PATHS[path].items():
+        monkeypatch.setenv(k, v)
+    inp = make_inputs(C, D, N, dtype="f16", seed=C * 7 + D + N, bias=True, dy=True)
+    plan = Plan(C, D, "f16")
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    dx = plan.backward_input(to_dev(inp["dy"]))
+    _sync()
+    err = rel_err(to_np64(dx), oracle.backward_input(inp["dy"], inp["W"]))
+    print(f"backward_input {path} C={C} D={D} N={N}: rel err {err:.3e}", flush=True)
+    assert err <= TOL["f16"], err
 
 
 # backward-weight paths forced one at a time (binary16)
