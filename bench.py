@@ -370,8 +370,10 @@ def copy_calibration():
 # Which pass each library kernel belongs to on the benchmark workload.
 KERNEL_ROLES = (
     ("k_weight_spectra", "set_weight"),
+    ("k_fwd_ws", "forward"),
     ("k_fwd_coop", "forward"),
     ("k_fwd_stream", "forward"),
+    ("k_bwd_input_ws", "backward_input"),
     ("k_gemm_kstream", "backward_input"),
     ("k_bwd_weight", "backward_weight"),  # partial + finish kernels
 )

@@ -73,9 +73,10 @@ hipError_t launch_stream(eqlinear_dtype_t dt, const void* a, const void* spec, c
 // Weight-stationary pipelined kernel (binary16, reduction width <= 192).
 hipError_t launch_coop(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias,
                        void* y, int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
-// Producer/consumer forward kernel (binary16, reduction width <= 192).
+// Producer/consumer spectral kernel (binary16): the forward, or with the
+// conjugate-transposed spectra (adjoint = true) the backward-input pass.
 hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                     int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
+                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, hipStream_t s);
 // K-streaming kernel (binary16, weights of the output range in LDS).
 hipError_t launch_kstream(eqlinear_dtype_t dt, const void* a, const void* spec, const float* bias,
                           void* out, int64_t N, int K, int k_pad, int n_out, int n_pad,

@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
 // channels 32s + 8g .. 32s + 8g + 7.
 template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER>
-__global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
+__device__ __forceinline__ void ws_body(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
   constexpr int BN = NC * NB * 16;
@@ -333,6 +333,23 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
   }
 }
 
+// Two entry points share the body so that the passes are told apart in
+// kernel traces: the forward (weight spectra) and the backward-input pass
+// (conjugate-transposed spectra, zero bias).
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER>
+__global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
+    const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
+    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
+  ws_body<NC, NP, NB, KS, YP, PACKED, G8, STAGGER>(x, spec, bias, y, N, K, n_out, n_pad, n_ct, Qx);
+}
+
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER>
+__global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
+    const _Float16* __restrict__ dy, const _Float16* __restrict__ spec, const float* __restrict__ bias,
+    _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
+  ws_body<NC, NP, NB, KS, YP, PACKED, G8, STAGGER>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx);
+}
+
 // ---------------------------------------------------------------------------
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -341,7 +358,7 @@ static int env_int(const char* name, int dflt) {
 
 template <int NC, int NP, int NB, int KS>
 static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias, void* y, int64_t N,
-                              int K, int n_out, int n_pad, int wpc, hipStream_t s) {
+                              int K, int n_out, int n_pad, int wpc, bool adjoint, hipStream_t s) {
   constexpr int BN = NC * NB * 16;
   const int n_ct = (n_out + BN - 1) / BN;
   if ((int64_t)n_ct * BN > n_pad) return hipErrorNotSupported;  // weight reads stay in the planes
@@ -361,9 +378,17 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   const bool packed = env_int("EQL_WS_PACKED", 0) != 0;
   const bool g8 = env_int("EQL_WS_G8", KS > 6 ? 1 : 0) != 0;
   const dim3 grid(blocks), block((NC + NP) * 64);
-#define EQL_WS_LAUNCH(YP_, PK_, G8_, ST_)                                                                 \
-  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, PK_, G8_, ST_>), grid, block, 0, s, (const _Float16*)x, \
-                     (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, n_pad, n_ct, qx)
+#define EQL_WS_LAUNCH(YP_, PK_, G8_, ST_)                                                              \
+  do {                                                                                              \
+    if (adjoint)                                                                                    \
+      hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, NB, KS, YP_, PK_, G8_, ST_>), grid, block, 0, s,  \
+                         (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
+                         n_pad, n_ct, qx);                                                          \
+    else                                                                                            \
+      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, PK_, G8_, ST_>), grid, block, 0, s,        \
+                         (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
+                         n_pad, n_ct, qx);                                                          \
+  } while (0)
   const int v = (stream ? 4 : 0) | (packed ? 2 : 0) | (g8 ? 1 : 0);
   if (env_int("EQL_WS_STAGGER", 1)) {
     switch (v) {
@@ -394,7 +419,7 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
 
 // hipErrorNotSupported when outside this kernel's limits.
 hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                     int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
+                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, hipStream_t s) {
   if (env_int("EQL_NO_WS", 0) || dt != EQL_F16) return hipErrorNotSupported;
   // exact 32-channel steps (x rows are read without a channel mask) and whole
   // 4-channel output groups (32-byte stores)
@@ -417,7 +442,7 @@ hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const
   const int wpc = env_int("EQL_WS_WPC", 1);
 #define EQL_WS_CASE(NC_, NP_, NB_, KS_) \
   if (nc == NC_ && np == NP_ && nb == NB_ && ks == KS_) \
-    return launch_ws_t<NC_, NP_, NB_, KS_>(x, spec, bias, y, N, K, n_out, n_pad, wpc, s);
+    return launch_ws_t<NC_, NP_, NB_, KS_>(x, spec, bias, y, N, K, n_out, n_pad, wpc, adjoint, s);
   EQL_WS_CASE(4, 4, 2, 1)
   EQL_WS_CASE(4, 4, 2, 2)
   EQL_WS_CASE(4, 4, 2, 3)
