@@ -14,7 +14,7 @@ OUT = os.path.join(PKG, "libeqlinear.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["eqlinear_api.hip", "k_spectra.hip", "k_spectral_gemm.hip", "k_fwd_stream.hip", "k_fwd_coop.hip", "k_fwd_ws.hip",
+SOURCES = ["eqlinear_api.hip", "k_spectra.hip", "k_spectral_gemm.hip", "k_fwd_stream.hip", "k_fwd_coop.hip", "k_fwd_ws.hip", "k_fwd_ws32.hip",
            "k_bwd_weight.hip", "k_bwd_weight_mfma.hip", "k_bwd_weight_ws.hip",
            "k_gemm_kstream.hip"]
 

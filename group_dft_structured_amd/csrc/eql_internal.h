@@ -77,6 +77,9 @@ hipError_t launch_coop(eqlinear_dtype_t dt, const void* x, const void* spec, con
 // conjugate-transposed spectra (adjoint = true) the backward-input pass.
 hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
                      int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, hipStream_t s);
+// Producer/consumer forward kernel, binary32 (reduction width a multiple of 16, <= 192).
+hipError_t launch_ws32(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
+                       int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
 // K-streaming kernel (binary16, weights of the output range in LDS).
 hipError_t launch_kstream(eqlinear_dtype_t dt, const void* a, const void* spec, const float* bias,
                           void* out, int64_t N, int K, int k_pad, int n_out, int n_pad,

@@ -207,7 +207,7 @@ __device__ __forceinline__ void ws_body(
       // every work-group's first tile is requested before any second or
       // third one, so the first tiles are not queued behind the whole
       // prefetch burst of the grid
-      __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0xF << 8) | (0x0 << 14));  // vmcnt(0)
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): expcnt, lgkmcnt not waited
     }
     load_tile(rb, 1);
     load_tile(rc, 2);

@@ -271,6 +271,9 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
   hipError_t e = launch_ws(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
                            (int)p->D, (int)p->fwd.n_pad, false, s);
   if (e != hipErrorNotSupported) return e;
+  e = launch_ws32(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, (int)p->D,
+                  (int)p->fwd.n_pad, s);
+  if (e != hipErrorNotSupported) return e;
   e = launch_coop(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
                              (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, s);
   if (e != hipErrorNotSupported) return e;

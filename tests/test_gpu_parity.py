@@ -182,6 +182,32 @@ def test_backward_ragged(C, D, N, dtype):
     _backward_case(C, D, N, dtype, seed=7 + C)
 
 
+# every compiled (consumer waves, producer waves, 16-channel reduction
+# blocks) case of the binary32 producer/consumer forward, both store policies
+WS32_CASES = [(6, 2, 6), (4, 2, 6), (6, 2, 2), (6, 2, 4), (8, 2, 2), (8, 2, 4), (4, 4, 8), (4, 4, 12)]
+
+
+@pytest.mark.parametrize("nc,np_,kb", WS32_CASES)
+def test_forward_ws32_cases(nc, np_, kb, monkeypatch):
+    monkeypatch.setenv("EQL_WS32_NC", str(nc))
+    monkeypatch.setenv("EQL_WS32_NP", str(np_))
+    for stream in ("0", "1"):
+        monkeypatch.setenv("EQL_WS32_STREAM", stream)
+        check_forward_full(16 * kb, 264, 1234 + kb, "f32", seed=nc * 100 + kb)
+
+
+F32_PATHS = {"ws32": {}, "stream": {"EQL_NO_WS32": "1"}, "tiled": {"EQL_NO_WS32": "1", "EQL_NO_STREAM": "1"}}
+
+
+@pytest.mark.parametrize("path", sorted(F32_PATHS))
+@pytest.mark.parametrize("C,D,N", [(16, 4, 3), (96, 96, 12608), (48, 100, 999), (192, 768, 2049),
+                                   (64, 36, 257)])
+def test_forward_f32_paths(C, D, N, path, monkeypatch):
+    for k, v in F32_PATHS[path].items():
+        monkeypatch.setenv(k, v)
+    check_forward_full(C, D, N, "f32", seed=C * 1000 + D + 11)
+
+
 # backward-input paths forced one at a time (binary16)
 BI_PATHS = {
     "ws": {},
