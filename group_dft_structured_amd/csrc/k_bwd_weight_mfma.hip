@@ -266,14 +266,31 @@ __global__ __launch_bounds__(256) void k_bwd_weight_finish(const float* __restri
   float P[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
   if (d < D) {
     const int64_t o = (int64_t)c * d_pad + d;
-#pragma unroll 4
-    for (int s = w; s < S; s += 4) {
-      const float* ps = part + (int64_t)s * 4 * plane + o;
-      P[0] += ps[0];
-      P[1] += ps[plane];
-      P[2] += ps[2 * plane];
-      P[3] += ps[3 * plane];
-      if (bias_block) P[4] += part_b[(int64_t)s * d_pad + d];
+    // chunks of eight splits per wave: all their loads are in flight before
+    // the first add, and the adds keep the split order s = w, w + 4, ...
+    constexpr int IT = 8;
+    for (int s0 = w; s0 < S; s0 += 4 * IT) {
+      float v[IT][5];
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int s = s0 + 4 * i;
+        if (s < S) {
+          const float* ps = part + (int64_t)s * 4 * plane + o;
+          v[i][0] = ps[0];
+          v[i][1] = ps[plane];
+          v[i][2] = ps[2 * plane];
+          v[i][3] = ps[3 * plane];
+          v[i][4] = bias_block ? part_b[(int64_t)s * d_pad + d] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        if (s0 + 4 * i < S) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) P[p] += v[i][p];
+          if (bias_block) P[4] += v[i][4];
+        }
+      }
     }
   }
 #pragma unroll

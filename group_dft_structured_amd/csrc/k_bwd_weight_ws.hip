@@ -190,6 +190,8 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
     // step i+4 into the slot it frees (steps past the split load as zeros).
     half8 ra[UPT][4], rb[UPT][4], rc[UPT][4];
     load_step(ra, 0);
+    // every work-group's first step is requested before any later one
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
     load_step(rb, 1);
     load_step(rc, 2);
     store_step(ra, lds);
@@ -393,6 +395,7 @@ hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, flo
   switch (bws_sel()) {
     case 1: e = launch_bws_t<1, 2, 1, 3, 7>(m, p, x, dy, part, part_b, N, s); break;
     case 2: e = launch_bws_t<2, 2, 1, 3, 4>(m, p, x, dy, part, part_b, N, s); break;
+
     default: e = launch_bws_t<2, 2, 1, 3, 8>(m, p, x, dy, part, part_b, N, s); break;
   }
   if (e != hipSuccess) return e;

@@ -57,11 +57,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 
 // Cache policy of the output stores (instruction cache-policy bits): 0 is
-// the default write-back policy, 2 the non-temporal (streaming) hint.  For
+// the default write-back policy, 2 the non-temporal (streaming) hint, 0x11
+// system scope (sc0 | sc1: written through the L2, used with whole-line
+// stores only).  For
 // outputs that fit in the memory-side cache the streaming hint shortens the
 // write-back of dirty L2 lines after the last wave (several microseconds
 // per launch at a few tens of MB); for outputs of a GB it costs bandwidth.
-constexpr int POLICY_DEFAULT = 0, POLICY_STREAM = 2;
+constexpr int POLICY_DEFAULT = 0, POLICY_STREAM = 2, POLICY_THROUGH = 0x11;
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const f16x2 h = {(_Float16)a, (_Float16)b};
@@ -74,7 +76,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // hold one 1 KB fragment at (p*KS + s)*512 halves; lane (i16, g) of the B
 // operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
 // channels 32s + 8g .. 32s + 8g + 7.
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER>
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER, bool STG>
 __device__ __forceinline__ void ws_body(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
@@ -93,7 +95,10 @@ __device__ __forceinline__ void ws_body(
   constexpr int UPT = (UNITS + PT - 1) / PT;         // units per producer thread
   constexpr int LPT = UPT * LPU;                     // loads per producer thread
   constexpr int DUMMY = (UNITS % PT != 0) ? (G8 ? 8 : 2) * PT : 0;  // halves
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY];
+  // staged epilogue: each consumer wave owns 16 rows x 16*NB channels x 4
+  // group values of output, re-read row-contiguous for whole-line stores
+  constexpr int STW = 16 * 64 * NB;  // halves per consumer wave
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY + (STG ? NC * STW : 0)];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
@@ -305,6 +310,7 @@ __device__ __forceinline__ void ws_body(
       }
       // lane holds channels d0 + 16nb + 4g + r of row r0 + i16; rows past N
       // fall outside the store range and are dropped
+      _Float16* const stg = xs + 2 * BUF + DUMMY + wave * STW;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         uint32_t o[8];
@@ -314,13 +320,36 @@ __device__ __forceinline__ void ws_body(
           o[2 * r] = pack2(v[0], v[1]);
           o[2 * r + 1] = pack2(v[2], v[3]);
         }
-        // channel groups past n_out (last range) would alias the next row:
-        // give them an offset outside the range so the stores are dropped
-        const int col = d0 + nb * 16 + 4 * g;
-        const uint32_t off = col < n_out ? (uint32_t)((i16 * n_out + col) * 8) : 0x7FFFFFF0u;
         const u32x4 lo = {o[0], o[1], o[2], o[3]}, hi = {o[4], o[5], o[6], o[7]};
-        __builtin_amdgcn_raw_buffer_store_b128(lo, ry, off, 0, YP);
-        __builtin_amdgcn_raw_buffer_store_b128(hi, ry, off + 16, 0, YP);
+        if (STG) {
+          // row i16 of the wave's slice, channels 16nb + 4g .. + 3: 32 bytes
+          _Float16* const sp = stg + (i16 * 16 * NB + nb * 16 + 4 * g) * 4;
+          *reinterpret_cast<u32x4*>(sp) = lo;
+          *reinterpret_cast<u32x4*>(sp + 8) = hi;
+        } else {
+          // channel groups past n_out (last range) would alias the next row:
+          // give them an offset outside the range so the stores are dropped
+          const int col = d0 + nb * 16 + 4 * g;
+          const uint32_t off = col < n_out ? (uint32_t)((i16 * n_out + col) * 8) : 0x7FFFFFF0u;
+          __builtin_amdgcn_raw_buffer_store_b128(lo, ry, off, 0, YP);
+          __builtin_amdgcn_raw_buffer_store_b128(hi, ry, off + 16, 0, YP);
+        }
+      }
+      if (STG) {
+        // re-read row-contiguous: a row of the slice is 16*NB channels x 8
+        // bytes = 8*NB lanes of 16 bytes; each store instruction writes
+        // 64/(8*NB) whole row segments
+        constexpr int LPR = 8 * NB;   // lanes per row
+        constexpr int RPP = 64 / LPR; // rows per pass
+        const int lr = lane / LPR, ch = lane % LPR;
+        const int col = d0 + 2 * ch;  // first of the two channels of the chunk
+#pragma unroll
+        for (int pass = 0; pass < 16 / RPP; ++pass) {
+          const int row = pass * RPP + lr;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (row * 16 * NB + 2 * ch) * 4);
+          const uint32_t off = col < n_out ? (uint32_t)((row * n_out + col) * 8) : 0x7FFFFFF0u;
+          __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, YP);
+        }
       }
     };
     __syncthreads();  // barrier 0
@@ -336,18 +365,18 @@ __device__ __forceinline__ void ws_body(
 // Two entry points share the body so that the passes are told apart in
 // kernel traces: the forward (weight spectra) and the backward-input pass
 // (conjugate-transposed spectra, zero bias).
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER>
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STG>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
-  ws_body<NC, NP, NB, KS, YP, PACKED, G8, STAGGER>(x, spec, bias, y, N, K, n_out, n_pad, n_ct, Qx);
+  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG>(x, spec, bias, y, N, K, n_out, n_pad, n_ct, Qx);
 }
 
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER>
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STG>
 __global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
     const _Float16* __restrict__ dy, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
-  ws_body<NC, NP, NB, KS, YP, PACKED, G8, STAGGER>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx);
+  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx);
 }
 
 // ---------------------------------------------------------------------------
@@ -369,9 +398,11 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   if (qx > max_qx) qx = (int)(max_qx < 1 ? 1 : max_qx);
   qx = env_int("EQL_WS_QX", qx);
   const unsigned blocks = (unsigned)(8 * n_ct * qx);
-  // streaming stores while the output fits well inside the 256 MB memory-side cache
+  // streaming stores while the output fits well inside the 256 MB
+  // memory-side cache; beyond, whole-row stores written through the L2
+  // (measured on MI355X: c2 15.1 us streaming vs 16.1 staged; c3 620 us vs 582)
   const int64_t y_bytes = N * (int64_t)n_out * 8;
-  const bool stream = env_int("EQL_WS_STREAM", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
+  const bool small = y_bytes <= (128LL << 20);
   // 8-channel producer units for long reductions (fewer instructions per
   // tile); the packed butterfly (two roundings of X0, X2) only on request:
   // it saves little and its error grows with the reduction width
@@ -389,29 +420,23 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
                          (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
                          n_pad, n_ct, qx);                                                          \
   } while (0)
-  const int v = (stream ? 4 : 0) | (packed ? 2 : 0) | (g8 ? 1 : 0);
-  if (env_int("EQL_WS_STAGGER", 1)) {
-    switch (v) {
-      case 0: EQL_WS_LAUNCH(POLICY_DEFAULT, false, false, true); break;
-      case 1: EQL_WS_LAUNCH(POLICY_DEFAULT, false, true, true); break;
-      case 2: EQL_WS_LAUNCH(POLICY_DEFAULT, true, false, true); break;
-      case 3: EQL_WS_LAUNCH(POLICY_DEFAULT, true, true, true); break;
-      case 4: EQL_WS_LAUNCH(POLICY_STREAM, false, false, true); break;
-      case 5: EQL_WS_LAUNCH(POLICY_STREAM, false, true, true); break;
-      case 6: EQL_WS_LAUNCH(POLICY_STREAM, true, false, true); break;
-      default: EQL_WS_LAUNCH(POLICY_STREAM, true, true, true); break;
-    }
-  } else {
-    switch (v) {
-      case 0: EQL_WS_LAUNCH(POLICY_DEFAULT, false, false, false); break;
-      case 1: EQL_WS_LAUNCH(POLICY_DEFAULT, false, true, false); break;
-      case 2: EQL_WS_LAUNCH(POLICY_DEFAULT, true, false, false); break;
-      case 3: EQL_WS_LAUNCH(POLICY_DEFAULT, true, true, false); break;
-      case 4: EQL_WS_LAUNCH(POLICY_STREAM, false, false, false); break;
-      case 5: EQL_WS_LAUNCH(POLICY_STREAM, false, true, false); break;
-      case 6: EQL_WS_LAUNCH(POLICY_STREAM, true, false, false); break;
-      default: EQL_WS_LAUNCH(POLICY_STREAM, true, true, false); break;
-    }
+  // output store mode: 0 default write-back, 1 streaming, 2 staged through
+  // LDS into whole rows and written through the L2 (system scope)
+  const int mode = env_int("EQL_WS_OUT", small ? 1 : 2);
+  const int v = mode * 4 + (packed ? 2 : 0) + (g8 ? 1 : 0);
+  switch (v) {
+    case 0: EQL_WS_LAUNCH(POLICY_DEFAULT, false, false, false); break;
+    case 1: EQL_WS_LAUNCH(POLICY_DEFAULT, false, true, false); break;
+    case 2: EQL_WS_LAUNCH(POLICY_DEFAULT, true, false, false); break;
+    case 3: EQL_WS_LAUNCH(POLICY_DEFAULT, true, true, false); break;
+    case 4: EQL_WS_LAUNCH(POLICY_STREAM, false, false, false); break;
+    case 5: EQL_WS_LAUNCH(POLICY_STREAM, false, true, false); break;
+    case 6: EQL_WS_LAUNCH(POLICY_STREAM, true, false, false); break;
+    case 7: EQL_WS_LAUNCH(POLICY_STREAM, true, true, false); break;
+    case 8: EQL_WS_LAUNCH(POLICY_THROUGH, false, false, true); break;
+    case 9: EQL_WS_LAUNCH(POLICY_THROUGH, false, true, true); break;
+    case 10: EQL_WS_LAUNCH(POLICY_THROUGH, true, false, true); break;
+    default: EQL_WS_LAUNCH(POLICY_THROUGH, true, true, true); break;
   }
 #undef EQL_WS_LAUNCH
   return hipGetLastError();

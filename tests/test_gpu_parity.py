@@ -122,8 +122,9 @@ def test_forward_ragged(C, D, N, dtype, kernel, monkeypatch):
 # binary16 forward paths forced one at a time (each falls back to the next
 # one in the library's order where a shape is outside its limits)
 F16_PATHS = {
-    "ws_stream": {"EQL_WS_STREAM": "1"},
-    "ws_default": {"EQL_WS_STREAM": "0"},
+    "ws_stream": {"EQL_WS_OUT": "1"},
+    "ws_default": {"EQL_WS_OUT": "0"},
+    "ws_staged": {"EQL_WS_OUT": "2"},
     "ws_8x1": {"EQL_WS_NC": "8", "EQL_WS_NB": "1"},
     "coop": {"EQL_NO_WS": "1"},
     "stream": {"EQL_NO_WS": "1", "EQL_NO_COOP": "1"},
@@ -149,18 +150,17 @@ WS_CASES = [(4, 4, 2, 1), (4, 4, 2, 2), (4, 4, 2, 3), (8, 4, 1, 1), (8, 4, 1, 2)
 
 @pytest.mark.parametrize("nc,np_,nb,ks", WS_CASES)
 def test_forward_ws_cases(nc, np_, nb, ks, monkeypatch):
-    """Each case with both store policies, both producer unit shapes, both
-    butterfly forms and both prologue orders (output width 264 is not a
-    multiple of any channel range, so the last range is ragged)."""
+    """Each case with the three output store modes (write-back, streaming,
+    staged through LDS and written through), both producer unit shapes and
+    both butterfly forms (output width 264 is not a multiple of any channel
+    range, so the last range is ragged)."""
     monkeypatch.setenv("EQL_WS_NC", str(nc))
     monkeypatch.setenv("EQL_WS_NP", str(np_))
     monkeypatch.setenv("EQL_WS_NB", str(nb))
-    for stream, g8, packed, stagger in (("0", "0", "0", "1"), ("1", "1", "0", "1"), ("0", "1", "1", "0"),
-                                        ("1", "0", "1", "0")):
-        monkeypatch.setenv("EQL_WS_STREAM", stream)
+    for out, g8, packed in (("0", "0", "0"), ("1", "1", "0"), ("2", "1", "1"), ("2", "0", "0")):
+        monkeypatch.setenv("EQL_WS_OUT", out)
         monkeypatch.setenv("EQL_WS_G8", g8)
         monkeypatch.setenv("EQL_WS_PACKED", packed)
-        monkeypatch.setenv("EQL_WS_STAGGER", stagger)
         check_forward_full(32 * ks, 264, 1234 + ks, "f16", seed=nc * 100 + ks)
 
 
@@ -237,6 +237,7 @@ BW_PATHS = {
     "ws_32x96": {"EQL_BWS_CFG": "0"},
     "ws_16x96": {"EQL_BWS_CFG": "1"},
     "ws_32x96_np4": {"EQL_BWS_CFG": "2"},
+
     "ws_few_splits": {"EQL_BWS_S": "3"},
     "mfma_64x96": {"EQL_NO_BWS": "1"},
     "tiled": {"EQL_BW_TILED": "1"},
