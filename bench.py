@@ -53,6 +53,8 @@ def parse_args():
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs found under DIR")
     ap.add_argument("--all-configs", action="store_true",
                     help="time every workload/dtype pass and print one JSON line per pass")
+    ap.add_argument("--configs", default=None,
+                    help="with --all-configs: comma-separated workload names to time")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run found under DIR")
     return ap.parse_args()
@@ -84,6 +86,13 @@ def read_traffic(kernel_key, src_hash):
         return None
     v = vals.get(("traffic_bytes_per_launch", kernel_key))
     return float(v) if v is not None else None
+
+
+def real_products(T):
+    """Real matrix products per (row, input channel, output channel) of the
+    group-DFT method: one per real kept frequency (0, and T/2 for even T) and
+    four per complex kept frequency; T = 4 gives the six products of p4."""
+    return 1 + 4 * ((T - 1) // 2) + (1 if T % 2 == 0 else 0)
 
 
 def main():
@@ -131,7 +140,7 @@ def main():
     dx = torch.empty((N, C, T), dtype=tdt, device=dev)
     dW = torch.empty((D, C, T), dtype=torch.float32, device=dev)
     db = torch.empty((D,), dtype=torch.float32, device=dev)
-    plan = eq.Plan(C, D, dtype)
+    plan = eq.Plan(C, D, dtype, T=T)
     ws_bytes = plan.workspace_bytes(N)
     ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
 
@@ -205,9 +214,10 @@ def main():
         plan.close()
         return
 
-    flops = 12.0 * N * C * D  # six real N x C x D products, 2 flops per MAC
-    dense_flops = 32.0 * N * C * D
-    spec_bytes = 4 * C * D * esz
+    # real N x C x D products (six for p4), 2 flops per multiply-accumulate
+    flops = 2.0 * real_products(T) * N * C * D
+    dense_flops = 2.0 * T * T * N * C * D
+    spec_bytes = T * C * D * esz
     bytes_alg = {
         "set_weight": D * C * T * esz + D * esz + 2 * spec_bytes + 4 * D,
         "forward": N * T * (C + D) * esz + spec_bytes + 4 * D,
@@ -306,23 +316,24 @@ def all_configs(args):
     eq.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
-    for w in WORKLOADS.values():
+    names = args.configs.split(",") if args.configs else list(WORKLOADS)
+    for w in (WORKLOADS[n] for n in names):
         for dtype in w.dtypes:
             N, C, D, T = w.N, w.C, w.D, w.T
             esz = 2 if dtype == "f16" else 4
             inp = make_inputs(C, D, N, T, dtype=dtype, seed=0, bias=w.bias,
                               dy="backward" in w.passes)
             t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items() if v is not None}
-            plan = eq.Plan(C, D, dtype)
+            plan = eq.Plan(C, D, dtype, T=T)
             plan.set_weight(t["W"], t.get("bias"))
-            flops = 12.0 * N * C * D
-            spec = 4 * C * D * esz
+            flops = 2.0 * real_products(T) * N * C * D
+            spec = T * C * D * esz
             passes = {}
             if "forward" in w.passes:
                 y = torch.empty((N, D, T), dtype=t["x"].dtype, device=dev)
                 passes["forward"] = (lambda: plan.forward(t["x"], y),
                                      N * T * (C + D) * esz + spec + 4 * D)
-            else:
+            if "backward" in w.passes:
                 dx = torch.empty((N, C, T), dtype=t["x"].dtype, device=dev)
                 dW = torch.empty((D, C, T), dtype=torch.float32, device=dev)
                 db = torch.empty((D,), dtype=torch.float32, device=dev)
@@ -339,10 +350,10 @@ def all_configs(args):
                 ridge = PEAK_MFMA_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
                 bound = "hbm" if flops / nbytes < ridge else "mfma"
                 frac = gbps / PEAK_HBM_GBPS if bound == "hbm" else tf / PEAK_MFMA_TFLOPS[dtype]
-                print(json.dumps({"workload": w.name, "N": N, "C": C, "D": D, "dtype": dtype,
+                print(json.dumps({"workload": w.name, "N": N, "C": C, "D": D, "T": T, "dtype": dtype,
                                   "pass": name, "us": round(us, 3),
                                   "tflops_actual": round(tf, 2),
-                                  "tflops_dense_equiv": round(tf * 32.0 / 12.0, 2),
+                                  "tflops_dense_equiv": round(tf * T * T / real_products(T), 2),
                                   "mfma_peak_frac": round(tf / PEAK_MFMA_TFLOPS[dtype], 4),
                                   "hbm_gbps": round(gbps, 1), "alg_bytes": nbytes,
                                   "roofline": {"bound": bound, "frac": round(frac, 4)}}),

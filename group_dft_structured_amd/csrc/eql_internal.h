@@ -28,14 +28,16 @@ struct SpectraLayout {
 
 struct eqlinear_plan {
   int64_t C, D;
+  int T;        // group size (2..16)
+  bool cyclic;  // served by the cyclic-group kernels (every T but 4, or on request)
   eqlinear_dtype_t dtype;
   size_t esize;  // bytes per element of the plan dtype
   int device;    // device of the spectra, -1 before the first set_weight
   bool has_weight;
-  // Forward operand: 4 planes {W0, W2, Wr, Wi}, each [D_pad][C_pad].
+  // Forward operand: T planes, each [D_pad][C_pad]: for the p4 kernels
+  // {W0, W2, Wr, Wi}, for the cyclic kernels the order of cyc_device.h.
   eql::SpectraLayout fwd;
-  // Backward-input operand: conjugate transpose {W0^T, W2^T, Wr^T, -Wi^T},
-  // each [C_pad][D_pad].
+  // Backward-input operand: the conjugate transposes, each [C_pad][D_pad].
   eql::SpectraLayout adj;
   void* spec_fwd;     // device, plan dtype
   void* spec_adj;     // device, plan dtype
@@ -89,5 +91,16 @@ hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* d
                                  hipStream_t s);
 hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
                                   float* dbias, int64_t N, void* ws, hipStream_t s);
+
+// Cyclic-group kernels (k_cyclic.hip), any group size 2 <= T <= 16.
+namespace cyc {
+size_t workspace_bytes(const eqlinear_plan* p, int64_t N);
+hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
+hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s);
+hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
+                                 hipStream_t s);
+hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
+                                  float* dbias, int64_t N, void* ws, hipStream_t s);
+}  // namespace cyc
 
 }  // namespace eql

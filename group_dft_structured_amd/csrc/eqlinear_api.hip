@@ -22,6 +22,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // the kernels stays in range below these).
 constexpr int64_t MAX_CHANNELS = 1 << 16;
 constexpr int64_t MAX_ROWS = (int64_t)1 << 30;
+// Group sizes with kernels: the cyclic groups C_2 .. C_16.
+constexpr int64_t MIN_T = 2, MAX_T = 16;
 
 eqlinear_status_t check_device(const eqlinear_plan* p) {
   int cur = -1;
@@ -62,7 +64,7 @@ eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T, eqlinear
                                        eqlinear_plan_t* out) {
   if (out == nullptr) return EQL_ERR_INVALID_ARG;
   *out = nullptr;
-  if (T != 4) return EQL_ERR_UNSUPPORTED;
+  if (T < MIN_T || T > MAX_T) return EQL_ERR_UNSUPPORTED;
   if (dtype != EQL_F32 && dtype != EQL_F16) return EQL_ERR_UNSUPPORTED;
   if (C <= 0 || D <= 0 || C > MAX_CHANNELS || D > MAX_CHANNELS) return EQL_ERR_INVALID_ARG;
   eqlinear_plan* p = new (std::nothrow) eqlinear_plan;
@@ -70,6 +72,12 @@ eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T, eqlinear
   memset(p, 0, sizeof(*p));
   p->C = C;
   p->D = D;
+  p->T = (int)T;
+  {
+    // T = 4 runs the p4 kernels unless EQL_CYCLIC_P4 asks for the cyclic ones
+    const char* env = getenv("EQL_CYCLIC_P4");
+    p->cyclic = T != 4 || (env != nullptr && atoi(env) != 0);
+  }
   p->dtype = dtype;
   p->esize = dtype == EQL_F16 ? 2 : 4;
   p->device = -1;
@@ -107,8 +115,8 @@ eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t p, const void* W, const vo
   eqlinear_status_t st = check_device(p);
   if (st != EQL_OK) return st;
   if (p->spec_fwd == nullptr) {
-    const size_t fwd_bytes = 4 * p->fwd.plane_elems() * p->esize;
-    const size_t adj_bytes = 4 * p->adj.plane_elems() * p->esize;
+    const size_t fwd_bytes = (size_t)p->T * p->fwd.plane_elems() * p->esize;
+    const size_t adj_bytes = (size_t)p->T * p->adj.plane_elems() * p->esize;
     const size_t bias_bytes = (size_t)p->fwd.n_pad * sizeof(float);
     const size_t zero_bytes = (size_t)p->adj.n_pad * sizeof(float);
     void* mem = nullptr;
@@ -203,11 +211,14 @@ eqlinear_status_t eqlinear_backward_weight(eqlinear_plan_t p, const void* x, con
 eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t p, int64_t N, int64_t* spectral_macs,
                                       int64_t* dense_macs) {
   if (p == nullptr || N < 0) return EQL_ERR_INVALID_ARG;
-  // p4: frequencies 0 and 2 are real (one product each), frequency 1 is
-  // complex (four real products), frequency 3 is its conjugate (free).
+  // Real DFT of length T: frequency 0 (and T/2 for even T) is real, one
+  // product each; each kept complex frequency 1 <= k < T - k costs four real
+  // products; the others are conjugates (free).  p4: 1 + 4 + 1 = 6 of 16.
+  const int64_t T = p->T;
+  const int64_t products = 1 + 4 * ((T - 1) / 2) + (T % 2 == 0 ? 1 : 0);
   const int64_t ncd = N * p->C * p->D;
-  if (spectral_macs) *spectral_macs = 6 * ncd;
-  if (dense_macs) *dense_macs = 16 * ncd;
+  if (spectral_macs) *spectral_macs = products * ncd;
+  if (dense_macs) *dense_macs = T * T * ncd;
   return EQL_OK;
 }
 

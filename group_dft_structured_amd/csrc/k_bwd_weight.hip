@@ -272,6 +272,7 @@ static bool use_mfma_path(const eqlinear_plan* p) {
 }
 
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N) {
+  if (p->cyclic) return cyc::workspace_bytes(p, N);
   if (use_mfma_path(p)) return bws_supported(p) ? bws_workspace(p, N) : bwd_weight_mfma_workspace(p, N);
   int64_t S, dp, cp;
   bw_dims(p, N, &S, &dp, &cp);
@@ -308,13 +309,14 @@ __global__ void k_zero_f32(float* __restrict__ a, int64_t n) {
 hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
                                   float* dbias, int64_t N, void* ws, hipStream_t s) {
   if (N == 0) {
-    const int64_t n = p->C * p->D * 4;
+    const int64_t n = p->C * p->D * p->T;
     hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dW, n);
     if (dbias)
       hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((p->D + 255) / 256)), dim3(256), 0, s, dbias,
                          (int64_t)p->D);
     return hipGetLastError();
   }
+  if (p->cyclic) return cyc::launch_backward_weight(p, x, dy, dW, dbias, N, ws, s);
   if (use_mfma_path(p))
     return bws_supported(p) ? launch_bws(p, x, dy, dW, dbias, N, ws, s)
                             : launch_bwd_weight_mfma(p, x, dy, dW, dbias, N, ws, s);

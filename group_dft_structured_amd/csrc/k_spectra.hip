@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256) void k_weight_spectra(
 }
 
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s) {
+  if (p->cyclic) return cyc::launch_spectra(p, W, bias, s);
   const int64_t total = (int64_t)p->fwd.plane_elems() + (int64_t)p->adj.plane_elems() +
                         p->fwd.n_pad + p->adj.n_pad;
   const int threads = 256;

@@ -268,6 +268,7 @@ static int pick_cfg(int64_t n_out) {
 }
 
 hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s) {
+  if (p->cyclic) return cyc::launch_forward(p, x, y, N, s);
   hipError_t e = launch_ws(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
                            (int)p->D, (int)p->fwd.n_pad, false, s);
   if (e != hipErrorNotSupported) return e;
@@ -291,6 +292,7 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
 
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s) {
+  if (p->cyclic) return cyc::launch_backward_input(p, dy, dx, N, s);
   hipError_t e = launch_ws(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad,
                            (int)p->C, (int)p->adj.n_pad, true, s);
   if (e != hipErrorNotSupported) return e;

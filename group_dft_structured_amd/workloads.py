@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the p4 EQ-Linear layer.
+"""Seeded synthetic workloads for the EQ-Linear layer (p4 and other cyclic groups).
 
 This module holds the workload shapes and the seeded input generators, and
 nothing of the layer's arithmetic.  It is the one module shared by the oracle
@@ -10,6 +10,8 @@ Flash EQ-ViT / Flash EQ-Swin).  The paper's own operator shapes are not given,
 so ViT-S-like (64 images x 197 tokens, 384 features) and Swin-like
 (64 images x 56 x 56 tokens, 768 features) layers are used, with C and D
 counted per group element (a row holds C*T input and D*T output features).
+The C8 workload keeps the ViT-S-like MLP widths (384 -> 1536 features) on the
+rotation group of order 8, so C and D are half of the p4 ones.
 
 Drawing rule: numpy PCG64 seeded with ``seed``, draws in the order x, W, bias,
 dy, each in fp64, then cast to fp32 and, for fp16 runs, from fp32 to fp16 with
@@ -46,6 +48,10 @@ WORKLOADS = {
                            "Swin-like stage, 64 images x 56x56 tokens, 768->3072 features"),
     "vit_s_mlp_bwd": Workload("vit_s_mlp_bwd", 12608, 96, 384, T_P4, ("f16",), True, ("backward",),
                               "backward of the ViT-S-like MLP expansion (dX, dW, dbias)"),
+    "vit_s_mlp_c8": Workload("vit_s_mlp_c8", 12608, 48, 192, 8, ("f16", "f32"), True,
+                             ("forward", "backward"),
+                             "ViT-S-like MLP expansion on the rotation group C8, "
+                             "64 images x 197 tokens, 384->1536 features"),
 }
 
 _NP_DTYPE = {"f32": np.float32, "f16": np.float16}

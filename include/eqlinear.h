@@ -1,6 +1,7 @@
 /*
- * eqlinear.h -- C ABI of libeqlinear, the p4 equivariant linear layer
- * (EQ-Linear, group size T = 4) on AMD MI355X (gfx950).
+ * eqlinear.h -- C ABI of libeqlinear, the equivariant linear layer
+ * (EQ-Linear) of a cyclic rotation group of order T, 2 <= T <= 16, on AMD
+ * MI355X (gfx950); the p4 group (T = 4) has its own specialised kernels.
  *
  * The operation.  Flash EQ-Linear: Accelerating Equivariant Linear Layers via
  * Group-wise Discrete Fourier Transform (gist.science technical summary,
@@ -9,15 +10,17 @@
  * with a linear map along channels.  With C input and D output channels per
  * group element,
  *
- *     y[n,d,t] = sum_{c<C} sum_{s<4} W[d,c,(t-s) mod 4] * x[n,c,s]  + bias[d]
+ *     y[n,d,t] = sum_{c<C} sum_{s<T} W[d,c,(t-s) mod T] * x[n,c,s]  + bias[d]
  *
  * It is the dense product with the unrolled group-circulant matrix
  * ("Problematica"), computed exactly through a real DFT along the group axis
- * ("Approccio Algoritmico"; "Specializzazione per il Gruppo di Rotazione p4":
- * adds/subtracts for the transforms and six real matrix products).
+ * ("Approccio Algoritmico": one product per kept frequency k <= T/2, 2T - 2
+ * real matrix products for even T and 2T - 1 for odd T;
+ * "Specializzazione per il Gruppo di Rotazione p4": for T = 4 the transforms
+ * are adds/subtracts and there are six real matrix products).
  *
  * Layouts.  Every tensor is dense, row-major, with the group index fastest:
- *     x, dx : [N][C][4]      y, dy : [N][D][4]      W, dW : [D][C][4]
+ *     x, dx : [N][C][T]      y, dy : [N][D][T]      W, dW : [D][C][T]
  *     bias, dbias : [D]
  * x, y, dx, dy, W and bias hold the plan's dtype (EQL_F32 = IEEE binary32,
  * EQL_F16 = IEEE binary16); dW and dbias are always binary32.  Every pointer
@@ -57,7 +60,7 @@ typedef enum { EQL_F32 = 0, EQL_F16 = 1 } eqlinear_dtype_t;
 typedef enum {
   EQL_OK = 0,
   EQL_ERR_INVALID_ARG = 1, /* NULL pointer, C/D <= 0, N < 0, size overflow */
-  EQL_ERR_UNSUPPORTED = 2, /* T != 4 or unknown dtype */
+  EQL_ERR_UNSUPPORTED = 2, /* T outside [2, 16] or unknown dtype */
   EQL_ERR_NO_WEIGHT = 3,   /* forward/backward before set_weight */
   EQL_ERR_MISALIGNED = 4,  /* a buffer is not 16-byte aligned */
   EQL_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
@@ -66,10 +69,12 @@ typedef enum {
 } eqlinear_status_t;
 
 /* Create a plan for C input and D output channels per group element, group
- * size T, and dtype.  The group DFT method is specialised to the p4 group
- * ("Limitazioni e Lavoro Futuro": the implementation covers p4 only), so
- * T != 4 returns EQL_ERR_UNSUPPORTED.  Host-only: allocates no device memory.
- * On success *out holds a new plan. */
+ * size T, and dtype.  T = 4 (the p4 group) runs the specialised p4 kernels;
+ * every other T in [2, 16] runs the cyclic-group kernels (the general method
+ * of "Approccio Algoritmico", of which the pages' own implementation covers
+ * p4 only, "Limitazioni e Lavoro Futuro").  Other T return
+ * EQL_ERR_UNSUPPORTED.  Host-only: allocates no device memory.  On success
+ * *out holds a new plan. */
 eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T,
                                        eqlinear_dtype_t dtype,
                                        eqlinear_plan_t* out);
@@ -78,27 +83,27 @@ eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T,
  * must ensure no call using the plan is still in flight. */
 eqlinear_status_t eqlinear_plan_destroy(eqlinear_plan_t plan);
 
-/* Weight-spectrum precompute (once per weight update).  Reads W[D][C][4] and
+/* Weight-spectrum precompute (once per weight update).  Reads W[D][C][T] and
  * bias[D] (NULL = no bias) in the plan dtype and writes the plan's spectra:
- * the length-4 real DFT of every W[d,c,:] (frequency 0, 2, and the real and
- * imaginary part of frequency 1; frequency 3 is its conjugate, "Approccio
- * Algoritmico": conjugate symmetry of the real DFT) in the layouts the
- * forward and backward kernels read.  On the first call it allocates the
+ * the length-T real DFT of every W[d,c,:], frequencies k <= T/2 only (real
+ * and imaginary parts as T real planes; the others are conjugates,
+ * "Approccio Algoritmico": conjugate symmetry of the real DFT) in the layouts
+ * the forward and backward kernels read.  On the first call it allocates the
  * spectra on the current device (EQL_ERR_ALLOC on failure); later calls
  * must run on the same device. */
 eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t plan, const void* W,
                                       const void* bias, void* stream);
 
-/* Forward: y[N][D][4] from x[N][C][4] (formula above, with the bias given to
- * set_weight).  One fused kernel: group DFT of x in registers, six real
- * products on the matrix cores (fp32 accumulation; binary16 operands for
- * EQL_F16, binary32 for EQL_F32), inverse DFT, bias and the store.  N = 0 is
- * a successful no-op. */
+/* Forward: y[N][D][T] from x[N][C][T] (formula above, with the bias given to
+ * set_weight).  One fused kernel: group DFT of x on chip, the real products
+ * of every kept frequency on the matrix cores (fp32 accumulation; binary16
+ * operands for EQL_F16, binary32 for EQL_F32), inverse DFT, bias and the
+ * store.  N = 0 is a successful no-op. */
 eqlinear_status_t eqlinear_forward(eqlinear_plan_t plan, const void* x, void* y,
                                    int64_t N, void* stream);
 
 /* Backward with respect to the input ("Implementazione": forward and backward
- * passes): dx[n,c,s] = sum_{d,t} W[d,c,(t-s) mod 4] * dy[n,d,t], i.e. the
+ * passes): dx[n,c,s] = sum_{d,t} W[d,c,(t-s) mod T] * dy[n,d,t], i.e. the
  * transpose of the forward map, computed with the conjugate weight spectra.
  * dx has the plan dtype.  N = 0 is a successful no-op. */
 eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t plan, const void* dy,
@@ -109,7 +114,7 @@ eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t plan, const void* dy,
 size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t N);
 
 /* Backward with respect to the weight and bias:
- *     dW[d,c,r] = sum_{n,t} dy[n,d,t] * x[n,c,(t-r) mod 4]   (binary32)
+ *     dW[d,c,r] = sum_{n,t} dy[n,d,t] * x[n,c,(t-r) mod T]   (binary32)
  *     dbias[d]  = sum_{n,t} dy[n,d,t]                          (binary32)
  * i.e. the gradient of every replica of a shared weight summed back onto it.
  * dW and dbias (NULL = not wanted) are overwritten, not accumulated into.
@@ -130,8 +135,9 @@ const char* eqlinear_status_string(eqlinear_status_t st);
 const char* eqlinear_last_error(void);
 
 /* Real multiply-accumulates of one forward over N rows as computed by the
- * library (6*N*C*D for p4) and of the dense unrolled product (16*N*C*D);
- * the ratio is 2(T-1)/T^2 = 3/8 (authors' abstract).  Either pointer may be
+ * library ((2T - 2)*N*C*D for even T, (2T - 1)*N*C*D for odd T; 6*N*C*D for
+ * p4) and of the dense unrolled product (T*T*N*C*D); for even T the ratio is
+ * 2(T-1)/T^2, 3/8 at T = 4 (authors' abstract).  Either pointer may be
  * NULL. */
 eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t plan, int64_t N,
                                       int64_t* spectral_macs, int64_t* dense_macs);

@@ -96,7 +96,7 @@ def _brute_forward(x, W, b):
 def check_brute_force(impl):
     """Direct loops over the circular-convolution sum, tiny sizes, several T."""
     rng = _rng(11)
-    for T in (1, 2, 3, 4, 5, 8):
+    for T in (1, 2, 3, 4, 5, 6, 8, 12, 16):
         for (N, C, D) in ((1, 1, 1), (3, 2, 3), (5, 3, 2)):
             x = rng.standard_normal((N, C, T))
             W = rng.standard_normal((D, C, T))
@@ -110,7 +110,7 @@ def check_brute_force(impl):
 def check_one_hot(impl):
     """C = D = 1 and x = e_s (one-hot on group element s): y = W rolled by s."""
     rng = _rng(12)
-    for T in (4, 5):
+    for T in (4, 5, 8, 16):
         W = rng.standard_normal((1, 1, T))
         for s in range(T):
             x = np.zeros((1, 1, T))
@@ -164,14 +164,15 @@ def check_equivariance(impl):
     """Rolling x along the group axis rolls y the same way (rotation
     equivariance, "Contributi Chiave")."""
     rng = _rng(16)
-    N, C, D, T = 5, 3, 4, 4
-    x = rng.standard_normal((N, C, T))
-    W = rng.standard_normal((D, C, T))
-    b = rng.standard_normal(D)
-    y = np.asarray(impl.forward(x, W, b))
-    for r in range(1, T):
-        yr = np.asarray(impl.forward(np.roll(x, r, axis=2), W, b))
-        assert _rel(yr, np.roll(y, r, axis=2)) < 1e-13, r
+    for T in (3, 4, 8, 16):
+        N, C, D = 5, 3, 4
+        x = rng.standard_normal((N, C, T))
+        W = rng.standard_normal((D, C, T))
+        b = rng.standard_normal(D)
+        y = np.asarray(impl.forward(x, W, b))
+        for r in range(1, T):
+            yr = np.asarray(impl.forward(np.roll(x, r, axis=2), W, b))
+            assert _rel(yr, np.roll(y, r, axis=2)) < 1e-13, (T, r)
 
 
 def _fft_forward(x, W, b):
@@ -186,7 +187,7 @@ def _fft_forward(x, W, b):
 def check_fft_identity(impl):
     """The DFT path (numpy FFT, per-frequency products) equals the layer."""
     rng = _rng(17)
-    for T in (2, 3, 4, 8):
+    for T in (2, 3, 4, 5, 6, 7, 8, 12, 16):
         x = rng.standard_normal((6, 5, T))
         W = rng.standard_normal((7, 5, T))
         b = rng.standard_normal(7)
@@ -202,7 +203,7 @@ def _loss(impl, x, W, b, dy):
 def check_backward_input_adjoint(impl):
     """<dy, f(x)> = <f*(dy), x> for the bias-free layer f."""
     rng = _rng(21)
-    for T in (3, 4):
+    for T in (3, 4, 8, 16):
         x = rng.standard_normal((5, 3, T))
         W = rng.standard_normal((4, 3, T))
         dy = rng.standard_normal((5, 4, T))
@@ -230,13 +231,14 @@ def check_backward_input_fd(impl):
 def check_backward_input_as_forward(impl):
     """dx equals a forward with the adjoint weight W*[c,d,u] = W[d,c,(-u) mod T]."""
     rng = _rng(23)
-    N, C, D, T = 6, 3, 5, 4
-    W = rng.standard_normal((D, C, T))
-    dy = rng.standard_normal((N, D, T))
-    Wadj = np.empty((C, D, T))
-    for u in range(T):
-        Wadj[:, :, u] = W[:, :, (-u) % T].T
-    assert _rel(impl.backward_input(dy, W), _brute_forward(dy, Wadj, None)) < 1e-13
+    for T in (4, 8, 13):
+        N, C, D = 6, 3, 5
+        W = rng.standard_normal((D, C, T))
+        dy = rng.standard_normal((N, D, T))
+        Wadj = np.empty((C, D, T))
+        for u in range(T):
+            Wadj[:, :, u] = W[:, :, (-u) % T].T
+        assert _rel(impl.backward_input(dy, W), _brute_forward(dy, Wadj, None)) < 1e-13, T
 
 
 def check_backward_weight_fd(impl):
@@ -265,7 +267,7 @@ def check_backward_weight_fd(impl):
 def check_backward_weight_brute(impl):
     """dW[d,c,r] = sum_{n,t} dy[n,d,t] x[n,c,(t-r) mod T], by direct loops."""
     rng = _rng(25)
-    for T in (3, 4):
+    for T in (3, 4, 8, 16):
         N, C, D = 4, 3, 2
         x = rng.standard_normal((N, C, T))
         dy = rng.standard_normal((N, D, T))

@@ -47,8 +47,12 @@ def _raw_plan(lib, C=8, D=8, T=4, dtype=eq.EQL_F32):
 
 def test_plan_create_validation():
     lib = _lib()
-    assert _raw_plan(lib, T=8)[0] == 2          # EQL_ERR_UNSUPPORTED: p4 only
-    assert _raw_plan(lib, T=2)[0] == 2
+    for T in (-4, 0, 1, 17, 32):                # EQL_ERR_UNSUPPORTED: cyclic groups C_2 .. C_16
+        assert _raw_plan(lib, T=T)[0] == 2
+    for T in (2, 3, 8, 16):
+        st, h = _raw_plan(lib, T=T)
+        assert st == 0 and h
+        assert lib.eqlinear_plan_destroy(h) == 0
     assert _raw_plan(lib, dtype=7)[0] == 2
     assert _raw_plan(lib, C=0)[0] == 1          # EQL_ERR_INVALID_ARG
     assert _raw_plan(lib, D=-3)[0] == 1
@@ -101,12 +105,35 @@ def test_mac_counts_and_ratio():
         eq.eqlinear_plan_destroy(p)
 
 
+def test_mac_counts_every_group_size():
+    # Kept frequencies of a real DFT of length T are those numpy's rfft
+    # returns; frequency 0 (and T/2 for even T) is real and costs one real
+    # product per (n, c, d), every other kept frequency is complex and costs
+    # four.  The unrolled dense weight costs T^2.
+    import numpy as np
+    _lib()
+    for T in range(2, 17):
+        kept = np.fft.rfft(np.zeros(T)).shape[0]
+        real = 1 + (T % 2 == 0)
+        products = real + 4 * (kept - real)
+        p = eq.eqlinear_plan_create(5, 7, T, eq.EQL_F32)
+        try:
+            s, d = eq.eqlinear_mac_counts(p, 3)
+            assert s == products * 3 * 5 * 7 and d == T * T * 3 * 5 * 7
+            # about 2/T of the dense count, exactly 2(T-1)/T^2 for even T
+            assert 2 * T - 2 <= products <= 2 * T - 1
+            if T % 2 == 0:
+                assert s * T * T == d * 2 * (T - 1)
+        finally:
+            eq.eqlinear_plan_destroy(p)
+
+
 def test_status_strings_and_python_errors():
     _lib()
     for code in range(8):
         assert eq.eqlinear_status_string(code)
     with pytest.raises(eq.EqlinearError) as ei:
-        eq.eqlinear_plan_create(8, 8, 3, eq.EQL_F32)
+        eq.eqlinear_plan_create(8, 8, 17, eq.EQL_F32)
     assert ei.value.name == "EQL_ERR_UNSUPPORTED"
 
 
@@ -118,3 +145,10 @@ def test_workspace_grows_with_rows():
         assert sizes[0] == 0 and 0 < sizes[1] <= sizes[2] <= sizes[3]
     finally:
         eq.eqlinear_plan_destroy(p)
+    for T in (3, 8, 16):
+        p = eq.eqlinear_plan_create(48, 192, T, eq.EQL_F16)
+        try:
+            sizes = [eq.eqlinear_backward_weight_workspace(p, n) for n in (0, 1, 600, 12608)]
+            assert sizes[0] == 0 and 0 < sizes[1] <= sizes[2] <= sizes[3]
+        finally:
+            eq.eqlinear_plan_destroy(p)
