@@ -30,6 +30,9 @@ struct eqlinear_plan {
   int64_t C, D;
   int T;        // group size (2..16)
   bool cyclic;  // served by the cyclic-group kernels (every T but 4, or on request)
+  // cyclic backward_weight: tile edge (64 or 32) and work-group target, fixed
+  // at plan creation so that workspace size and launch always agree
+  int cyc_bw_tile, cyc_bw_wgs;
   eqlinear_dtype_t dtype;
   size_t esize;  // bytes per element of the plan dtype
   int device;    // device of the spectra, -1 before the first set_weight

@@ -77,6 +77,10 @@ eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T, eqlinear
     // T = 4 runs the p4 kernels unless EQL_CYCLIC_P4 asks for the cyclic ones
     const char* env = getenv("EQL_CYCLIC_P4");
     p->cyclic = T != 4 || (env != nullptr && atoi(env) != 0);
+    const char* tile = getenv("EQL_CYC_BW_TILE");
+    p->cyc_bw_tile = (tile != nullptr && atoi(tile) == 64 && T <= 8) ? 64 : 32;
+    const char* wgs = getenv("EQL_CYC_BW_WGS");
+    p->cyc_bw_wgs = (wgs != nullptr && atoi(wgs) > 0) ? atoi(wgs) : 512;
   }
   p->dtype = dtype;
   p->esize = dtype == EQL_F16 ? 2 : 4;

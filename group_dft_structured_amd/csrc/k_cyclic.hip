@@ -33,6 +33,8 @@
 //    matrix cores; fp32 partials per split.  The finish kernel sums the
 //    splits in order, applies the inverse DFT (dW[r] is the inverse DFT of
 //    P at r) and sums the bias partials (dbias = sum_n G[0]).
+#include <stdlib.h>
+
 #include "cyc_device.h"
 #include "eql_device.h"
 #include "eql_internal.h"
@@ -584,11 +586,6 @@ __global__ __launch_bounds__(256) void k_cyc_bwf(const float* __restrict__ part,
 }
 
 // ---- host side -------------------------------------------------------------
-template <int T>
-constexpr int tile_of() {
-  return T <= 8 ? 64 : 32;
-}
-
 struct BwDims {
   int64_t S, rows_per_split;
   int TD, d_pad, c_pad, d_tiles, c_tiles;
@@ -596,15 +593,16 @@ struct BwDims {
 
 BwDims bw_dims(const eqlinear_plan* p, int64_t N) {
   BwDims b;
-  b.TD = p->T <= 8 ? 64 : 32;
+  b.TD = p->cyc_bw_tile;
   b.d_tiles = (int)((p->D + b.TD - 1) / b.TD);
   b.c_tiles = (int)((p->C + b.TD - 1) / b.TD);
   b.d_pad = b.d_tiles * b.TD;
   b.c_pad = b.c_tiles * b.TD;
   const int64_t tiles = (int64_t)b.d_tiles * b.c_tiles;
-  // about two work-groups per compute unit, at least 256 rows per split
-  int64_t S = (512 + tiles - 1) / tiles;
-  const int64_t smax = N / 256 > 1 ? N / 256 : 1;
+  // about cyc_bw_wgs work-groups (two per compute unit by default), at least
+  // 128 rows per split
+  int64_t S = (p->cyc_bw_wgs + tiles - 1) / tiles;
+  const int64_t smax = N / 128 > 1 ? N / 128 : 1;
   if (S > smax) S = smax;
   if (S < 1) S = 1;
   b.rows_per_split = (N + S - 1) / S;
@@ -613,10 +611,9 @@ BwDims bw_dims(const eqlinear_plan* p, int64_t N) {
   return b;
 }
 
-template <int T, typename DT>
-hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, void* out, int64_t N,
-                         int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
-  constexpr int BM = tile_of<T>(), BN = tile_of<T>();
+template <int T, typename DT, int BM, int BN>
+hipError_t launch_gemm_tile(const void* a, const void* spec, const float* bias, void* out,
+                            int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
   const int64_t row_tiles = (N + BM - 1) / BM;
   const int col_tiles = (n_out + BN - 1) / BN;
   const int64_t tiles = row_tiles * col_tiles;
@@ -628,11 +625,35 @@ hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, voi
   return hipGetLastError();
 }
 
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v != nullptr && *v) ? atoi(v) : dflt;
+}
+
+// Tile shapes (rows x output channels): 0 = 64x64, 1 = 64x32, 2 = 32x64,
+// 3 = 32x32 (EQL_CYC_TILE overrides the default).
 template <int T, typename DT>
-hipError_t launch_bw_t(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
-                       float* dbias, int64_t N, void* ws, hipStream_t s) {
-  constexpr int TD = tile_of<T>();
+hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, void* out, int64_t N,
+                         int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
+  int cfg = env_int("EQL_CYC_TILE", T <= 8 && sizeof(DT) == 2 ? 2 : 3);
+  if (T > 8 && cfg == 0) cfg = 3;
+  switch (cfg) {
+    case 0:
+      if constexpr (T <= 8)
+        return launch_gemm_tile<T, DT, 64, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
+      return hipErrorInvalidValue;
+    case 1: return launch_gemm_tile<T, DT, 64, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
+    case 2: return launch_gemm_tile<T, DT, 32, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
+    case 3: return launch_gemm_tile<T, DT, 32, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int T, typename DT, int TD>
+hipError_t launch_bw_tile(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
+                          float* dbias, int64_t N, void* ws, hipStream_t s) {
   const BwDims b = bw_dims(p, N);
+  if (b.TD != TD) return hipErrorInvalidValue;
   float* part = (float*)ws;
   float* part_b = part + b.S * T * (int64_t)b.d_pad * b.c_pad;
   const int64_t n_tiles = b.S * b.d_tiles * b.c_tiles;
@@ -647,6 +668,15 @@ hipError_t launch_bw_t(const eqlinear_plan* p, const void* x, const void* dy, fl
   hipLaunchKernelGGL(k_cyc_bwf<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
                      part_b, dW, dbias, (int)p->C, (int)p->D, b.d_pad, b.c_pad, (int)b.S);
   return hipGetLastError();
+}
+
+template <int T, typename DT>
+hipError_t launch_bw_t(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
+                       float* dbias, int64_t N, void* ws, hipStream_t s) {
+  if constexpr (T <= 8) {
+    if (p->cyc_bw_tile == 64) return launch_bw_tile<T, DT, 64>(p, x, dy, dW, dbias, N, ws, s);
+  }
+  return launch_bw_tile<T, DT, 32>(p, x, dy, dW, dbias, N, ws, s);
 }
 
 template <int T, typename DT>

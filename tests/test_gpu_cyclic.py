@@ -135,3 +135,30 @@ def test_cyclic_zero_rows_and_determinism():
     for a, b in zip(*outs):
         assert torch.equal(a, b)
     plan.close()
+
+
+# every tile shape of the cyclic matrix-core kernel (rows x output channels:
+# 0 = 64x64 for T <= 8, 1 = 64x32, 2 = 32x64, 3 = 32x32)
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("T,dtype", [(3, "f32"), (8, "f16"), (8, "f32"), (12, "f16")])
+def test_cyclic_tiles(tile, T, dtype, monkeypatch):
+    monkeypatch.setenv("EQL_CYC_TILE", str(tile))
+    _forward_case(33, 70, 517, T, dtype, seed=11)
+    inp = make_inputs(33, 70, 517, T, dtype=dtype, seed=12, bias=True, dy=True)
+    plan = Plan(33, 70, dtype, T=T)
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    dx = plan.backward_input(to_dev(inp["dy"]))
+    _sync()
+    err = rel_err(to_np64(dx), oracle.backward_input(inp["dy"], inp["W"]))
+    assert err <= TOL[dtype], err
+    plan.close()
+
+
+# backward_weight tile edges (64 only for T <= 8) and work-group targets,
+# which set the number of row splits
+@pytest.mark.parametrize("bw_tile,bw_wgs", [(32, 512), (64, 512), (32, 64), (32, 2048)])
+@pytest.mark.parametrize("T,dtype", [(3, "f32"), (8, "f16"), (12, "f32")])
+def test_cyclic_backward_weight_configs(bw_tile, bw_wgs, T, dtype, monkeypatch):
+    monkeypatch.setenv("EQL_CYC_BW_TILE", str(bw_tile))
+    monkeypatch.setenv("EQL_CYC_BW_WGS", str(bw_wgs))
+    _backward_case(70, 45, 1500, T, dtype, seed=13)
