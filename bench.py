@@ -333,6 +333,9 @@ def all_configs(args):
                 y = torch.empty((N, D, T), dtype=t["x"].dtype, device=dev)
                 passes["forward"] = (lambda: plan.forward(t["x"], y),
                                      N * T * (C + D) * esz + spec + 4 * D)
+                # forward with the GELU fused into the epilogue (same bytes)
+                passes["forward_gelu"] = (lambda: plan.forward(t["x"], y, act="gelu"),
+                                          N * T * (C + D) * esz + spec + 4 * D)
             if "backward" in w.passes:
                 dx = torch.empty((N, C, T), dtype=t["x"].dtype, device=dev)
                 dW = torch.empty((D, C, T), dtype=torch.float32, device=dev)

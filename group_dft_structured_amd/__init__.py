@@ -1,4 +1,5 @@
-"""Python binding of libeqlinear, the p4 EQ-Linear layer on MI355X (gfx950).
+"""Python binding of libeqlinear, the EQ-Linear layer of the cyclic rotation
+groups (p4 and C_2 .. C_16) on MI355X (gfx950).
 
 Argument marshalling only: every step of the layer runs in the HIP kernels of
 ``libeqlinear.so``.  PyTorch supplies device memory and streams; the functions
@@ -17,6 +18,12 @@ LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
 EQL_F32 = 0
 EQL_F16 = 1
 
+EQL_ACT_NONE = 0
+EQL_ACT_GELU = 1
+EQL_ACT_GELU_TANH = 2
+ACTIVATIONS = {None: EQL_ACT_NONE, "none": EQL_ACT_NONE, "gelu": EQL_ACT_GELU,
+               "gelu_tanh": EQL_ACT_GELU_TANH}
+
 STATUS = {
     0: "EQL_OK",
     1: "EQL_ERR_INVALID_ARG",
@@ -33,6 +40,7 @@ EXPORTED = (
     "eqlinear_plan_destroy",
     "eqlinear_set_weight",
     "eqlinear_forward",
+    "eqlinear_forward_act",
     "eqlinear_backward_input",
     "eqlinear_backward_weight_workspace",
     "eqlinear_backward_weight",
@@ -77,6 +85,8 @@ def load_library(path=LIB_PATH):
     lib.eqlinear_set_weight.restype = st
     lib.eqlinear_forward.argtypes = [vp, vp, vp, i64, vp]
     lib.eqlinear_forward.restype = st
+    lib.eqlinear_forward_act.argtypes = [vp, vp, vp, i64, ctypes.c_int, vp]
+    lib.eqlinear_forward_act.restype = st
     lib.eqlinear_backward_input.argtypes = [vp, vp, vp, i64, vp]
     lib.eqlinear_backward_input.restype = st
     lib.eqlinear_backward_weight_workspace.argtypes = [vp, i64]
@@ -140,6 +150,11 @@ def eqlinear_set_weight(plan, W, bias=None, stream=None):
 def eqlinear_forward(plan, x, y, N, stream=None):
     _check(load_library().eqlinear_forward(plan, _ptr(x), _ptr(y), N, _stream(stream)),
            "eqlinear_forward")
+
+
+def eqlinear_forward_act(plan, x, y, N, act, stream=None):
+    _check(load_library().eqlinear_forward_act(plan, _ptr(x), _ptr(y), N, act, _stream(stream)),
+           "eqlinear_forward_act")
 
 
 def eqlinear_backward_input(plan, dy, dx, N, stream=None):
@@ -213,14 +228,18 @@ class Plan:
             self._expect(bias, (self.D,))
         eqlinear_set_weight(self.handle, W, bias, stream)
 
-    def forward(self, x, y=None, stream=None):
+    def forward(self, x, y=None, stream=None, act=None):
+        """y = act(layer(x)); act is None, "gelu" or "gelu_tanh" (fused)."""
         import torch
         N = x.shape[0]
         self._expect(x, (N, self.C, self.T))
         if y is None:
             y = torch.empty((N, self.D, self.T), dtype=x.dtype, device=x.device)
         self._expect(y, (N, self.D, self.T))
-        eqlinear_forward(self.handle, x, y, N, stream)
+        if act is None:
+            eqlinear_forward(self.handle, x, y, N, stream)
+        else:
+            eqlinear_forward_act(self.handle, x, y, N, ACTIVATIONS[act], stream)
         return y
 
     def backward_input(self, dy, dx=None, stream=None):

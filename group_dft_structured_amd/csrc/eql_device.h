@@ -50,6 +50,46 @@ __device__ __forceinline__ floatx4 idft4(float Y0, float Y2, float Yr, float Yi)
   return o;
 }
 
+// ---- pointwise activation of the forward epilogue ---------------------------
+// Applied after the bias, in fp32, before the rounding to the output dtype.
+// It acts on each output value alone, so it commutes with the group action
+// and the layer stays equivariant.
+//   1: GELU, v * Phi(v) = (v/2) (1 + erf(v / sqrt 2))
+//   2: GELU with the tanh approximation,
+//      (v/2) (1 + tanh(s)) = v / (1 + exp(-2 s)),  s = sqrt(2/pi) (v + 0.044715 v^3)
+// Both are evaluated with the hardware base-2 exponential and reciprocal
+// (about 1 ulp each); erf uses formula 7.1.26 of Abramowitz and Stegun,
+// Handbook of Mathematical Functions (absolute error <= 1.5e-7):
+//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z), z >= 0, and erf(-z) = -erf(z).
+// The epilogue runs on few waves, so a short instruction sequence matters.
+constexpr int ACT_NONE = 0, ACT_GELU = 1, ACT_GELU_TANH = 2;
+
+__device__ __forceinline__ float erf_as(float z) {
+  const float a = __builtin_fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+  float q = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  q = __builtin_fmaf(q, t, 1.421413741f);
+  q = __builtin_fmaf(q, t, -0.284496736f);
+  q = __builtin_fmaf(q, t, 0.254829592f);
+  q *= t;
+  // exp(-a^2) = 2^(-a^2 log2 e)
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * a * a);
+  const float r = __builtin_fmaf(-q, e, 1.0f);
+  return __builtin_copysignf(r, z);
+}
+
+__device__ __forceinline__ float activate(float v, int act) {
+  if (act == ACT_GELU) return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
+  if (act == ACT_GELU_TANH) {
+    // -2 s log2(e) = v (k1 + k2 v^2), k1 = -2 sqrt(2/pi) log2 e, k2 = 0.044715 k1
+    const float k1 = -2.3022082f, k2 = -0.10294324f;
+    const float e = __builtin_amdgcn_exp2f(v * __builtin_fmaf(k2, v * v, k1));
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+  }
+  return v;
+}
+
 // ---- element type traits ---------------------------------------------------
 // Loads/stores of one group quad (4 elements of the type) and conversions.
 template <typename T>

@@ -80,16 +80,20 @@ hipError_t launch_coop(eqlinear_dtype_t dt, const void* x, const void* spec, con
                        void* y, int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
 // Producer/consumer spectral kernel (binary16): the forward, or with the
 // conjugate-transposed spectra (adjoint = true) the backward-input pass.
+// act: pointwise activation of the forward epilogue (0 none, 1 GELU, 2 GELU
+// with the tanh approximation); 0 for backward_input.
 hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, hipStream_t s);
+                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, int act,
+                     hipStream_t s);
 // Producer/consumer forward kernel, binary32 (reduction width a multiple of 16, <= 192).
 hipError_t launch_ws32(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                       int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
+                       int64_t N, int K, int k_pad, int n_out, int n_pad, int act, hipStream_t s);
 // K-streaming kernel (binary16, weights of the output range in LDS).
 hipError_t launch_kstream(eqlinear_dtype_t dt, const void* a, const void* spec, const float* bias,
                           void* out, int64_t N, int K, int k_pad, int n_out, int n_pad,
                           hipStream_t s);
-hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s);
+hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, int act,
+                          hipStream_t s);
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s);
 hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
@@ -99,7 +103,8 @@ hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const v
 namespace cyc {
 size_t workspace_bytes(const eqlinear_plan* p, int64_t N);
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
-hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s);
+hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, int act,
+                          hipStream_t s);
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s);
 hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,

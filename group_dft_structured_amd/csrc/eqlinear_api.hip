@@ -160,11 +160,18 @@ static eqlinear_status_t check_gemm_args(eqlinear_plan_t p, const void* in, cons
 
 eqlinear_status_t eqlinear_forward(eqlinear_plan_t p, const void* x, void* y, int64_t N,
                                    void* stream) {
+  return eqlinear_forward_act(p, x, y, N, EQL_ACT_NONE, stream);
+}
+
+eqlinear_status_t eqlinear_forward_act(eqlinear_plan_t p, const void* x, void* y, int64_t N,
+                                       eqlinear_act_t act, void* stream) {
+  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU && act != EQL_ACT_GELU_TANH)
+    return EQL_ERR_INVALID_ARG;
   eqlinear_status_t st = check_gemm_args(p, x, y, N);
   if (st != EQL_OK || N == 0) return st;
   st = check_device(p);
   if (st != EQL_OK) return st;
-  hipError_t e = eql::launch_forward(p, x, y, N, (hipStream_t)stream);
+  hipError_t e = eql::launch_forward(p, x, y, N, (int)act, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("forward launch", e);
     return EQL_ERR_HIP;

@@ -219,13 +219,13 @@ __global__ __launch_bounds__(256) void k_cyc_spectra(
 // Tile BM rows x BN output channels, 4 waves as 2 x 2, each wave (BM/2) x
 // (BN/2) in 16 x 16 blocks.  LDS per chunk: T planes of the a-tile [BM][64 B]
 // and of the weight tile [BN][64 B].
-template <int T, typename DT, int BM, int BN>
+template <int T, typename DT, int BM, int BN, bool ACT>
 __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
                                                   const DT* __restrict__ spec,
                                                   const float* __restrict__ bias,
                                                   DT* __restrict__ out, int N, int K, int k_pad,
                                                   int n_out, int n_pad, int row_tiles,
-                                                  int col_tiles, int per_xcd) {
+                                                  int col_tiles, int per_xcd, int act) {
   typedef Tr<DT> F;
   typedef typename F::frag frag;
   constexpr int KC = F::KC;
@@ -361,7 +361,11 @@ __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
         dft_inv<T, float>(Q, y);
         DT o[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) o[t] = (DT)(y[t] + b);
+        for (int t = 0; t < T; ++t) {
+          float v = y[t] + b;
+          if constexpr (ACT) v = activate(v, act);
+          o[t] = (DT)v;
+        }
         const uint32_t off =
             d < n_out ? (uint32_t)(((int64_t)rr * n_out + d) * T * (int64_t)sizeof(DT)) : OOB;
         store_unit<T, DT>(ro, off, o);
@@ -611,17 +615,18 @@ BwDims bw_dims(const eqlinear_plan* p, int64_t N) {
   return b;
 }
 
-template <int T, typename DT, int BM, int BN>
+template <int T, typename DT, int BM, int BN, bool ACT = false>
 hipError_t launch_gemm_tile(const void* a, const void* spec, const float* bias, void* out,
-                            int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
+                            int64_t N, int K, int k_pad, int n_out, int n_pad, int act,
+                            hipStream_t s) {
   const int64_t row_tiles = (N + BM - 1) / BM;
   const int col_tiles = (n_out + BN - 1) / BN;
   const int64_t tiles = row_tiles * col_tiles;
   if (tiles > (int64_t)1 << 31) return hipErrorInvalidValue;
   const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL((k_cyc_gemm<T, DT, BM, BN>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_cyc_gemm<T, DT, BM, BN, ACT>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, s,
                      (const DT*)a, (const DT*)spec, bias, (DT*)out, (int)N, K, k_pad, n_out, n_pad,
-                     (int)row_tiles, col_tiles, (int)per_xcd);
+                     (int)row_tiles, col_tiles, (int)per_xcd, act);
   return hipGetLastError();
 }
 
@@ -634,17 +639,25 @@ int env_int(const char* name, int dflt) {
 // 3 = 32x32 (EQL_CYC_TILE overrides the default).
 template <int T, typename DT>
 hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, void* out, int64_t N,
-                         int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
-  int cfg = env_int("EQL_CYC_TILE", T <= 8 && sizeof(DT) == 2 ? 2 : 3);
+                         int K, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
+  const bool wide = T <= 8 && sizeof(DT) == 2;
+  if (act != ACT_NONE) {  // fused activation: the default tile only
+    if (wide)
+      return launch_gemm_tile<T, DT, 32, 64, true>(a, spec, bias, out, N, K, k_pad, n_out, n_pad,
+                                                   act, s);
+    return launch_gemm_tile<T, DT, 32, 32, true>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act,
+                                                 s);
+  }
+  int cfg = env_int("EQL_CYC_TILE", wide ? 2 : 3);
   if (T > 8 && cfg == 0) cfg = 3;
   switch (cfg) {
     case 0:
       if constexpr (T <= 8)
-        return launch_gemm_tile<T, DT, 64, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
+        return launch_gemm_tile<T, DT, 64, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
       return hipErrorInvalidValue;
-    case 1: return launch_gemm_tile<T, DT, 64, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
-    case 2: return launch_gemm_tile<T, DT, 32, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
-    case 3: return launch_gemm_tile<T, DT, 32, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, s);
+    case 1: return launch_gemm_tile<T, DT, 64, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
+    case 2: return launch_gemm_tile<T, DT, 32, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
+    case 3: return launch_gemm_tile<T, DT, 32, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -726,11 +739,11 @@ hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bia
 #undef EQL_CALL
 }
 
-hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N,
+hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, int act,
                           hipStream_t s) {
 #define EQL_CALL(T_, DT_)                                                                     \
   launch_gemm_t<T_, DT_>(x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, \
-                         (int)p->D, (int)p->fwd.n_pad, s)
+                         (int)p->D, (int)p->fwd.n_pad, act, s)
   EQL_CYC_DISPATCH(p->T, p->dtype, EQL_CALL)
 #undef EQL_CALL
 }
@@ -739,7 +752,7 @@ hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* d
                                  hipStream_t s) {
 #define EQL_CALL(T_, DT_)                                                                       \
   launch_gemm_t<T_, DT_>(dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad, \
-                         (int)p->C, (int)p->adj.n_pad, s)
+                         (int)p->C, (int)p->adj.n_pad, ACT_NONE, s)
   EQL_CYC_DISPATCH(p->T, p->dtype, EQL_CALL)
 #undef EQL_CALL
 }

@@ -76,10 +76,11 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // hold one 1 KB fragment at (p*KS + s)*512 halves; lane (i16, g) of the B
 // operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
 // channels 32s + 8g .. 32s + 8g + 7.
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER, bool STG>
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER, bool STG,
+          bool ACT = false>
 __device__ __forceinline__ void ws_body(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
-    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
+    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
   constexpr int BN = NC * NB * 16;
   constexpr int KP = KS * 32;
   constexpr int FRAG = 512;                   // halves per fragment
@@ -316,7 +317,11 @@ __device__ __forceinline__ void ws_body(
         uint32_t o[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const f32x4 v = epi4(c0[nb][r], c2[nb][r], cr[nb][r], ci[nb][r], bc[nb][r]);
+          f32x4 v = epi4(c0[nb][r], c2[nb][r], cr[nb][r], ci[nb][r], bc[nb][r]);
+          if constexpr (ACT) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = activate(v[t], act);
+          }
           o[2 * r] = pack2(v[0], v[1]);
           o[2 * r + 1] = pack2(v[2], v[3]);
         }
@@ -365,18 +370,20 @@ __device__ __forceinline__ void ws_body(
 // Two entry points share the body so that the passes are told apart in
 // kernel traces: the forward (weight spectra) and the backward-input pass
 // (conjugate-transposed spectra, zero bias).
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STG>
+template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STG, bool ACT = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
-    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
-  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG>(x, spec, bias, y, N, K, n_out, n_pad, n_ct, Qx);
+    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
+  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG, ACT>(x, spec, bias, y, N, K, n_out, n_pad, n_ct,
+                                                          Qx, act);
 }
 
 template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STG>
 __global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
     const _Float16* __restrict__ dy, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
-  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx);
+  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx,
+                                                     ACT_NONE);
 }
 
 // ---------------------------------------------------------------------------
@@ -387,7 +394,8 @@ static int env_int(const char* name, int dflt) {
 
 template <int NC, int NP, int NB, int KS>
 static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias, void* y, int64_t N,
-                              int K, int n_out, int n_pad, int wpc, bool adjoint, hipStream_t s) {
+                              int K, int n_out, int n_pad, int wpc, bool adjoint, int act,
+                              hipStream_t s) {
   constexpr int BN = NC * NB * 16;
   const int n_ct = (n_out + BN - 1) / BN;
   if ((int64_t)n_ct * BN > n_pad) return hipErrorNotSupported;  // weight reads stay in the planes
@@ -418,10 +426,23 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
     else                                                                                            \
       hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, PK_, G8_, ST_>), grid, block, 0, s,        \
                          (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
-                         n_pad, n_ct, qx);                                                          \
+                         n_pad, n_ct, qx, act);                                                     \
   } while (0)
   // output store mode: 0 default write-back, 1 streaming, 2 staged through
   // LDS into whole rows and written through the L2 (system scope)
+  if (act != ACT_NONE && !adjoint) {
+    // fused activation: the default store mode and butterfly only
+#define EQL_WS_ACT(YP_, G8_, ST_)                                                                   \
+  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, false, G8_, ST_, true>), grid, block, 0, s, \
+                     (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
+                     n_pad, n_ct, qx, act)
+    if (small && g8) EQL_WS_ACT(POLICY_STREAM, true, false);
+    else if (small) EQL_WS_ACT(POLICY_STREAM, false, false);
+    else if (g8) EQL_WS_ACT(POLICY_THROUGH, true, true);
+    else EQL_WS_ACT(POLICY_THROUGH, false, true);
+#undef EQL_WS_ACT
+    return hipGetLastError();
+  }
   const int mode = env_int("EQL_WS_OUT", small ? 1 : 2);
   const int v = mode * 4 + (packed ? 2 : 0) + (g8 ? 1 : 0);
   switch (v) {
@@ -444,7 +465,8 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
 
 // hipErrorNotSupported when outside this kernel's limits.
 hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, hipStream_t s) {
+                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, int act,
+                     hipStream_t s) {
   if (env_int("EQL_NO_WS", 0) || dt != EQL_F16) return hipErrorNotSupported;
   // exact 32-channel steps (x rows are read without a channel mask) and whole
   // 4-channel output groups (32-byte stores)
@@ -461,13 +483,17 @@ hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const
   // long reductions: 3 or 4 consumer waves, whichever pads the output
   // channels less (ties go to 4)
   const int pad3 = (n_out + 47) / 48 * 48 - n_out, pad4 = (n_out + 63) / 64 * 64 - n_out;
-  const int nc = env_int("EQL_WS_NC", wide ? 4 : deep ? (pad3 < pad4 ? 3 : 4) : 8);
+  // with a fused activation the epilogue carries most of the consumers' work:
+  // short reductions then take 8 consumer waves of 16 channels (measured at
+  // C = 96, D = 384 with GELU: 26.6 us against 37.6 us with 4 waves of 32)
+  const bool act_wide = wide && act != 0 && !adjoint;
+  const int nc = env_int("EQL_WS_NC", act_wide ? 8 : wide ? 4 : deep ? (pad3 < pad4 ? 3 : 4) : 8);
   const int np = env_int("EQL_WS_NP", 4);
-  const int nb = env_int("EQL_WS_NB", wide ? 2 : 1);
+  const int nb = env_int("EQL_WS_NB", wide && !act_wide ? 2 : 1);
   const int wpc = env_int("EQL_WS_WPC", 1);
 #define EQL_WS_CASE(NC_, NP_, NB_, KS_) \
   if (nc == NC_ && np == NP_ && nb == NB_ && ks == KS_) \
-    return launch_ws_t<NC_, NP_, NB_, KS_>(x, spec, bias, y, N, K, n_out, n_pad, wpc, adjoint, s);
+    return launch_ws_t<NC_, NP_, NB_, KS_>(x, spec, bias, y, N, K, n_out, n_pad, wpc, adjoint, act, s);
   EQL_WS_CASE(4, 4, 2, 1)
   EQL_WS_CASE(4, 4, 2, 2)
   EQL_WS_CASE(4, 4, 2, 3)

@@ -57,10 +57,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc32(const void* base, uint3
 // LDS per buffer: plane p, channel block j (16 channels): 1 KB at
 // (p*KB + j)*256 floats; lane (i16, g) reads the 16 bytes at (g*16 + i16)*4
 // floats = row i16, channels 16j + 4g .. 16j + 4g + 3.
-template <int NC, int NP, int KB, int YP>
+template <int NC, int NP, int KB, int YP, bool ACT = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     const float* __restrict__ x, const float* __restrict__ spec, const float* __restrict__ bias,
-    float* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
+    float* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
   constexpr int BN = NC * 16;
   constexpr int KP = KB * 16;                 // reduction channels
   constexpr int FRAG = 256;                   // floats per fragment block
@@ -231,7 +231,11 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
       const uint32_t off = col < n_out ? (uint32_t)((i16 * n_out + col) * 16) : 0x7FFFFFF0u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const f32x4 v = epi4_32(c0[r], c2[r], cr[r], ci[r], bc[r]);
+        f32x4 v = epi4_32(c0[r], c2[r], cr[r], ci[r], bc[r]);
+        if constexpr (ACT) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = activate(v[t], act);
+        }
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry, off + 16 * r, 0, YP);
       }
     };
@@ -253,7 +257,7 @@ static int env_int(const char* name, int dflt) {
 
 template <int NC, int NP, int KB>
 static hipError_t launch_ws32_t(const void* x, const void* spec, const float* bias, void* y, int64_t N,
-                                int K, int n_out, int n_pad, hipStream_t s) {
+                                int K, int n_out, int n_pad, int act, hipStream_t s) {
   constexpr int BN = NC * 16;
   const int n_ct = (n_out + BN - 1) / BN;
   const int64_t n_rt = (N + 15) / 16;
@@ -265,18 +269,26 @@ static hipError_t launch_ws32_t(const void* x, const void* spec, const float* bi
   const unsigned blocks = (unsigned)(8 * n_ct * qx);
   const int64_t y_bytes = N * (int64_t)n_out * 16;
   const bool stream = env_int("EQL_WS32_STREAM", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
-  if (stream)
+  if (act != ACT_NONE && stream)  // fused activation
+    hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 2, true>), dim3(blocks), dim3((NC + NP) * 64), 0, s,
+                       (const float*)x, (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad,
+                       n_ct, qx, act);
+  else if (act != ACT_NONE)
+    hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 0, true>), dim3(blocks), dim3((NC + NP) * 64), 0, s,
+                       (const float*)x, (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad,
+                       n_ct, qx, act);
+  else if (stream)
     hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 2>), dim3(blocks), dim3((NC + NP) * 64), 0, s, (const float*)x,
-                       (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx);
+                       (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx, act);
   else
     hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 0>), dim3(blocks), dim3((NC + NP) * 64), 0, s, (const float*)x,
-                       (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx);
+                       (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx, act);
   return hipGetLastError();
 }
 
 // hipErrorNotSupported when outside this kernel's limits.
 hipError_t launch_ws32(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                       int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s) {
+                       int64_t N, int K, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
   if (env_int("EQL_NO_WS32", 0) || dt != EQL_F32) return hipErrorNotSupported;
   // whole 16-channel reduction blocks read without a channel mask, whole
   // 4-channel output groups (64-byte stores)
@@ -291,7 +303,7 @@ hipError_t launch_ws32(eqlinear_dtype_t dt, const void* x, const void* spec, con
   const int np = env_int("EQL_WS32_NP", kb > 6 ? 4 : 2);
   if ((int64_t)((n_out + 16 * nc - 1) / (16 * nc)) * 16 * nc > n_pad) return hipErrorNotSupported;
 #define EQL_WS32_CASE(NC_, NP_, KB_) \
-  if (nc == NC_ && np == NP_ && kb == KB_) return launch_ws32_t<NC_, NP_, KB_>(x, spec, bias, y, N, K, n_out, n_pad, s);
+  if (nc == NC_ && np == NP_ && kb == KB_) return launch_ws32_t<NC_, NP_, KB_>(x, spec, bias, y, N, K, n_out, n_pad, act, s);
   EQL_WS32_CASE(6, 2, 6)
   EQL_WS32_CASE(4, 2, 6)
   EQL_WS32_CASE(6, 2, 2)

@@ -267,15 +267,16 @@ static int pick_cfg(int64_t n_out) {
   return n_out <= 64 ? 1 : 0;
 }
 
-hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, hipStream_t s) {
-  if (p->cyclic) return cyc::launch_forward(p, x, y, N, s);
-  hipError_t e = launch_ws(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
-                           (int)p->D, (int)p->fwd.n_pad, false, s);
-  if (e != hipErrorNotSupported) return e;
-  e = launch_ws32(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, (int)p->D,
-                  (int)p->fwd.n_pad, s);
-  if (e != hipErrorNotSupported) return e;
-  e = launch_coop(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
+// In-place pointwise activation, for the forward kernels without a fused one.
+template <typename T>
+__global__ __launch_bounds__(256) void k_activate(T* __restrict__ y, int64_t n, int act) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    y[i] = (T)activate((float)y[i], act);
+}
+
+static hipError_t launch_forward_plain(const eqlinear_plan* p, const void* x, void* y, int64_t N,
+                                       hipStream_t s) {
+  hipError_t e = launch_coop(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
                              (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, s);
   if (e != hipErrorNotSupported) return e;
   e = launch_stream(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
@@ -290,11 +291,34 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
                             N, (int)p->C, (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, s);
 }
 
+hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, int act,
+                          hipStream_t s) {
+  if (p->cyclic) return cyc::launch_forward(p, x, y, N, act, s);
+  // the producer/consumer kernels apply the activation in their epilogue
+  hipError_t e = launch_ws(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
+                           (int)p->D, (int)p->fwd.n_pad, false, act, s);
+  if (e != hipErrorNotSupported) return e;
+  e = launch_ws32(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, (int)p->D,
+                  (int)p->fwd.n_pad, act, s);
+  if (e != hipErrorNotSupported) return e;
+  // the fallbacks store the linear output; a second pass applies the activation
+  e = launch_forward_plain(p, x, y, N, s);
+  if (e != hipSuccess || act == ACT_NONE) return e;
+  const int64_t n = N * p->D * p->T;
+  const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+  if (p->dtype == EQL_F16)
+    hipLaunchKernelGGL(k_activate<_Float16>, dim3((unsigned)blocks), dim3(256), 0, s, (_Float16*)y, n,
+                       act);
+  else
+    hipLaunchKernelGGL(k_activate<float>, dim3((unsigned)blocks), dim3(256), 0, s, (float*)y, n, act);
+  return hipGetLastError();
+}
+
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s) {
   if (p->cyclic) return cyc::launch_backward_input(p, dy, dx, N, s);
   hipError_t e = launch_ws(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad,
-                           (int)p->C, (int)p->adj.n_pad, true, s);
+                           (int)p->C, (int)p->adj.n_pad, true, ACT_NONE, s);
   if (e != hipErrorNotSupported) return e;
   e = launch_kstream(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D,
                                 (int)p->adj.k_pad, (int)p->C, (int)p->adj.n_pad, s);

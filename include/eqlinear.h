@@ -102,6 +102,27 @@ eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t plan, const void* W,
 eqlinear_status_t eqlinear_forward(eqlinear_plan_t plan, const void* x, void* y,
                                    int64_t N, void* stream);
 
+/* Pointwise activation fused into the forward epilogue. */
+typedef enum {
+  EQL_ACT_NONE = 0,      /* y as above */
+  EQL_ACT_GELU = 1,      /* GELU: v * Phi(v) = (v/2) (1 + erf(v / sqrt 2)) */
+  EQL_ACT_GELU_TANH = 2  /* GELU, tanh form: (v/2)(1 + tanh(sqrt(2/pi)(v + 0.044715 v^3))) */
+} eqlinear_act_t;
+
+/* Forward followed by a pointwise activation: y = act(forward(x)), with act
+ * applied to every output value after the bias, in binary32, before the one
+ * rounding to the plan dtype.  The pages' fused dataflow ("Implementazione":
+ * no intermediate written to global memory) carried one step further, for
+ * the EQ-Linear -> GELU -> EQ-Linear chain of the equivariant transformers
+ * the layer serves ("Livello di Rete").  A pointwise map commutes with the
+ * group action, so the result stays equivariant.  The default kernels apply
+ * the activation in their epilogue; shapes served by the fallback kernels
+ * get a second in-place pass over y.  act outside eqlinear_act_t returns
+ * EQL_ERR_INVALID_ARG; otherwise as eqlinear_forward (which is
+ * eqlinear_forward_act with EQL_ACT_NONE). */
+eqlinear_status_t eqlinear_forward_act(eqlinear_plan_t plan, const void* x, void* y,
+                                       int64_t N, eqlinear_act_t act, void* stream);
+
 /* Backward with respect to the input ("Implementazione": forward and backward
  * passes): dx[n,c,s] = sum_{d,t} W[d,c,(t-s) mod T] * dy[n,d,t], i.e. the
  * transpose of the forward map, computed with the conjugate weight spectra.

@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the p4 EQ-Linear layer.
+"""Plain fp64 CPU oracle for the EQ-Linear layer (any cyclic group size T).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this package:
 only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -14,6 +14,9 @@ differences); none of it is "parity unpinned".
 from .eqlinear_oracle import (  # noqa: F401
     unroll_block_circulant,
     forward,
+    gelu,
+    gelu_tanh,
+    forward_act,
     backward_input,
     backward_weight,
     mac_counts,

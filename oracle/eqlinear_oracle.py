@@ -68,6 +68,34 @@ def forward(x, W, bias=None):
     return y
 
 
+def gelu(v):
+    """GELU in fp64: v * Phi(v), Phi the standard normal distribution
+    function, written (v/2)(1 + erf(v / sqrt 2)) with scipy's erf.
+
+    The pages do not define the activation; this is the GELU of the
+    transformer MLP blocks (EQ-Linear -> GELU -> EQ-Linear) in the networks
+    the layer is built into ("Livello di Rete": Flash EQ-ViT)."""
+    from scipy.special import erf
+    v = _f64(v)
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+def gelu_tanh(v):
+    """GELU with its usual tanh approximation, fp64:
+    (v/2)(1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))."""
+    v = _f64(v)
+    return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+
+
+ACTIVATIONS = {None: lambda v: _f64(v), "gelu": gelu, "gelu_tanh": gelu_tanh}
+
+
+def forward_act(x, W, bias=None, act=None):
+    """act(forward(x, W, bias)): the activation applied to every output value
+    after the bias (a pointwise map, so the result stays equivariant)."""
+    return ACTIVATIONS[act](forward(x, W, bias))
+
+
 def backward_input(dy, W):
     """dx = dy_flat . Wd (the transpose of the forward map), in fp64.
 

@@ -282,6 +282,62 @@ def check_backward_weight_brute(impl):
         assert _rel(db, dy.sum(axis=(0, 2))) < 1e-13
 
 
+# ---------------------------------------------------------- activation pins
+
+# Standard normal distribution function at a few points (values of the
+# normal table, to 16 digits): Phi(0.5), Phi(1), Phi(2).
+_PHI = {0.5: 0.6914624612740131, 1.0: 0.8413447460685429, 2.0: 0.9772498680518208}
+
+
+def check_gelu_normal_cdf(impl):
+    """GELU(v) = v Phi(v): the normal table, Phi(-v) = 1 - Phi(v), GELU(0) = 0."""
+    assert float(np.asarray(impl.gelu(np.array([0.0])))[0]) == 0.0
+    for v, phi in _PHI.items():
+        for sv, ph in ((v, phi), (-v, 1.0 - phi)):
+            got = float(np.asarray(impl.gelu(np.array([sv])))[0])
+            assert abs(got - sv * ph) < 1e-15, (sv, got, sv * ph)
+
+
+def check_gelu_odd_part(impl):
+    """GELU(v) - GELU(-v) = v for both forms (Phi(v) + Phi(-v) = 1, and
+    tanh is odd); large |v| gives v or 0."""
+    rng = _rng(31)
+    v = rng.standard_normal(1000) * 3
+    for f in (impl.gelu, impl.gelu_tanh):
+        g = np.asarray(f(v)) - np.asarray(f(-v))
+        assert np.max(np.abs(g - v)) < 1e-14
+        big = np.asarray(f(np.array([12.0, -12.0])))
+        assert abs(big[0] - 12.0) < 1e-12 and abs(big[1]) < 1e-12
+
+
+def check_gelu_tanh_close(impl):
+    """The tanh form stays within 1e-3 of GELU everywhere (it is an
+    approximation of the same function, not another one)."""
+    v = np.linspace(-8, 8, 16001)
+    d = np.abs(np.asarray(impl.gelu(v)) - np.asarray(impl.gelu_tanh(v)))
+    assert d.max() < 1e-3, d.max()
+
+
+def check_forward_act(impl):
+    """forward_act = brute-force layer, then the activation per value with
+    math.erf (independent of the oracle's erf); equivariant under rolls."""
+    import math
+    rng = _rng(32)
+    for T in (3, 4, 8):
+        x = rng.standard_normal((5, 3, T))
+        W = rng.standard_normal((4, 3, T))
+        b = rng.standard_normal(4)
+        lin = _brute_forward(x, W, b)
+        ref = np.vectorize(lambda v: 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))))(lin)
+        got = np.asarray(impl.forward_act(x, W, b, "gelu"))
+        assert _rel(got, ref) < 1e-14, T
+        assert _rel(impl.forward_act(x, W, b, None), lin) < 1e-13, T
+        for r in range(1, T):
+            yr = np.asarray(impl.forward_act(np.roll(x, r, axis=2), W, b, "gelu_tanh"))
+            assert _rel(yr, np.roll(np.asarray(impl.forward_act(x, W, b, "gelu_tanh")), r,
+                                    axis=2)) < 1e-13, (T, r)
+
+
 # ------------------------------------------------------------------ cost pins
 
 def check_mac_counts(impl):
@@ -312,6 +368,7 @@ ALL_CHECKS = [
     check_group_constant, check_trivial_group, check_equivariance, check_fft_identity,
     check_backward_input_adjoint, check_backward_input_fd, check_backward_input_as_forward,
     check_backward_weight_fd, check_backward_weight_brute, check_mac_counts, check_param_counts,
+    check_gelu_normal_cdf, check_gelu_odd_part, check_gelu_tanh_close, check_forward_act,
 ]
 
 

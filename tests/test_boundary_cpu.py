@@ -94,6 +94,18 @@ def test_calls_before_set_weight_and_bad_arguments():
         lib.eqlinear_plan_destroy(h)
 
 
+def test_forward_act_rejects_unknown_activation():
+    lib = _lib()
+    st, h = _raw_plan(lib)
+    try:
+        # checked before anything else, including the missing weight
+        assert lib.eqlinear_forward_act(h, None, None, 0, 3, None) == 1
+        assert lib.eqlinear_forward_act(h, None, None, 0, -1, None) == 1
+        assert lib.eqlinear_forward_act(h, None, None, 0, 1, None) == 3   # EQL_ERR_NO_WEIGHT
+    finally:
+        lib.eqlinear_plan_destroy(h)
+
+
 def test_mac_counts_and_ratio():
     _lib()
     p = eq.eqlinear_plan_create(96, 384, 4, eq.EQL_F16)

@@ -162,3 +162,16 @@ def test_cyclic_backward_weight_configs(bw_tile, bw_wgs, T, dtype, monkeypatch):
     monkeypatch.setenv("EQL_CYC_BW_TILE", str(bw_tile))
     monkeypatch.setenv("EQL_CYC_BW_WGS", str(bw_wgs))
     _backward_case(70, 45, 1500, T, dtype, seed=13)
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+@pytest.mark.parametrize("T,dtype", [(3, "f32"), (8, "f16"), (8, "f32"), (16, "f16")])
+def test_cyclic_forward_act(T, dtype, act):
+    inp = make_inputs(33, 70, 517, T, dtype=dtype, seed=17)
+    plan = Plan(33, 70, dtype, T=T)
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    y = plan.forward(to_dev(inp["x"]), act=act)
+    _sync()
+    err = rel_err(to_np64(y), oracle.forward_act(inp["x"], inp["W"], inp["bias"], act))
+    assert err <= TOL[dtype], err
+    plan.close()

@@ -339,3 +339,55 @@ def test_set_weight_twice_replaces_spectra():
     _sync()
     ref = oracle.forward(inp1["x"], inp2["W"], inp2["bias"])
     assert rel_err(to_np64(y), ref) <= TOL["f32"]
+
+
+# ---- fused activation (forward_act) ------------------------------------------
+
+def _forward_act_case(C, D, N, dtype, act, T=4, seed=0):
+    inp = make_inputs(C, D, N, T, dtype=dtype, seed=seed, bias=True)
+    plan = Plan(C, D, dtype, T=T)
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    y = plan.forward(to_dev(inp["x"]), act=act)
+    _sync()
+    ref = oracle.forward_act(inp["x"], inp["W"], inp["bias"], act)
+    err = rel_err(to_np64(y), ref)
+    print(f"forward_act {act} T={T} C={C} D={D} N={N} {dtype}: rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype], err
+    plan.close()
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+@pytest.mark.parametrize("C,D,N,dtype,env", [
+    (96, 384, 3001, "f16", {}),                         # producer/consumer binary16, streaming stores
+    (96, 384, 3001, "f16", {"EQL_WS_OUT": "2"}),        # default mode ignored with act: still fused
+    (96, 384, 3001, "f16", {"EQL_WS_NC": "4", "EQL_WS_NB": "2"}),  # 4 consumers of 32 channels
+    (256, 96, 700, "f16", {}),                          # 8-channel producer units (long reduction)
+    (96, 384, 3001, "f32", {}),                         # producer/consumer binary32
+    (33, 130, 65, "f16", {}),                           # fallback kernel + activation pass
+    (33, 130, 65, "f32", {}),
+    (96, 96, 1000, "f16", {"EQL_NO_WS": "1"}),          # weight-stationary fallback + pass
+    (96, 96, 1000, "f32", {"EQL_NO_WS32": "1"}),        # streaming fallback + pass
+])
+def test_forward_act(C, D, N, dtype, env, act, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    _forward_act_case(C, D, N, dtype, act, seed=21)
+
+
+def test_forward_act_swin_stage_sampled():
+    """Full-size Swin-like stage with GELU: outputs beyond the memory-side
+    cache take the staged write-through stores; sampled rows vs the oracle."""
+    w = WORKLOADS["swin_stage"]
+    inp = make_inputs(w.C, w.D, w.N, dtype="f16", seed=0)
+    plan = Plan(w.C, w.D, "f16")
+    plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+    y = plan.forward(to_dev(inp["x"]), act="gelu")
+    rng = np.random.default_rng(321)
+    rows = np.unique(np.concatenate([rng.choice(w.N, 1024, replace=False),
+                                     np.arange(32), np.arange(w.N - 32, w.N)]))
+    got = to_np64(y[torch_mod().from_numpy(rows).to("cuda")])
+    ref = oracle.forward_act(inp["x"][rows], inp["W"], inp["bias"], "gelu")
+    err = rel_err(got, ref)
+    print(f"swin_stage gelu sampled: rel err {err:.3e}", flush=True)
+    assert err <= TOL["f16"], err
+    plan.close()

@@ -26,7 +26,7 @@ def _unroll_with(tap):
 def _impl(**over):
     ns = {k: getattr(oracle, k) for k in
           ("forward", "backward_input", "backward_weight", "mac_counts", "param_counts",
-           "unroll_block_circulant")}
+           "unroll_block_circulant", "gelu", "gelu_tanh", "forward_act")}
     ns.update(over)
     return types.SimpleNamespace(**ns)
 
@@ -87,6 +87,24 @@ def _mac_counts_gauss(N, C, D, T):
     return (real + 3 * cplx) * N * C * D, T * T * N * C * D
 
 
+def _gelu_no_sqrt2(v):
+    from scipy.special import erf
+    v = np.asarray(v, np.float64)
+    return 0.5 * v * (1.0 + erf(v))
+
+
+def _gelu_tanh_const(k):
+    def f(v):
+        v = np.asarray(v, np.float64)
+        return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + k * v ** 3)))
+    return f
+
+
+def _act_before_bias(x, W, bias=None, act=None):
+    y = O.ACTIVATIONS[act](O.forward(x, W, None))
+    return y + (np.asarray(bias, np.float64)[None, :, None] if bias is not None else 0.0)
+
+
 corr = _unroll_with(lambda t, s, T: (s - t) % T)
 off_by_one = _unroll_with(lambda t, s, T: (t - s + 1) % T)
 no_shift = _unroll_with(lambda t, s, T: 0 if t == s else (t - s) % T if (t + s) % 2 else 1)
@@ -113,6 +131,12 @@ MUTANTS = {
     "mac_counts_without_symmetry": _impl(mac_counts=_mac_counts_no_symmetry),
     "mac_counts_gauss_trick": _impl(mac_counts=_mac_counts_gauss),
     "param_counts_dense_equal": _impl(param_counts=lambda C, D, T: (D * C * T, D * C * T)),
+    "gelu_erf_without_sqrt2": _impl(gelu=_gelu_no_sqrt2),
+    "gelu_missing_half": _impl(gelu=lambda v: np.asarray(O.gelu(v)) * 2),
+    "gelu_tanh_cubic_constant": _impl(gelu_tanh=_gelu_tanh_const(0.44715)),
+    "gelu_tanh_without_cubic": _impl(gelu_tanh=_gelu_tanh_const(0.0)),
+    "forward_act_before_bias": _impl(forward_act=_act_before_bias),
+    "forward_act_ignores_act": _impl(forward_act=lambda x, W, bias=None, act=None: O.forward(x, W, bias)),
 }
 
 
