@@ -9,19 +9,22 @@
 // Organisation on CDNA4.  A persistent work-group owns BN = 16*NB*NC output
 // channels and walks 16-row tiles of x.  Its waves have one of two roles:
 //  * NP producer waves stream x: range-checked 16-byte buffer loads three
-//    tiles ahead in a register ring, the length-4 butterfly (X0, X2 exact in
-//    fp32 via v_dot2 with +-1, rounded once to binary16; Xr and Xi from one
+//    tiles ahead in a register ring, the length-4 butterfly (X0, X2 from
+//    pair sums in fp32, rounded once to binary16; Xr and -Xi from one
 //    correctly rounded packed subtraction) and the write of the four planes
-//    to LDS in matrix-core fragment order (double buffered);
+//    to LDS in matrix-core fragment order (double buffered).  They also
+//    write the previous tile's output, staged in LDS by the consumers, to
+//    memory as whole rows;
 //  * NC consumer waves keep the weight-spectrum fragments of their 16*NB
 //    channels in VGPRs, multiply the tile from LDS on the matrix cores
 //    (16x16x32 f16, fp32 accumulate), apply the inverse butterfly and the
-//    bias in fp32 and store 32 contiguous bytes per lane.
+//    bias in fp32 and leave the binary16 result in LDS.
 // The two roles run separate loops that meet at one work-group barrier per
-// tile, so the butterfly of tile i+1 overlaps the products of tile i, and
-// each role's wait counts only see its own memory operations (loads for the
-// producers, stores for the consumers).  Work-groups that read the same x
-// tiles (different channel ranges) sit on the same XCD and share its L2.
+// tile, so the butterfly of tile i+1 and the stores of tile i-1 overlap the
+// products of tile i.  The consumers never touch global memory in the loop,
+// so memory back-pressure never stalls the matrix cores.  Work-groups that
+// read the same x tiles (different channel ranges) sit on the same XCD and
+// share its L2.
 #include "eql_device.h"
 #include "eql_internal.h"
 
@@ -56,14 +59,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Cache policy of the output stores (instruction cache-policy bits): 0 is
-// the default write-back policy, 2 the non-temporal (streaming) hint, 0x11
-// system scope (sc0 | sc1: written through the L2, used with whole-line
-// stores only).  For
-// outputs that fit in the memory-side cache the streaming hint shortens the
-// write-back of dirty L2 lines after the last wave (several microseconds
-// per launch at a few tens of MB); for outputs of a GB it costs bandwidth.
-constexpr int POLICY_DEFAULT = 0, POLICY_STREAM = 2, POLICY_THROUGH = 0x11;
+// Cache policy of the output stores (instruction cache-policy bits): 2 is
+// the non-temporal (streaming) hint, 0x11 system scope (sc0 | sc1: written
+// through the L2, used with whole-line stores only).  Either shortens the
+// write-back of dirty L2 lines after the last wave, several microseconds
+// per launch at a few tens of MB; beyond the memory-side cache the
+// streaming hint sustains the higher bandwidth.
+constexpr int POLICY_STREAM = 2, POLICY_THROUGH = 0x11;
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const f16x2 h = {(_Float16)a, (_Float16)b};
@@ -76,7 +78,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // hold one 1 KB fragment at (p*KS + s)*512 halves; lane (i16, g) of the B
 // operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
 // channels 32s + 8g .. 32s + 8g + 7.
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STAGGER, bool STG,
+template <int NC, int NP, int NB, int KS, int YP, bool G8, bool STAGGER, bool PST,
           bool ACT = false>
 __device__ __forceinline__ void ws_body(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
@@ -96,10 +98,15 @@ __device__ __forceinline__ void ws_body(
   constexpr int UPT = (UNITS + PT - 1) / PT;         // units per producer thread
   constexpr int LPT = UPT * LPU;                     // loads per producer thread
   constexpr int DUMMY = (UNITS % PT != 0) ? (G8 ? 8 : 2) * PT : 0;  // halves
-  // staged epilogue: each consumer wave owns 16 rows x 16*NB channels x 4
-  // group values of output, re-read row-contiguous for whole-line stores
-  constexpr int STW = 16 * 64 * NB;  // halves per consumer wave
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY + (STG ? NC * STW : 0)];
+  // producer-stored output (PST): the consumers leave each output tile in
+  // LDS, row-major over the work-group's BN channels, double buffered; the
+  // producers write it to memory during the next tile.  The 16-byte pad per
+  // row puts the 16-byte writes of 8 consecutive consumer lanes (8 rows) on
+  // distinct LDS banks.
+  constexpr int OPITCH = BN * 4 + 8;  // halves per staged output row
+  constexpr int OBUF = 16 * OPITCH;   // halves per staged output tile
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY + (PST ? 2 * OBUF : 0)];
+  _Float16* const obuf = xs + 2 * BUF + DUMMY;  // PST staging (two tiles)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
@@ -115,9 +122,23 @@ __device__ __forceinline__ void ws_body(
     // =========================== producer waves ===========================
     const int ptid = tid - NC * 64;
     const int64_t row_elems = (int64_t)K * 4;
-    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
-    const f16x2 pm = {(_Float16)1.f, (_Float16)-1.f};
-    // unit u -> (row = u % 16, channel group u / 16): a wave reads 16 rows
+    // unit u -> (row, channel group).  A wave's 64 units cover 16 rows and
+    // 4 consecutive groups, so its loads touch 16 row segments of 64 bytes
+    // either way; the lane order is chosen for the LDS writes.  With 8-channel
+    // units, rows fastest: lane l writes the 16-byte fragment slot l, so a
+    // wave writes 1 KB contiguously.  With 2-channel units, groups fastest:
+    // lane l writes the l-th 4-byte word of a 256-byte run, where rows
+    // fastest would put rows r and r + 8 on the same LDS bank (measured on
+    // gfx950: 2-way conflicts, half of the write cycles).
+    auto unit_pos = [](int u, int& row, int& grp) {
+      if (G8) {
+        row = u % 16;
+        grp = u / 16;
+      } else {
+        row = (u >> 2) & 15;
+        grp = ((u >> 6) << 2) | (u & 3);
+      }
+    };
     auto load_tile = [&](half8 (&raw)[LPT], int i) {
       const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
       const int64_t rows = r0 < N ? (N - r0 < 16 ? N - r0 : 16) : 0;
@@ -125,7 +146,8 @@ __device__ __forceinline__ void ws_body(
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const int u = k * PT + ptid;
-        const int row = u % 16, grp = u / 16;
+        int row, grp;
+        unit_pos(u, row, grp);
         const bool real = UNITS % PT == 0 || u < UNITS;
         const uint32_t off = (uint32_t)(row * row_elems + 4 * CPU * grp) * 2;
 #pragma unroll
@@ -135,40 +157,35 @@ __device__ __forceinline__ void ws_body(
       }
     };
     // butterfly of one 16-byte word (channels c, c + 1, four group values
-    // each) into packed binary16 pairs (X0, X2, Xr, Xi) of the two channels
+    // each) into packed binary16 pairs (X0, X2, Xr, -Xi) of the two channels.
+    // X0 and X2 from the pair sums x0 + x2 and x1 + x3 in fp32, rounded once
+    // to binary16; Xr = x0 - x2 and -Xi = x1 - x3 from one correctly rounded
+    // packed subtraction.  The fourth plane holds -Xi so that no lane ever
+    // negates a fragment; the consumers fold the sign into their sums.
+    // The multiplier 1.0 is made opaque to the optimiser so that each pair
+    // sum stays one mixed-precision fma (binary16 operands, fp32 result)
+    // instead of two conversions and an add.
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
     auto bfly = [&](const half8& w, uint32_t& o0, uint32_t& o2, uint32_t& orr, uint32_t& oi) {
+      const float sa = __builtin_fmaf((float)w[0], one, (float)w[2]);
+      const float ta = __builtin_fmaf((float)w[1], one, (float)w[3]);
+      const float sb = __builtin_fmaf((float)w[4], one, (float)w[6]);
+      const float tb = __builtin_fmaf((float)w[5], one, (float)w[7]);
+      o0 = pack2(sa + ta, sb + tb);
+      o2 = pack2(sa - ta, sb - tb);
       const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};  // channel c
       const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};  // channel c + 1
-      if (PACKED) {
-        // pair sums (x0 + x2, x1 + x3) rounded to binary16, then X0 and X2
-        // as their sum and difference: two roundings, about half the
-        // instructions of the exact form
-        const f16x2 sa = a01 + a23, sb = b01 + b23;
-        const f16x2 p = {sa[0], sb[0]}, q = {sa[1], sb[1]};
-        o0 = __builtin_bit_cast(uint32_t, p + q);
-        o2 = __builtin_bit_cast(uint32_t, p - q);
-        const f16x2 a0n1 = {w[0], -w[1]}, na2a3 = {-w[2], w[3]};
-        const f16x2 b0n1 = {w[4], -w[5]}, nb2b3 = {-w[6], w[7]};
-        const f16x2 ra = a0n1 + na2a3, rb = b0n1 + nb2b3;  // (Xr, Xi) of each channel
-        orr = __builtin_bit_cast(uint32_t, f16x2{ra[0], rb[0]});
-        oi = __builtin_bit_cast(uint32_t, f16x2{ra[1], rb[1]});
-      } else {
-        const float x0a = __builtin_amdgcn_fdot2(a01, ones, __builtin_amdgcn_fdot2(a23, ones, 0.f, false), false);
-        const float x0b = __builtin_amdgcn_fdot2(b01, ones, __builtin_amdgcn_fdot2(b23, ones, 0.f, false), false);
-        const float x2a = __builtin_amdgcn_fdot2(a01, pm, __builtin_amdgcn_fdot2(a23, pm, 0.f, false), false);
-        const float x2b = __builtin_amdgcn_fdot2(b01, pm, __builtin_amdgcn_fdot2(b23, pm, 0.f, false), false);
-        o0 = pack2(x0a, x0b);
-        o2 = pack2(x2a, x2b);
-        const f16x2 da = a01 - a23, db = b01 - b23;  // (Xr, -Xi) of each channel
-        orr = __builtin_bit_cast(uint32_t, f16x2{da[0], db[0]});
-        oi = __builtin_bit_cast(uint32_t, f16x2{-da[1], -db[1]});
-      }
+      const f16x2 da = a01 - a23, db = b01 - b23;           // (Xr, -Xi) of each channel
+      orr = __builtin_bit_cast(uint32_t, f16x2{da[0], db[0]});
+      oi = __builtin_bit_cast(uint32_t, f16x2{da[1], db[1]});
     };
     auto store_tile = [&](const half8 (&raw)[LPT], _Float16* buf) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const int u = k * PT + ptid;
-        const int row = u % 16, grp = u / 16;
+        int row, grp;
+        unit_pos(u, row, grp);
         const int c = CPU * grp;  // first channel of the unit
         const int s = c >> 5, gg = (c & 31) >> 3, jj = c & 7;
         const bool real = UNITS % PT == 0 || u < UNITS;
@@ -200,6 +217,33 @@ __device__ __forceinline__ void ws_body(
         }
       }
     };
+    // PST: write the staged output of this worker's tile t (16 rows x BN
+    // channels, one 16-byte chunk = 2 channels x 4 group values per lane,
+    // whole rows per wave instruction) from staging buffer t % 2
+    auto store_out = [&](int t) {
+      const int64_t r0 = (int64_t)(q + (int64_t)t * Q) * 16;
+      const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+      const __amdgpu_buffer_rsrc_t ry = rsrc(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 8));
+      const _Float16* const sb = obuf + (t & 1) * OBUF;
+      constexpr int LPR = BN / 2;                // chunks per row
+      constexpr int CH = 16 * LPR;               // chunks per tile
+      constexpr int SPT = (CH + PT - 1) / PT;    // chunks per producer thread
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) {
+        const int u0 = k * PT + ptid;
+        const bool real = CH % PT == 0 || u0 < CH;
+        const int u = real ? u0 : 0;
+        const int row = u / LPR, ch = u % LPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * OPITCH + 8 * ch);
+        const int col = j * BN + 2 * ch;
+        const uint32_t off = (real && col < n_out) ? (uint32_t)((row * n_out + col) * 8) : 0x7FFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, YP);
+      }
+    };
+    // phase p (between barriers p and p + 1) first writes out tile p - 1
+    auto out_step = [&](int p) {
+      if (PST && p >= 1) store_out(p - 1);
+    };
     // Ring: tile i sits in slot i % 3 from its load until its butterfly;
     // between barriers i and i+1 the producers transform tile i+1 and load
     // tile i+4 into the slot it frees.  Only loads are in flight here, so
@@ -223,18 +267,21 @@ __device__ __forceinline__ void ws_body(
     int cur = 1;      // buffer of the next tile
     int i = 0;        // barriers i .. : tile i+1 goes to buffer cur
     for (; i + 3 <= n_my - 1; i += 3) {
+      out_step(i);
       store_tile(rb, xs + cur * BUF);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(rb, i + 4);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       cur ^= 1;
+      out_step(i + 1);
       store_tile(rc, xs + cur * BUF);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(rc, i + 5);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       cur ^= 1;
+      out_step(i + 2);
       store_tile(ra, xs + cur * BUF);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(ra, i + 6);
@@ -244,13 +291,21 @@ __device__ __forceinline__ void ws_body(
     }
     const int rest = n_my - 1 - i;  // 0, 1 or 2 transforms left
     if (rest > 0) {
+      out_step(i);
       store_tile(rb, xs + cur * BUF);
       __syncthreads();
       cur ^= 1;
       if (rest > 1) {
+        out_step(i + 1);
         store_tile(rc, xs + cur * BUF);
         __syncthreads();
       }
+    }
+    if (PST) {
+      // phase n_my - 1, then barrier n_my (after the consumers' last tile)
+      out_step(n_my - 1);
+      __syncthreads();
+      store_out(n_my - 1);
     }
   } else {
     // =========================== consumer waves ===========================
@@ -288,36 +343,36 @@ __device__ __forceinline__ void ws_body(
       const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
       const int64_t rows = N - r0 < 16 ? N - r0 : 16;
       const __amdgpu_buffer_rsrc_t ry = rsrc(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 8));
-      f32x4 c0[NB], c2[NB], cr[NB], ci[NB];
+      // Yr = Wr Xr - Wi Xi and Yi = Wi Xr + Wr Xi with the plane xn = -Xi:
+      // cr + cq and ci - cn, six independent accumulators
+      f32x4 c0[NB], c2[NB], cr[NB], cq[NB], ci[NB], cn[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) c0[nb] = c2[nb] = cr[nb] = ci[nb] = f32x4{};
+      for (int nb = 0; nb < NB; ++nb) c0[nb] = c2[nb] = cr[nb] = cq[nb] = ci[nb] = cn[nb] = f32x4{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const _Float16* f = buf + s * FRAG + lane * 8;
         const half8 x0 = *reinterpret_cast<const half8*>(f + 0 * PS);
         const half8 x2 = *reinterpret_cast<const half8*>(f + 1 * PS);
         const half8 xr = *reinterpret_cast<const half8*>(f + 2 * PS);
-        const half8 xi = *reinterpret_cast<const half8*>(f + 3 * PS);
-        const half8 xq = -xi;
+        const half8 xn = *reinterpret_cast<const half8*>(f + 3 * PS);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           c0[nb] = mma16(w0[nb][s], x0, c0[nb]);
           cr[nb] = mma16(wr[nb][s], xr, cr[nb]);
           c2[nb] = mma16(w2[nb][s], x2, c2[nb]);
           ci[nb] = mma16(wi[nb][s], xr, ci[nb]);
-          cr[nb] = mma16(wi[nb][s], xq, cr[nb]);
-          ci[nb] = mma16(wr[nb][s], xi, ci[nb]);
+          cq[nb] = mma16(wi[nb][s], xn, cq[nb]);
+          cn[nb] = mma16(wr[nb][s], xn, cn[nb]);
         }
       }
       // lane holds channels d0 + 16nb + 4g + r of row r0 + i16; rows past N
       // fall outside the store range and are dropped
-      _Float16* const stg = xs + 2 * BUF + DUMMY + wave * STW;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         uint32_t o[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          f32x4 v = epi4(c0[nb][r], c2[nb][r], cr[nb][r], ci[nb][r], bc[nb][r]);
+          f32x4 v = epi4(c0[nb][r], c2[nb][r], cr[nb][r] + cq[nb][r], ci[nb][r] - cn[nb][r], bc[nb][r]);
           if constexpr (ACT) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[t] = activate(v[t], act);
@@ -326,9 +381,9 @@ __device__ __forceinline__ void ws_body(
           o[2 * r + 1] = pack2(v[2], v[3]);
         }
         const u32x4 lo = {o[0], o[1], o[2], o[3]}, hi = {o[4], o[5], o[6], o[7]};
-        if (STG) {
-          // row i16 of the wave's slice, channels 16nb + 4g .. + 3: 32 bytes
-          _Float16* const sp = stg + (i16 * 16 * NB + nb * 16 + 4 * g) * 4;
+        if (PST) {
+          // row i16, work-group channels wave*16NB + 16nb + 4g .. + 3
+          _Float16* const sp = obuf + (i & 1) * OBUF + i16 * OPITCH + (wave * NB * 16 + nb * 16 + 4 * g) * 4;
           *reinterpret_cast<u32x4*>(sp) = lo;
           *reinterpret_cast<u32x4*>(sp + 8) = hi;
         } else {
@@ -340,50 +395,36 @@ __device__ __forceinline__ void ws_body(
           __builtin_amdgcn_raw_buffer_store_b128(hi, ry, off + 16, 0, YP);
         }
       }
-      if (STG) {
-        // re-read row-contiguous: a row of the slice is 16*NB channels x 8
-        // bytes = 8*NB lanes of 16 bytes; each store instruction writes
-        // 64/(8*NB) whole row segments
-        constexpr int LPR = 8 * NB;   // lanes per row
-        constexpr int RPP = 64 / LPR; // rows per pass
-        const int lr = lane / LPR, ch = lane % LPR;
-        const int col = d0 + 2 * ch;  // first of the two channels of the chunk
-#pragma unroll
-        for (int pass = 0; pass < 16 / RPP; ++pass) {
-          const int row = pass * RPP + lr;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (row * 16 * NB + 2 * ch) * 4);
-          const uint32_t off = col < n_out ? (uint32_t)((row * n_out + col) * 8) : 0x7FFFFFF0u;
-          __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, YP);
-        }
-      }
     };
     __syncthreads();  // barrier 0
     int cur = 0;
     for (int i = 0; i < n_my; ++i) {
       compute_tile(i, xs + cur * BUF);
       cur ^= 1;
-      if (i + 1 < n_my) __syncthreads();  // barrier i+1
+      // barrier i+1 (with PST also after the last tile: its staged output
+      // is then complete for the producers)
+      if (PST || i + 1 < n_my) __syncthreads();
     }
   }
 }
 
 // Two entry points share the body so that the passes are told apart in
 // kernel traces: the forward (weight spectra) and the backward-input pass
-// (conjugate-transposed spectra, zero bias).
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STG, bool ACT = false>
+// (conjugate-transposed spectra, zero bias).  PST selects the output path:
+// the producers write whole rows staged through LDS (the default), or the
+// consumers store their fragments directly.
+template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool ACT = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
-  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG, ACT>(x, spec, bias, y, N, K, n_out, n_pad, n_ct,
-                                                          Qx, act);
+  ws_body<NC, NP, NB, KS, YP, G8, true, PST, ACT>(x, spec, bias, y, N, K, n_out, n_pad, n_ct, Qx, act);
 }
 
-template <int NC, int NP, int NB, int KS, int YP, bool PACKED, bool G8, bool STG>
+template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST>
 __global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
     const _Float16* __restrict__ dy, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
-  ws_body<NC, NP, NB, KS, YP, PACKED, G8, true, STG>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx,
-                                                     ACT_NONE);
+  ws_body<NC, NP, NB, KS, YP, G8, true, PST>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx, ACT_NONE);
 }
 
 // ---------------------------------------------------------------------------
@@ -406,58 +447,44 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   if (qx > max_qx) qx = (int)(max_qx < 1 ? 1 : max_qx);
   qx = env_int("EQL_WS_QX", qx);
   const unsigned blocks = (unsigned)(8 * n_ct * qx);
-  // streaming stores while the output fits well inside the 256 MB
-  // memory-side cache; beyond, whole-row stores written through the L2
-  // (measured on MI355X: c2 15.1 us streaming vs 16.1 staged; c3 620 us vs 582)
+  // Output path (measured on MI355X, binary16): the producers store whole
+  // rows, written through the L2 while the output fits well inside the
+  // 256 MB memory-side cache (C=96, D=384, N=12608: 11.2 us against 13.3
+  // with streaming consumer stores) and streamed beyond it (C=192, D=768,
+  // N=200704: 484 us against 507 written through).
   const int64_t y_bytes = N * (int64_t)n_out * 8;
   const bool small = y_bytes <= (128LL << 20);
   // 8-channel producer units for long reductions (fewer instructions per
-  // tile); the packed butterfly (two roundings of X0, X2) only on request:
-  // it saves little and its error grows with the reduction width
-  const bool packed = env_int("EQL_WS_PACKED", 0) != 0;
+  // tile)
   const bool g8 = env_int("EQL_WS_G8", KS > 6 ? 1 : 0) != 0;
   const dim3 grid(blocks), block((NC + NP) * 64);
-#define EQL_WS_LAUNCH(YP_, PK_, G8_, ST_)                                                              \
+#define EQL_WS_LAUNCH(YP_, G8_, PST_)                                                                \
   do {                                                                                              \
     if (adjoint)                                                                                    \
-      hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, NB, KS, YP_, PK_, G8_, ST_>), grid, block, 0, s,  \
+      hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_>), grid, block, 0, s,     \
                          (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
                          n_pad, n_ct, qx);                                                          \
+    else if (act != ACT_NONE)                                                                       \
+      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, true>), grid, block, 0, s,     \
+                         (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
+                         n_pad, n_ct, qx, act);                                                     \
     else                                                                                            \
-      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, PK_, G8_, ST_>), grid, block, 0, s,        \
+      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_>), grid, block, 0, s,           \
                          (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
                          n_pad, n_ct, qx, act);                                                     \
   } while (0)
-  // output store mode: 0 default write-back, 1 streaming, 2 staged through
-  // LDS into whole rows and written through the L2 (system scope)
-  if (act != ACT_NONE && !adjoint) {
-    // fused activation: the default store mode and butterfly only
-#define EQL_WS_ACT(YP_, G8_, ST_)                                                                   \
-  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, false, G8_, ST_, true>), grid, block, 0, s, \
-                     (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
-                     n_pad, n_ct, qx, act)
-    if (small && g8) EQL_WS_ACT(POLICY_STREAM, true, false);
-    else if (small) EQL_WS_ACT(POLICY_STREAM, false, false);
-    else if (g8) EQL_WS_ACT(POLICY_THROUGH, true, true);
-    else EQL_WS_ACT(POLICY_THROUGH, false, true);
-#undef EQL_WS_ACT
-    return hipGetLastError();
-  }
-  const int mode = env_int("EQL_WS_OUT", small ? 1 : 2);
-  const int v = mode * 4 + (packed ? 2 : 0) + (g8 ? 1 : 0);
-  switch (v) {
-    case 0: EQL_WS_LAUNCH(POLICY_DEFAULT, false, false, false); break;
-    case 1: EQL_WS_LAUNCH(POLICY_DEFAULT, false, true, false); break;
-    case 2: EQL_WS_LAUNCH(POLICY_DEFAULT, true, false, false); break;
-    case 3: EQL_WS_LAUNCH(POLICY_DEFAULT, true, true, false); break;
-    case 4: EQL_WS_LAUNCH(POLICY_STREAM, false, false, false); break;
-    case 5: EQL_WS_LAUNCH(POLICY_STREAM, false, true, false); break;
-    case 6: EQL_WS_LAUNCH(POLICY_STREAM, true, false, false); break;
-    case 7: EQL_WS_LAUNCH(POLICY_STREAM, true, true, false); break;
-    case 8: EQL_WS_LAUNCH(POLICY_THROUGH, false, false, true); break;
-    case 9: EQL_WS_LAUNCH(POLICY_THROUGH, false, true, true); break;
-    case 10: EQL_WS_LAUNCH(POLICY_THROUGH, true, false, true); break;
-    default: EQL_WS_LAUNCH(POLICY_THROUGH, true, true, true); break;
+  // output mode: 0 producer stores (written through small outputs,
+  // streamed large ones); 1 consumer stores, streaming
+  const int mode = env_int("EQL_WS_OUT", 0);
+  if (mode == 1) {
+    if (g8) EQL_WS_LAUNCH(POLICY_STREAM, true, false);
+    else EQL_WS_LAUNCH(POLICY_STREAM, false, false);
+  } else if (small) {
+    if (g8) EQL_WS_LAUNCH(POLICY_THROUGH, true, true);
+    else EQL_WS_LAUNCH(POLICY_THROUGH, false, true);
+  } else {
+    if (g8) EQL_WS_LAUNCH(POLICY_STREAM, true, true);
+    else EQL_WS_LAUNCH(POLICY_STREAM, false, true);
   }
 #undef EQL_WS_LAUNCH
   return hipGetLastError();
