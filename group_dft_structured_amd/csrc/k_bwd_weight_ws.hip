@@ -245,13 +245,17 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
   } else {
     // =========================== consumer waves ===========================
     const int wd = wave / NWC, wc = wave % NWC;
-    f32x4 acc[DB][CB][4];
+    // acc[..][3] collects Gi^T Xr and accn the Gr^T Xi it loses (Pi is their
+    // difference, taken once at the end): no fragment is ever negated
+    f32x4 acc[DB][CB][4], accn[DB][CB];
 #pragma unroll
     for (int a = 0; a < DB; ++a)
 #pragma unroll
-      for (int b = 0; b < CB; ++b)
+      for (int b = 0; b < CB; ++b) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) acc[a][b][p] = f32x4{};
+        accn[a][b] = f32x4{};
+      }
     auto compute_step = [&](const _Float16* buf) {
       half8 gf[DB][4];
 #pragma unroll
@@ -266,7 +270,6 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
         const half8 x2 = *reinterpret_cast<const half8*>(xb + 1 * PSTR);
         const half8 xr = *reinterpret_cast<const half8*>(xb + 2 * PSTR);
         const half8 xi = *reinterpret_cast<const half8*>(xb + 3 * PSTR);
-        const half8 xq = -xi;
 #pragma unroll
         for (int a = 0; a < DB; ++a) {
           acc[a][b][0] = mma16(gf[a][0], x0, acc[a][b][0]);
@@ -274,7 +277,7 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
           acc[a][b][1] = mma16(gf[a][1], x2, acc[a][b][1]);
           acc[a][b][3] = mma16(gf[a][3], xr, acc[a][b][3]);
           acc[a][b][2] = mma16(gf[a][3], xi, acc[a][b][2]);
-          acc[a][b][3] = mma16(gf[a][2], xq, acc[a][b][3]);
+          accn[a][b] = mma16(gf[a][2], xi, accn[a][b]);
         }
       }
     };
@@ -296,6 +299,7 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
       for (int b = 0; b < CB; ++b) {
         const int d = d0 + (wd * DB + a) * 16 + 4 * g;
         const int c = c0 + (wc * CB + b) * 16 + i16;
+        acc[a][b][3] -= accn[a][b];
 #pragma unroll
         for (int p = 0; p < 4; ++p)
           *reinterpret_cast<f32x4*>(pout + p * plane + (int64_t)c * d_pad + d) = acc[a][b][p];
