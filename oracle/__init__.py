@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for the EQ-Linear layer (any cyclic group size T).
+"""Plain fp64 CPU oracle for the EQ-Linear layer (cyclic groups C_T and
+dihedral groups D_n).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this package:
 only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -12,6 +13,11 @@ forms, special cases that reduce to library routines, invariants, finite
 differences); none of it is "parity unpinned".
 """
 from .eqlinear_oracle import (  # noqa: F401
+    GROUPS,
+    dihedral_multiply,
+    dihedral_inverse,
+    tap_table,
+    unroll_group,
     unroll_block_circulant,
     forward,
     gelu,
