@@ -88,10 +88,15 @@ def read_traffic(kernel_key, src_hash):
     return float(v) if v is not None else None
 
 
-def real_products(T):
+def real_products(T, group="cyclic"):
     """Real matrix products per (row, input channel, output channel) of the
-    group-DFT method: one per real kept frequency (0, and T/2 for even T) and
-    four per complex kept frequency; T = 4 gives the six products of p4."""
+    group-DFT method.  Cyclic: one per real kept frequency (0, and T/2 for
+    even T) and four per complex kept frequency; T = 4 gives the six products
+    of p4.  Dihedral D_n (T = 2n): one per one-dimensional representation and
+    eight per 2 x 2 block; p4m (T = 8) gives 12."""
+    if group == "dihedral":
+        n = T // 2
+        return (4 if n % 2 == 0 else 2) + 8 * ((n - 1) // 2)
     return 1 + 4 * ((T - 1) // 2) + (1 if T % 2 == 0 else 0)
 
 
@@ -324,9 +329,9 @@ def all_configs(args):
             inp = make_inputs(C, D, N, T, dtype=dtype, seed=0, bias=w.bias,
                               dy="backward" in w.passes)
             t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items() if v is not None}
-            plan = eq.Plan(C, D, dtype, T=T)
+            plan = eq.Plan(C, D, dtype, T=T, group=w.group)
             plan.set_weight(t["W"], t.get("bias"))
-            flops = 2.0 * real_products(T) * N * C * D
+            flops = 2.0 * real_products(T, w.group) * N * C * D
             spec = T * C * D * esz
             passes = {}
             if "forward" in w.passes:
@@ -353,10 +358,11 @@ def all_configs(args):
                 ridge = PEAK_MFMA_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
                 bound = "hbm" if flops / nbytes < ridge else "mfma"
                 frac = gbps / PEAK_HBM_GBPS if bound == "hbm" else tf / PEAK_MFMA_TFLOPS[dtype]
-                print(json.dumps({"workload": w.name, "N": N, "C": C, "D": D, "T": T, "dtype": dtype,
+                print(json.dumps({"workload": w.name, "group": w.group, "N": N, "C": C, "D": D, "T": T,
+                                  "dtype": dtype,
                                   "pass": name, "us": round(us, 3),
                                   "tflops_actual": round(tf, 2),
-                                  "tflops_dense_equiv": round(tf * T * T / real_products(T), 2),
+                                  "tflops_dense_equiv": round(tf * T * T / real_products(T, w.group), 2),
                                   "mfma_peak_frac": round(tf / PEAK_MFMA_TFLOPS[dtype], 4),
                                   "hbm_gbps": round(gbps, 1), "alg_bytes": nbytes,
                                   "roofline": {"bound": bound, "frac": round(frac, 4)}}),

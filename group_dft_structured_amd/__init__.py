@@ -1,5 +1,6 @@
 """Python binding of libeqlinear, the EQ-Linear layer of the cyclic rotation
-groups (p4 and C_2 .. C_16) on MI355X (gfx950).
+groups (p4 and C_2 .. C_16) and of the dihedral groups (p4m and D_2 .. D_8)
+on MI355X (gfx950).
 
 Argument marshalling only: every step of the layer runs in the HIP kernels of
 ``libeqlinear.so``.  PyTorch supplies device memory and streams; the functions
@@ -17,6 +18,10 @@ LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
 
 EQL_F32 = 0
 EQL_F16 = 1
+
+EQL_GROUP_CYCLIC = 0
+EQL_GROUP_DIHEDRAL = 1
+GROUPS = {"cyclic": EQL_GROUP_CYCLIC, "dihedral": EQL_GROUP_DIHEDRAL}
 
 EQL_ACT_NONE = 0
 EQL_ACT_GELU = 1
@@ -37,6 +42,7 @@ STATUS = {
 
 EXPORTED = (
     "eqlinear_plan_create",
+    "eqlinear_plan_create_group",
     "eqlinear_plan_destroy",
     "eqlinear_set_weight",
     "eqlinear_forward",
@@ -79,6 +85,9 @@ def load_library(path=LIB_PATH):
     vp, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.eqlinear_plan_create.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(vp)]
     lib.eqlinear_plan_create.restype = st
+    lib.eqlinear_plan_create_group.argtypes = [i64, i64, ctypes.c_int, i64, ctypes.c_int,
+                                               ctypes.POINTER(vp)]
+    lib.eqlinear_plan_create_group.restype = st
     lib.eqlinear_plan_destroy.argtypes = [vp]
     lib.eqlinear_plan_destroy.restype = st
     lib.eqlinear_set_weight.argtypes = [vp, vp, vp, vp]
@@ -138,6 +147,14 @@ def eqlinear_plan_create(C, D, T=4, dtype=EQL_F32):
     return h.value
 
 
+def eqlinear_plan_create_group(C, D, group, n, dtype=EQL_F32):
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.eqlinear_plan_create_group(C, D, group, n, dtype, ctypes.byref(h)),
+           "eqlinear_plan_create_group")
+    return h.value
+
+
 def eqlinear_plan_destroy(plan):
     _check(load_library().eqlinear_plan_destroy(plan), "eqlinear_plan_destroy")
 
@@ -194,11 +211,21 @@ _DTYPE_CODE = {"f32": EQL_F32, "f16": EQL_F16}
 
 
 class Plan:
-    """Owns one plan handle; calls take contiguous torch CUDA tensors."""
+    """Owns one plan handle; calls take contiguous torch CUDA tensors.
 
-    def __init__(self, C, D, dtype="f16", T=4):
-        self.C, self.D, self.T, self.dtype = C, D, T, dtype
-        self.handle = eqlinear_plan_create(C, D, T, _DTYPE_CODE[dtype])
+    group="cyclic": C_T with T group values per channel (T = 4 is p4).
+    group="dihedral": D_n with n = T // 2 rotations and T = 2n group values
+    per channel (T = 8 is p4m); T must then be even."""
+
+    def __init__(self, C, D, dtype="f16", T=4, group="cyclic"):
+        self.C, self.D, self.T, self.dtype, self.group = C, D, T, dtype, group
+        if group == "cyclic":
+            self.handle = eqlinear_plan_create(C, D, T, _DTYPE_CODE[dtype])
+        else:
+            if T % 2:
+                raise ValueError("a dihedral group has an even number of elements")
+            self.handle = eqlinear_plan_create_group(C, D, GROUPS[group], T // 2,
+                                                     _DTYPE_CODE[dtype])
 
     def close(self):
         if self.handle:

@@ -1,5 +1,6 @@
-// Device helpers for the cyclic-group kernels: the real DFT of length T
-// along the group axis and its inverse, for any group size 2 <= T <= 16.
+// Device helpers for the generic group kernels: the real DFT of length T
+// along the group axis and its inverse, for any group size 2 <= T <= 16, and
+// the group descriptors (cyclic C_T, dihedral D_n) built on it.
 //
 // Flash EQ-Linear, "Approccio Algoritmico": the EQ-Linear layer is a
 // circular convolution along the group axis composed with a linear map
@@ -188,6 +189,196 @@ __host__ __device__ __forceinline__ void dft_inv(const R (&Q)[T], R (&y)[T]) {
     }
   });
 }
+
+// ---- group descriptors ------------------------------------------------------
+// The kernels of k_cyclic.hip are written once over a descriptor G that
+// gives the group order T (values per group vector and spectral planes),
+// the forward transform of one group vector into its T planes, the inverse
+// (with the 1/|G| scalings), the plane map of the adjoint spectrum, and the
+// matrix-core products of the forward (input planes times weight planes)
+// and of the weight gradient (upstream-gradient planes against input
+// planes, summed over rows).  Each product step takes a functor
+// mma(a, b, c) = c + a b over fragments of the two operands (and neg(a) =
+// -a), so the same schedule serves matrix-core fragments and scalars.
+
+// Cyclic group C_T: the real DFT above.  Frequency k > 0 below T/2 is a
+// complex product (Xr + i Xi)(Wr + i Wi), four real products; the adjoint
+// spectrum is the complex conjugate (imaginary planes negated).
+template <int TT>
+struct Cyclic {
+  static constexpr int T = TT;
+  static constexpr int PRODUCTS = 1 + 4 * NCX<T> + (HAS_NYQ<T> ? 1 : 0);
+  template <typename R>
+  static __host__ __device__ __forceinline__ void fwd(const R (&x)[T], R (&X)[T]) {
+    dft_fwd<T, R>(x, X);
+  }
+  template <typename R>
+  static __host__ __device__ __forceinline__ void inv(const R (&Q)[T], R (&y)[T]) {
+    dft_inv<T, R>(Q, y);
+  }
+  static constexpr __host__ __device__ int adj_src(int j) { return j; }
+  static constexpr __host__ __device__ bool adj_neg(int j) {
+    return j >= 2 && j <= 2 * NCX<T> && (j % 2) == 0;
+  }
+  // c += A W per frequency; the minus sign of the real part is a sign flip of
+  // the imaginary input fragment (neg)
+  template <typename Acc, typename Frag, typename Mma, typename Neg>
+  static __host__ __device__ __forceinline__ void fwd_mma(Acc (&c)[T], const Frag (&a)[T],
+                                                          const Frag (&b)[T], Mma mma, Neg neg) {
+    c[0] = mma(a[0], b[0], c[0]);
+    static_for<1, NCX<T> + 1>([&](auto kk) {
+      constexpr int k = decltype(kk)::value, re = 2 * k - 1, im = 2 * k;
+      // (Xr + i Xi)(Wr + i Wi) = (Xr Wr - Xi Wi) + i (Xr Wi + Xi Wr)
+      c[re] = mma(a[re], b[re], c[re]);
+      c[re] = mma(neg(a[im]), b[im], c[re]);
+      c[im] = mma(a[re], b[im], c[im]);
+      c[im] = mma(a[im], b[re], c[im]);
+    });
+    if constexpr (HAS_NYQ<T>) c[T - 1] = mma(a[T - 1], b[T - 1], c[T - 1]);
+  }
+  // c += G conj(X) per frequency (the weight gradient before the inverse)
+  template <typename Acc, typename Frag, typename Mma, typename Neg>
+  static __host__ __device__ __forceinline__ void bw_mma(Acc (&c)[T], const Frag (&g)[T],
+                                                         const Frag (&x)[T], Mma mma, Neg neg) {
+    c[0] = mma(g[0], x[0], c[0]);
+    static_for<1, NCX<T> + 1>([&](auto kk) {
+      constexpr int k = decltype(kk)::value, re = 2 * k - 1, im = 2 * k;
+      // G conj(X) = (Gr Xr + Gi Xi) + i (Gi Xr - Gr Xi)
+      c[re] = mma(g[re], x[re], c[re]);
+      c[re] = mma(g[im], x[im], c[re]);
+      c[im] = mma(g[im], x[re], c[im]);
+      c[im] = mma(neg(g[re]), x[im], c[im]);
+    });
+    if constexpr (HAS_NYQ<T>) c[T - 1] = mma(g[T - 1], x[T - 1], c[T - 1]);
+  }
+};
+
+// Dihedral group D_n of order T = 2n, elements rho^r sigma^m at index
+// m n + r (rho the rotation by 2 pi / n, sigma a reflection,
+// sigma rho sigma = rho^-1), read as the reflection groups the pages name as
+// the next step ("Limitazioni e Lavoro Futuro"; p4m is D_4).  The layer is
+// the group convolution y[g] = sum_h W[h^-1 g] x[h]; its group Fourier
+// transform over the real irreducible representations pi,
+// x^(pi) = sum_h x[h] pi(h), turns it into y^(pi) = x^(pi) W^(pi):
+//  * one-dimensional representations rho -> a, sigma -> b with a = +-1 (-1
+//    only for even n) and b = +-1: one real product each;
+//  * two-dimensional pi_k (1 <= k <= (n-1)/2): rho -> rotation by
+//    2 pi k / n, sigma -> diag(1, -1); a 2 x 2 block product, eight real
+//    products.
+// Both transforms need the length-n DFT of the two cosets only:
+// sum_r u[r] pi_k(rho^r) = [[a, -b], [b, a]] with a + i(-b) the DFT of u at
+// k, and the reflection coset is multiplied by diag(1, -1) on the right.
+// Planes: 0: (+,+) = S0 + S1, 1: (+,-) = S0 - S1, and for even n 2: (-,+) =
+// A0 + A1, 3: (-,-) = A0 - A1 (S_m, A_m the DFT of coset m at 0 and n/2);
+// then four planes per pi_k, the block entries 00, 01, 10, 11.  The
+// inversion y[g] = (1/2n) sum_pi dim(pi) tr(y^(pi) pi(g)^T) is, per coset,
+// a length-n inverse DFT of combined planes.
+template <int NN>
+struct Dihedral {
+  static constexpr int n = NN, T = 2 * NN;
+  static constexpr int N1 = (NN % 2 == 0) ? 4 : 2;  // one-dimensional representations
+  static constexpr int N2 = (NN - 1) / 2;            // two-dimensional representations
+  static constexpr int PRODUCTS = N1 + 8 * N2;
+  template <typename R>
+  static __host__ __device__ __forceinline__ void fwd(const R (&x)[T], R (&X)[T]) {
+    R u0[n], u1[n], U0[n], U1[n];
+    static_for<0, n>([&](auto ss) {
+      constexpr int s = decltype(ss)::value;
+      u0[s] = x[s];
+      u1[s] = x[n + s];
+    });
+    dft_fwd<n, R>(u0, U0);
+    dft_fwd<n, R>(u1, U1);
+    X[0] = U0[0] + U1[0];
+    X[1] = U0[0] - U1[0];
+    if constexpr (n % 2 == 0) {
+      X[2] = U0[n - 1] + U1[n - 1];
+      X[3] = U0[n - 1] - U1[n - 1];
+    }
+    static_for<1, N2 + 1>([&](auto kk) {
+      constexpr int k = decltype(kk)::value, p = N1 + 4 * (k - 1);
+      // a_m = Re U_m[k], b_m = -Im U_m[k]
+      X[p] = U0[2 * k - 1] + U1[2 * k - 1];       // a0 + a1
+      X[p + 1] = U0[2 * k] - U1[2 * k];           // -b0 + b1
+      X[p + 2] = -(U0[2 * k] + U1[2 * k]);        // b0 + b1
+      X[p + 3] = U0[2 * k - 1] - U1[2 * k - 1];   // a0 - a1
+    });
+  }
+  template <typename R>
+  static __host__ __device__ __forceinline__ void inv(const R (&Q)[T], R (&y)[T]) {
+    const R h = (R)0.5;
+    R V0[n], V1[n], y0[n], y1[n];
+    V0[0] = (Q[0] + Q[1]) * h;
+    V1[0] = (Q[0] - Q[1]) * h;
+    if constexpr (n % 2 == 0) {
+      V0[n - 1] = (Q[2] + Q[3]) * h;
+      V1[n - 1] = (Q[2] - Q[3]) * h;
+    }
+    static_for<1, N2 + 1>([&](auto kk) {
+      constexpr int k = decltype(kk)::value, p = N1 + 4 * (k - 1);
+      // rotation coset: tr(Y R^T) = cos (Y00 + Y11) + sin (Y10 - Y01);
+      // reflection coset: tr(Y (R F)^T) = cos (Y00 - Y11) + sin (Y01 + Y10)
+      V0[2 * k - 1] = (Q[p] + Q[p + 3]) * h;
+      V0[2 * k] = (Q[p + 1] - Q[p + 2]) * h;
+      V1[2 * k - 1] = (Q[p] - Q[p + 3]) * h;
+      V1[2 * k] = -(Q[p + 1] + Q[p + 2]) * h;
+    });
+    dft_inv<n, R>(V0, y0);
+    dft_inv<n, R>(V1, y1);
+    static_for<0, n>([&](auto ss) {
+      constexpr int s = decltype(ss)::value;
+      y[s] = y0[s];
+      y[n + s] = y1[s];
+    });
+  }
+  // adjoint (transposed) layer: W*[c, d, v] = W[d, c, v^-1] has spectrum
+  // W^(pi)^T, so the off-diagonal block entries swap
+  static constexpr __host__ __device__ int adj_src(int j) {
+    return j < N1 ? j : ((j - N1) % 4 == 1 ? j + 1 : (j - N1) % 4 == 2 ? j - 1 : j);
+  }
+  static constexpr __host__ __device__ bool adj_neg(int) { return false; }
+  // c += x^ W^ per representation
+  template <typename Acc, typename Frag, typename Mma, typename Neg>
+  static __host__ __device__ __forceinline__ void fwd_mma(Acc (&c)[T], const Frag (&a)[T],
+                                                          const Frag (&b)[T], Mma mma, Neg) {
+    static_for<0, N1>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      c[j] = mma(a[j], b[j], c[j]);
+    });
+    static_for<1, N2 + 1>([&](auto kk) {
+      constexpr int p = N1 + 4 * (decltype(kk)::value - 1);
+      c[p] = mma(a[p], b[p], c[p]);                  // Y00 = X00 W00 + X01 W10
+      c[p] = mma(a[p + 1], b[p + 2], c[p]);
+      c[p + 1] = mma(a[p], b[p + 1], c[p + 1]);      // Y01 = X00 W01 + X01 W11
+      c[p + 1] = mma(a[p + 1], b[p + 3], c[p + 1]);
+      c[p + 2] = mma(a[p + 2], b[p], c[p + 2]);      // Y10 = X10 W00 + X11 W10
+      c[p + 2] = mma(a[p + 3], b[p + 2], c[p + 2]);
+      c[p + 3] = mma(a[p + 2], b[p + 1], c[p + 3]);  // Y11 = X10 W01 + X11 W11
+      c[p + 3] = mma(a[p + 3], b[p + 3], c[p + 3]);
+    });
+  }
+  // c += x^(pi)^T g^(pi) per representation: the spectrum of the weight
+  // gradient, sum_h x[h] pi(h)^T times sum_v dy[v] pi(v)
+  template <typename Acc, typename Frag, typename Mma, typename Neg>
+  static __host__ __device__ __forceinline__ void bw_mma(Acc (&c)[T], const Frag (&g)[T],
+                                                         const Frag (&x)[T], Mma mma, Neg) {
+    static_for<0, N1>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      c[j] = mma(g[j], x[j], c[j]);
+    });
+    static_for<1, N2 + 1>([&](auto kk) {
+      constexpr int p = N1 + 4 * (decltype(kk)::value - 1);
+      c[p] = mma(g[p], x[p], c[p]);                  // P00 = X00 G00 + X10 G10
+      c[p] = mma(g[p + 2], x[p + 2], c[p]);
+      c[p + 1] = mma(g[p + 1], x[p], c[p + 1]);      // P01 = X00 G01 + X10 G11
+      c[p + 1] = mma(g[p + 3], x[p + 2], c[p + 1]);
+      c[p + 2] = mma(g[p], x[p + 1], c[p + 2]);      // P10 = X01 G00 + X11 G10
+      c[p + 2] = mma(g[p + 2], x[p + 3], c[p + 2]);
+      c[p + 3] = mma(g[p + 1], x[p + 1], c[p + 3]);  // P11 = X01 G01 + X11 G11
+      c[p + 3] = mma(g[p + 3], x[p + 3], c[p + 3]);
+    });
+  }
+};
 
 }  // namespace cyc
 }  // namespace eql

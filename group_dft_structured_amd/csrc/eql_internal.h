@@ -28,8 +28,9 @@ struct SpectraLayout {
 
 struct eqlinear_plan {
   int64_t C, D;
-  int T;        // group size (2..16)
-  bool cyclic;  // served by the cyclic-group kernels (every T but 4, or on request)
+  int T;        // group order: values per group vector (2..16)
+  eqlinear_group_t group;  // cyclic C_T or dihedral D_{T/2}
+  bool cyclic;  // served by the generic group kernels (every group but p4, or on request)
   // cyclic backward_weight: tile edge (64 or 32) and work-group target, fixed
   // at plan creation so that workspace size and launch always agree
   int cyc_bw_tile, cyc_bw_wgs;
@@ -38,9 +39,11 @@ struct eqlinear_plan {
   int device;    // device of the spectra, -1 before the first set_weight
   bool has_weight;
   // Forward operand: T planes, each [D_pad][C_pad]: for the p4 kernels
-  // {W0, W2, Wr, Wi}, for the cyclic kernels the order of cyc_device.h.
+  // {W0, W2, Wr, Wi}, for the generic kernels the order of the group
+  // descriptor in cyc_device.h.
   eql::SpectraLayout fwd;
-  // Backward-input operand: the conjugate transposes, each [C_pad][D_pad].
+  // Backward-input operand: the spectra of the adjoint layer (conjugate or
+  // block-transposed), each [C_pad][D_pad].
   eql::SpectraLayout adj;
   void* spec_fwd;     // device, plan dtype
   void* spec_adj;     // device, plan dtype

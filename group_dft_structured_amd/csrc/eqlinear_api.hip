@@ -22,8 +22,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // the kernels stays in range below these).
 constexpr int64_t MAX_CHANNELS = 1 << 16;
 constexpr int64_t MAX_ROWS = (int64_t)1 << 30;
-// Group sizes with kernels: the cyclic groups C_2 .. C_16.
+// Groups with kernels: the cyclic groups C_2 .. C_16 and the dihedral
+// groups D_2 .. D_8 (orders 4 .. 16).
 constexpr int64_t MIN_T = 2, MAX_T = 16;
+constexpr int64_t MIN_DIH = 2, MAX_DIH = 8;
 
 eqlinear_status_t check_device(const eqlinear_plan* p) {
   int cur = -1;
@@ -48,7 +50,7 @@ const char* eqlinear_status_string(eqlinear_status_t st) {
   switch (st) {
     case EQL_OK: return "ok";
     case EQL_ERR_INVALID_ARG: return "invalid argument";
-    case EQL_ERR_UNSUPPORTED: return "unsupported group size or dtype";
+    case EQL_ERR_UNSUPPORTED: return "unsupported group, group order or dtype";
     case EQL_ERR_NO_WEIGHT: return "no weight set on the plan";
     case EQL_ERR_MISALIGNED: return "buffer not 16-byte aligned";
     case EQL_ERR_WORKSPACE: return "workspace missing or too small";
@@ -62,9 +64,24 @@ const char* eqlinear_last_error(void) { return g_last_error; }
 
 eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T, eqlinear_dtype_t dtype,
                                        eqlinear_plan_t* out) {
+  return eqlinear_plan_create_group(C, D, EQL_GROUP_CYCLIC, T, dtype, out);
+}
+
+eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_group_t group,
+                                             int64_t n, eqlinear_dtype_t dtype,
+                                             eqlinear_plan_t* out) {
   if (out == nullptr) return EQL_ERR_INVALID_ARG;
   *out = nullptr;
-  if (T < MIN_T || T > MAX_T) return EQL_ERR_UNSUPPORTED;
+  int64_t T = 0;
+  if (group == EQL_GROUP_CYCLIC) {
+    if (n < MIN_T || n > MAX_T) return EQL_ERR_UNSUPPORTED;
+    T = n;
+  } else if (group == EQL_GROUP_DIHEDRAL) {
+    if (n < MIN_DIH || n > MAX_DIH) return EQL_ERR_UNSUPPORTED;
+    T = 2 * n;
+  } else {
+    return EQL_ERR_UNSUPPORTED;
+  }
   if (dtype != EQL_F32 && dtype != EQL_F16) return EQL_ERR_UNSUPPORTED;
   if (C <= 0 || D <= 0 || C > MAX_CHANNELS || D > MAX_CHANNELS) return EQL_ERR_INVALID_ARG;
   eqlinear_plan* p = new (std::nothrow) eqlinear_plan;
@@ -73,10 +90,12 @@ eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T, eqlinear
   p->C = C;
   p->D = D;
   p->T = (int)T;
+  p->group = group;
   {
-    // T = 4 runs the p4 kernels unless EQL_CYCLIC_P4 asks for the cyclic ones
+    // the cyclic T = 4 (p4) runs the p4 kernels unless EQL_CYCLIC_P4 asks for
+    // the generic ones; every other group runs the generic ones
     const char* env = getenv("EQL_CYCLIC_P4");
-    p->cyclic = T != 4 || (env != nullptr && atoi(env) != 0);
+    p->cyclic = group != EQL_GROUP_CYCLIC || T != 4 || (env != nullptr && atoi(env) != 0);
     const char* tile = getenv("EQL_CYC_BW_TILE");
     p->cyc_bw_tile = (tile != nullptr && atoi(tile) == 64 && T <= 8) ? 64 : 32;
     const char* wgs = getenv("EQL_CYC_BW_WGS");
@@ -222,11 +241,17 @@ eqlinear_status_t eqlinear_backward_weight(eqlinear_plan_t p, const void* x, con
 eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t p, int64_t N, int64_t* spectral_macs,
                                       int64_t* dense_macs) {
   if (p == nullptr || N < 0) return EQL_ERR_INVALID_ARG;
-  // Real DFT of length T: frequency 0 (and T/2 for even T) is real, one
-  // product each; each kept complex frequency 1 <= k < T - k costs four real
-  // products; the others are conjugates (free).  p4: 1 + 4 + 1 = 6 of 16.
+  // Cyclic: real DFT of length T: frequency 0 (and T/2 for even T) is real,
+  // one product each; each kept complex frequency 1 <= k < T - k costs four
+  // real products; the others are conjugates (free).  p4: 1 + 4 + 1 = 6 of 16.
+  // Dihedral D_n: one product per one-dimensional representation (4 for even
+  // n, 2 for odd n) and eight per two-dimensional one ((n - 1) / 2 of them).
   const int64_t T = p->T;
-  const int64_t products = 1 + 4 * ((T - 1) / 2) + (T % 2 == 0 ? 1 : 0);
+  int64_t products = 1 + 4 * ((T - 1) / 2) + (T % 2 == 0 ? 1 : 0);
+  if (p->group == EQL_GROUP_DIHEDRAL) {
+    const int64_t n = T / 2;
+    products = (n % 2 == 0 ? 4 : 2) + 8 * ((n - 1) / 2);
+  }
   const int64_t ncd = N * p->C * p->D;
   if (spectral_macs) *spectral_macs = products * ncd;
   if (dense_macs) *dense_macs = T * T * ncd;

@@ -97,6 +97,22 @@ struct Tr<float> {
   }
 };
 
+// Product step and sign flip of one fragment, as functors for the group
+// descriptors' product schedules.
+template <typename DT>
+struct MmaOp {
+  __device__ __forceinline__ f32x4 operator()(typename Tr<DT>::frag a, typename Tr<DT>::frag b,
+                                              f32x4 c) const {
+    return Tr<DT>::mma(a, b, c);
+  }
+};
+template <typename DT>
+struct NegOp {
+  __device__ __forceinline__ typename Tr<DT>::frag operator()(typename Tr<DT>::frag a) const {
+    return Tr<DT>::neg(a);
+  }
+};
+
 // One group vector (T contiguous values) in global memory.  Its byte offset
 // is a multiple of T * sizeof(DT) from a 16-byte aligned base, so it is
 // moved in pieces of the largest power of two dividing that size (<= 16).
@@ -160,18 +176,13 @@ __device__ __forceinline__ float to_f(DT v) {
   return (float)v;
 }
 
-// Imaginary planes (2k, 1 <= k <= NCX) change sign under conjugation.
-template <int T>
-__host__ __device__ constexpr bool is_imag_plane(int j) {
-  return j >= 2 && j <= 2 * NCX<T> && (j % 2) == 0;
-}
-
 // ---- weight spectra --------------------------------------------------------
-template <int T, typename DT>
+template <typename G, typename DT>
 __global__ __launch_bounds__(256) void k_cyc_spectra(
     const DT* __restrict__ W, const DT* __restrict__ bias, DT* __restrict__ spec_fwd,
     DT* __restrict__ spec_adj, float* __restrict__ bias_f32, float* __restrict__ zeros_f32, int C,
     int D, int fwd_n, int fwd_k, int adj_n, int adj_k) {
+  constexpr int T = G::T;
   const int64_t fwd_elems = (int64_t)fwd_n * fwd_k;
   const int64_t adj_elems = (int64_t)adj_n * adj_k;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(256) void k_cyc_spectra(
       double w[T];
       const DT* src = W + ((int64_t)d * C + c) * T;
       for (int s = 0; s < T; ++s) w[s] = (double)to_f(src[s]);
-      dft_fwd<T, double>(w, X);
+      G::template fwd<double>(w, X);
     }
   };
   if (i < fwd_elems) {
@@ -201,8 +212,8 @@ __global__ __launch_bounds__(256) void k_cyc_spectra(
     spectrum(d, c, X);
     static_for<0, T>([&](auto jj) {
       constexpr int j = decltype(jj)::value;
-      const float v = (float)X[j];
-      spec_adj[j * adj_elems + k] = (DT)(is_imag_plane<T>(j) ? -v : v);
+      const float v = (float)X[G::adj_src(j)];
+      spec_adj[j * adj_elems + k] = (DT)(G::adj_neg(j) ? -v : v);
     });
     return;
   }
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(256) void k_cyc_spectra(
 // Tile BM rows x BN output channels, 4 waves as 2 x 2, each wave (BM/2) x
 // (BN/2) in 16 x 16 blocks.  LDS per chunk: T planes of the a-tile [BM][64 B]
 // and of the weight tile [BN][64 B].
-template <int T, typename DT, int BM, int BN, bool ACT>
+template <typename G, typename DT, int BM, int BN, bool ACT>
 __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
                                                   const DT* __restrict__ spec,
                                                   const float* __restrict__ bias,
@@ -228,6 +239,7 @@ __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
                                                   int col_tiles, int per_xcd, int act) {
   typedef Tr<DT> F;
   typedef typename F::frag frag;
+  constexpr int T = G::T;
   constexpr int KC = F::KC;
   constexpr int RB = BM / 32, NB = BN / 32;
   constexpr int UX = BM * KC / 256;      // group vectors per thread per chunk
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
       float xf[T], X[T];
 #pragma unroll
       for (int s = 0; s < T; ++s) xf[s] = to_f(xv[i][s]);
-      dft_fwd<T, float>(xf, X);
+      G::template fwd<float>(xf, X);
 #pragma unroll
       for (int j = 0; j < T; ++j)
         *reinterpret_cast<DT*>(lx + (j * BM + r) * 64 + c * (int)sizeof(DT)) = (DT)X[j];
@@ -317,19 +329,8 @@ __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
         ax[j] = *reinterpret_cast<const frag*>(
             lx + (j * BM + wm * RB * 16 + rb * 16 + i16) * 64 + g * 16);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4(&c)[T] = acc[rb][nb];
-        c[0] = F::mma(ax[0], bw[nb][0], c[0]);
-        static_for<1, NCX<T> + 1>([&](auto kk) {
-          constexpr int k = decltype(kk)::value, re = 2 * k - 1, im = 2 * k;
-          // (Xr + i Xi)(Wr + i Wi) = (Xr Wr - Xi Wi) + i (Xr Wi + Xi Wr)
-          c[re] = F::mma(ax[re], bw[nb][re], c[re]);
-          c[re] = F::mma(F::neg(ax[im]), bw[nb][im], c[re]);
-          c[im] = F::mma(ax[re], bw[nb][im], c[im]);
-          c[im] = F::mma(ax[im], bw[nb][re], c[im]);
-        });
-        if constexpr (HAS_NYQ<T>) c[T - 1] = F::mma(ax[T - 1], bw[nb][T - 1], c[T - 1]);
-      }
+      for (int nb = 0; nb < NB; ++nb)
+        G::fwd_mma(acc[rb][nb], ax, bw[nb], MmaOp<DT>{}, NegOp<DT>{});
     }
   };
 
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
         float Q[T], y[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) Q[j] = acc[rb][nb][j][r];
-        dft_inv<T, float>(Q, y);
+        G::template inv<float>(Q, y);
         DT o[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
 // Tile TD (d) x TC (c), 4 waves as 2 x 2.  Per step of KC rows: the DFT of
 // dy and x, written to LDS transposed ([column][rows], rows contiguous, an
 // 80-byte pitch that spreads the column-wise writes over the banks).
-template <int T, typename DT, int TD, int TC>
+template <typename G, typename DT, int TD, int TC>
 __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
                                                  const DT* __restrict__ dy,
                                                  float* __restrict__ part,
@@ -388,6 +389,7 @@ __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
                                                  int per_xcd) {
   typedef Tr<DT> F;
   typedef typename F::frag frag;
+  constexpr int T = G::T;
   constexpr int RS = F::KC;  // rows per step
   constexpr int PITCH = 80;
   constexpr int RB = TD / 32, NB = TC / 32;
@@ -451,20 +453,20 @@ __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
   auto store_step = [&]() {
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
-      float G[2][T];
+      float Gs[2][T];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         float v[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) v[t] = to_f(gv[i][h][t]);
-        dft_fwd<T, float>(v, G[h]);
+        G::template fwd<float>(v, Gs[h]);
       }
-      bsum += G[0][0];
-      bsum += G[1][0];
+      bsum += Gs[0][0];
+      bsum += Gs[1][0];
       const int rp = dgrp + GD * i;
 #pragma unroll
       for (int j = 0; j < T; ++j) {
-        DT two[2] = {(DT)G[0][j], (DT)G[1][j]};
+        DT two[2] = {(DT)Gs[0][j], (DT)Gs[1][j]};
         __builtin_memcpy(lg + (j * TD + dcol) * PITCH + rp * 2 * (int)sizeof(DT), two, sizeof(two));
       }
     }
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
         float v[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) v[t] = to_f(xv[i][h][t]);
-        dft_fwd<T, float>(v, X[h]);
+        G::template fwd<float>(v, X[h]);
       }
       const int rp = cgrp + GC * i;
 #pragma unroll
@@ -511,19 +513,8 @@ __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
         ga[j] = *reinterpret_cast<const frag*>(
             lg + (j * TD + wm * RB * 16 + rb * 16 + i16) * PITCH + g * 16);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4(&c)[T] = acc[rb][nb];
-        c[0] = F::mma(ga[0], xb[nb][0], c[0]);
-        static_for<1, NCX<T> + 1>([&](auto kk) {
-          constexpr int k = decltype(kk)::value, re = 2 * k - 1, im = 2 * k;
-          // G conj(X) = (Gr Xr + Gi Xi) + i (Gi Xr - Gr Xi)
-          c[re] = F::mma(ga[re], xb[nb][re], c[re]);
-          c[re] = F::mma(ga[im], xb[nb][im], c[re]);
-          c[im] = F::mma(ga[im], xb[nb][re], c[im]);
-          c[im] = F::mma(F::neg(ga[re]), xb[nb][im], c[im]);
-        });
-        if constexpr (HAS_NYQ<T>) c[T - 1] = F::mma(ga[T - 1], xb[nb][T - 1], c[T - 1]);
-      }
+      for (int nb = 0; nb < NB; ++nb)
+        G::bw_mma(acc[rb][nb], ga, xb[nb], MmaOp<DT>{}, NegOp<DT>{});
     }
   };
 
@@ -562,11 +553,12 @@ __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
   }
 }
 
-template <int T>
+template <typename G>
 __global__ __launch_bounds__(256) void k_cyc_bwf(const float* __restrict__ part,
                                                  const float* __restrict__ part_b,
                                                  float* __restrict__ dW, float* __restrict__ dbias,
                                                  int C, int D, int d_pad, int c_pad, int S) {
+  constexpr int T = G::T;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t DC = (int64_t)D * C;
   if (i < DC) {
@@ -578,7 +570,7 @@ __global__ __launch_bounds__(256) void k_cyc_bwf(const float* __restrict__ part,
 #pragma unroll
       for (int j = 0; j < T; ++j) P[j] += part[(((int64_t)s * T + j) * d_pad + d) * c_pad + c];
     float w[T];
-    dft_inv<T, float>(P, w);
+    G::template inv<float>(P, w);
 #pragma unroll
     for (int r = 0; r < T; ++r) dW[i * T + r] = w[r];
   } else if (dbias != nullptr && i < DC + D) {
@@ -615,7 +607,7 @@ BwDims bw_dims(const eqlinear_plan* p, int64_t N) {
   return b;
 }
 
-template <int T, typename DT, int BM, int BN, bool ACT = false>
+template <typename G, typename DT, int BM, int BN, bool ACT = false>
 hipError_t launch_gemm_tile(const void* a, const void* spec, const float* bias, void* out,
                             int64_t N, int K, int k_pad, int n_out, int n_pad, int act,
                             hipStream_t s) {
@@ -624,7 +616,7 @@ hipError_t launch_gemm_tile(const void* a, const void* spec, const float* bias, 
   const int64_t tiles = row_tiles * col_tiles;
   if (tiles > (int64_t)1 << 31) return hipErrorInvalidValue;
   const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL((k_cyc_gemm<T, DT, BM, BN, ACT>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_cyc_gemm<G, DT, BM, BN, ACT>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, s,
                      (const DT*)a, (const DT*)spec, bias, (DT*)out, (int)N, K, k_pad, n_out, n_pad,
                      (int)row_tiles, col_tiles, (int)per_xcd, act);
   return hipGetLastError();
@@ -637,15 +629,16 @@ int env_int(const char* name, int dflt) {
 
 // Tile shapes (rows x output channels): 0 = 64x64, 1 = 64x32, 2 = 32x64,
 // 3 = 32x32 (EQL_CYC_TILE overrides the default).
-template <int T, typename DT>
+template <typename G, typename DT>
 hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, void* out, int64_t N,
                          int K, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
+  constexpr int T = G::T;
   const bool wide = T <= 8 && sizeof(DT) == 2;
   if (act != ACT_NONE) {  // fused activation: the default tile only
     if (wide)
-      return launch_gemm_tile<T, DT, 32, 64, true>(a, spec, bias, out, N, K, k_pad, n_out, n_pad,
+      return launch_gemm_tile<G, DT, 32, 64, true>(a, spec, bias, out, N, K, k_pad, n_out, n_pad,
                                                    act, s);
-    return launch_gemm_tile<T, DT, 32, 32, true>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act,
+    return launch_gemm_tile<G, DT, 32, 32, true>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act,
                                                  s);
   }
   int cfg = env_int("EQL_CYC_TILE", wide ? 2 : 3);
@@ -653,76 +646,91 @@ hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, voi
   switch (cfg) {
     case 0:
       if constexpr (T <= 8)
-        return launch_gemm_tile<T, DT, 64, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
+        return launch_gemm_tile<G, DT, 64, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
       return hipErrorInvalidValue;
-    case 1: return launch_gemm_tile<T, DT, 64, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
-    case 2: return launch_gemm_tile<T, DT, 32, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
-    case 3: return launch_gemm_tile<T, DT, 32, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
+    case 1: return launch_gemm_tile<G, DT, 64, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
+    case 2: return launch_gemm_tile<G, DT, 32, 64>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
+    case 3: return launch_gemm_tile<G, DT, 32, 32>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int T, typename DT, int TD>
+template <typename G, typename DT, int TD>
 hipError_t launch_bw_tile(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
                           float* dbias, int64_t N, void* ws, hipStream_t s) {
+  constexpr int T = G::T;
   const BwDims b = bw_dims(p, N);
   if (b.TD != TD) return hipErrorInvalidValue;
   float* part = (float*)ws;
   float* part_b = part + b.S * T * (int64_t)b.d_pad * b.c_pad;
   const int64_t n_tiles = b.S * b.d_tiles * b.c_tiles;
   const int64_t per_xcd = (n_tiles + 7) / 8;
-  hipLaunchKernelGGL((k_cyc_bwp<T, DT, TD, TD>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_cyc_bwp<G, DT, TD, TD>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, s,
                      (const DT*)x, (const DT*)dy, part, part_b, (int)N, (int)p->C, (int)p->D,
                      (int)b.rows_per_split, b.d_pad, b.c_pad, b.d_tiles, b.c_tiles, (int)n_tiles,
                      (int)per_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = p->D * p->C + p->D;
-  hipLaunchKernelGGL(k_cyc_bwf<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
+  hipLaunchKernelGGL(k_cyc_bwf<G>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
                      part_b, dW, dbias, (int)p->C, (int)p->D, b.d_pad, b.c_pad, (int)b.S);
   return hipGetLastError();
 }
 
-template <int T, typename DT>
+template <typename G, typename DT>
 hipError_t launch_bw_t(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
                        float* dbias, int64_t N, void* ws, hipStream_t s) {
-  if constexpr (T <= 8) {
-    if (p->cyc_bw_tile == 64) return launch_bw_tile<T, DT, 64>(p, x, dy, dW, dbias, N, ws, s);
+  if constexpr (G::T <= 8) {
+    if (p->cyc_bw_tile == 64) return launch_bw_tile<G, DT, 64>(p, x, dy, dW, dbias, N, ws, s);
   }
-  return launch_bw_tile<T, DT, 32>(p, x, dy, dW, dbias, N, ws, s);
+  return launch_bw_tile<G, DT, 32>(p, x, dy, dW, dbias, N, ws, s);
 }
 
-template <int T, typename DT>
+template <typename G, typename DT>
 hipError_t launch_spectra_t(const eqlinear_plan* p, const void* W, const void* bias,
                             hipStream_t s) {
   const int64_t total = (int64_t)p->fwd.plane_elems() + (int64_t)p->adj.plane_elems() +
                         p->fwd.n_pad + p->adj.n_pad;
-  hipLaunchKernelGGL((k_cyc_spectra<T, DT>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL((k_cyc_spectra<G, DT>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                      s, (const DT*)W, (const DT*)bias, (DT*)p->spec_fwd, (DT*)p->spec_adj,
                      p->bias_f32, p->zeros_f32, (int)p->C, (int)p->D, (int)p->fwd.n_pad,
                      (int)p->fwd.k_pad, (int)p->adj.n_pad, (int)p->adj.k_pad);
   return hipGetLastError();
 }
 
-// Calls F<T, DT>::run(args...) for the plan's group size and dtype.
-#define EQL_CYC_DISPATCH(T_, DTYPE, CALL)                                      \
-  switch (T_) {                                                                \
-    case 2: return DTYPE == EQL_F16 ? CALL(2, _Float16) : CALL(2, float);      \
-    case 3: return DTYPE == EQL_F16 ? CALL(3, _Float16) : CALL(3, float);      \
-    case 4: return DTYPE == EQL_F16 ? CALL(4, _Float16) : CALL(4, float);      \
-    case 5: return DTYPE == EQL_F16 ? CALL(5, _Float16) : CALL(5, float);      \
-    case 6: return DTYPE == EQL_F16 ? CALL(6, _Float16) : CALL(6, float);      \
-    case 7: return DTYPE == EQL_F16 ? CALL(7, _Float16) : CALL(7, float);      \
-    case 8: return DTYPE == EQL_F16 ? CALL(8, _Float16) : CALL(8, float);      \
-    case 9: return DTYPE == EQL_F16 ? CALL(9, _Float16) : CALL(9, float);      \
-    case 10: return DTYPE == EQL_F16 ? CALL(10, _Float16) : CALL(10, float);   \
-    case 11: return DTYPE == EQL_F16 ? CALL(11, _Float16) : CALL(11, float);   \
-    case 12: return DTYPE == EQL_F16 ? CALL(12, _Float16) : CALL(12, float);   \
-    case 13: return DTYPE == EQL_F16 ? CALL(13, _Float16) : CALL(13, float);   \
-    case 14: return DTYPE == EQL_F16 ? CALL(14, _Float16) : CALL(14, float);   \
-    case 15: return DTYPE == EQL_F16 ? CALL(15, _Float16) : CALL(15, float);   \
-    case 16: return DTYPE == EQL_F16 ? CALL(16, _Float16) : CALL(16, float);   \
-    default: return hipErrorInvalidValue;                                      \
+// Instantiates CALL(G, DT) for the plan's group (cyclic C_T or dihedral D_n,
+// n = T / 2) and dtype, and returns its result.
+#define EQL_DT(G_, CALL) (p->dtype == EQL_F16 ? CALL(G_, _Float16) : CALL(G_, float))
+#define EQL_GROUP_DISPATCH(CALL)                                   \
+  if (p->group == EQL_GROUP_DIHEDRAL) {                            \
+    switch (p->T / 2) {                                            \
+      case 2: return EQL_DT(Dihedral<2>, CALL);                    \
+      case 3: return EQL_DT(Dihedral<3>, CALL);                    \
+      case 4: return EQL_DT(Dihedral<4>, CALL);                    \
+      case 5: return EQL_DT(Dihedral<5>, CALL);                    \
+      case 6: return EQL_DT(Dihedral<6>, CALL);                    \
+      case 7: return EQL_DT(Dihedral<7>, CALL);                    \
+      case 8: return EQL_DT(Dihedral<8>, CALL);                    \
+      default: return hipErrorInvalidValue;                        \
+    }                                                              \
+  }                                                                \
+  switch (p->T) {                                                  \
+    case 2: return EQL_DT(Cyclic<2>, CALL);                        \
+    case 3: return EQL_DT(Cyclic<3>, CALL);                        \
+    case 4: return EQL_DT(Cyclic<4>, CALL);                        \
+    case 5: return EQL_DT(Cyclic<5>, CALL);                        \
+    case 6: return EQL_DT(Cyclic<6>, CALL);                        \
+    case 7: return EQL_DT(Cyclic<7>, CALL);                        \
+    case 8: return EQL_DT(Cyclic<8>, CALL);                        \
+    case 9: return EQL_DT(Cyclic<9>, CALL);                        \
+    case 10: return EQL_DT(Cyclic<10>, CALL);                      \
+    case 11: return EQL_DT(Cyclic<11>, CALL);                      \
+    case 12: return EQL_DT(Cyclic<12>, CALL);                      \
+    case 13: return EQL_DT(Cyclic<13>, CALL);                      \
+    case 14: return EQL_DT(Cyclic<14>, CALL);                      \
+    case 15: return EQL_DT(Cyclic<15>, CALL);                      \
+    case 16: return EQL_DT(Cyclic<16>, CALL);                      \
+    default: return hipErrorInvalidValue;                          \
   }
 
 }  // namespace
@@ -734,33 +742,33 @@ size_t workspace_bytes(const eqlinear_plan* p, int64_t N) {
 }
 
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s) {
-#define EQL_CALL(T_, DT_) launch_spectra_t<T_, DT_>(p, W, bias, s)
-  EQL_CYC_DISPATCH(p->T, p->dtype, EQL_CALL)
+#define EQL_CALL(G_, DT_) launch_spectra_t<G_, DT_>(p, W, bias, s)
+  EQL_GROUP_DISPATCH(EQL_CALL)
 #undef EQL_CALL
 }
 
 hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, int act,
                           hipStream_t s) {
-#define EQL_CALL(T_, DT_)                                                                     \
-  launch_gemm_t<T_, DT_>(x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, \
+#define EQL_CALL(G_, DT_)                                                                    \
+  launch_gemm_t<G_, DT_>(x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, \
                          (int)p->D, (int)p->fwd.n_pad, act, s)
-  EQL_CYC_DISPATCH(p->T, p->dtype, EQL_CALL)
+  EQL_GROUP_DISPATCH(EQL_CALL)
 #undef EQL_CALL
 }
 
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s) {
-#define EQL_CALL(T_, DT_)                                                                       \
-  launch_gemm_t<T_, DT_>(dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad, \
+#define EQL_CALL(G_, DT_)                                                                      \
+  launch_gemm_t<G_, DT_>(dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad, \
                          (int)p->C, (int)p->adj.n_pad, ACT_NONE, s)
-  EQL_CYC_DISPATCH(p->T, p->dtype, EQL_CALL)
+  EQL_GROUP_DISPATCH(EQL_CALL)
 #undef EQL_CALL
 }
 
 hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
                                   float* dbias, int64_t N, void* ws, hipStream_t s) {
-#define EQL_CALL(T_, DT_) launch_bw_t<T_, DT_>(p, x, dy, dW, dbias, N, ws, s)
-  EQL_CYC_DISPATCH(p->T, p->dtype, EQL_CALL)
+#define EQL_CALL(G_, DT_) launch_bw_t<G_, DT_>(p, x, dy, dW, dbias, N, ws, s)
+  EQL_GROUP_DISPATCH(EQL_CALL)
 #undef EQL_CALL
 }
 

@@ -1,4 +1,5 @@
-"""Seeded synthetic workloads for the EQ-Linear layer (p4 and other cyclic groups).
+"""Seeded synthetic workloads for the EQ-Linear layer (p4, other cyclic groups,
+and p4m).
 
 This module holds the workload shapes and the seeded input generators, and
 nothing of the layer's arithmetic.  It is the one module shared by the oracle
@@ -10,8 +11,9 @@ Flash EQ-ViT / Flash EQ-Swin).  The paper's own operator shapes are not given,
 so ViT-S-like (64 images x 197 tokens, 384 features) and Swin-like
 (64 images x 56 x 56 tokens, 768 features) layers are used, with C and D
 counted per group element (a row holds C*T input and D*T output features).
-The C8 workload keeps the ViT-S-like MLP widths (384 -> 1536 features) on the
-rotation group of order 8, so C and D are half of the p4 ones.
+The C8 and p4m workloads keep the ViT-S-like MLP widths (384 -> 1536
+features) on a group of order 8 (rotations by 45 degrees; rotations by 90
+degrees and reflections), so C and D are half of the p4 ones.
 
 Drawing rule: numpy PCG64 seeded with ``seed``, draws in the order x, W, bias,
 dy, each in fp64, then cast to fp32 and, for fp16 runs, from fp32 to fp16 with
@@ -35,6 +37,7 @@ class Workload:
     bias: bool
     passes: tuple  # subset of ("forward", "backward")
     desc: str
+    group: str = "cyclic"  # "cyclic" (C_T) or "dihedral" (D_{T/2})
 
 
 WORKLOADS = {
@@ -52,6 +55,11 @@ WORKLOADS = {
                              ("forward", "backward"),
                              "ViT-S-like MLP expansion on the rotation group C8, "
                              "64 images x 197 tokens, 384->1536 features"),
+    "vit_s_mlp_p4m": Workload("vit_s_mlp_p4m", 12608, 48, 192, 8, ("f16", "f32"), True,
+                              ("forward", "backward"),
+                              "ViT-S-like MLP expansion on p4m (rotations and reflections, "
+                              "the dihedral group D4), 64 images x 197 tokens, "
+                              "384->1536 features", group="dihedral"),
 }
 
 _NP_DTYPE = {"f32": np.float32, "f16": np.float16}

@@ -1,7 +1,9 @@
 /*
  * eqlinear.h -- C ABI of libeqlinear, the equivariant linear layer
- * (EQ-Linear) of a cyclic rotation group of order T, 2 <= T <= 16, on AMD
- * MI355X (gfx950); the p4 group (T = 4) has its own specialised kernels.
+ * (EQ-Linear) of a cyclic rotation group of order T, 2 <= T <= 16, or of a
+ * dihedral group (rotations and reflections) of order T = 2n, 2 <= n <= 8,
+ * on AMD MI355X (gfx950); the p4 group (cyclic, T = 4) has its own
+ * specialised kernels.
  *
  * The operation.  Flash EQ-Linear: Accelerating Equivariant Linear Layers via
  * Group-wise Discrete Fourier Transform (gist.science technical summary,
@@ -18,6 +20,21 @@
  * real matrix products for even T and 2T - 1 for odd T;
  * "Specializzazione per il Gruppo di Rotazione p4": for T = 4 the transforms
  * are adds/subtracts and there are six real matrix products).
+ *
+ * Reflection groups.  The pages' kernels cover p4 only and name reflection
+ * groups as the next step ("Limitazioni e Lavoro Futuro").  For the
+ * dihedral group D_n (n rotations rho^r and n reflections rho^r sigma,
+ * sigma rho sigma = rho^-1; p4m is D_4) the layer is read as the group
+ * convolution of the same construction,
+ *
+ *     y[n,d,g] = sum_{c<C} sum_{h<T} W[d,c,h^-1 g] * x[n,c,h]  + bias[d]
+ *
+ * with group index g = m*n + r for rho^r sigma^m (rotations first); for the
+ * cyclic group h^-1 g = (t - s) mod T and this is the formula above.  It is
+ * computed exactly through the group Fourier transform over the real
+ * irreducible representations: one real product per one-dimensional
+ * representation and a 2 x 2 block product (eight real products) per
+ * two-dimensional one, 12 real products against 64 for p4m.
  *
  * Layouts.  Every tensor is dense, row-major, with the group index fastest:
  *     x, dx : [N][C][T]      y, dy : [N][D][T]      W, dW : [D][C][T]
@@ -57,10 +74,16 @@ typedef struct eqlinear_plan* eqlinear_plan_t; /* opaque */
 
 typedef enum { EQL_F32 = 0, EQL_F16 = 1 } eqlinear_dtype_t;
 
+/* Symmetry group of the group axis. */
+typedef enum {
+  EQL_GROUP_CYCLIC = 0,   /* C_T, T = order, 2 <= T <= 16 */
+  EQL_GROUP_DIHEDRAL = 1  /* D_n, n = number of rotations, 2 <= n <= 8, T = 2n */
+} eqlinear_group_t;
+
 typedef enum {
   EQL_OK = 0,
   EQL_ERR_INVALID_ARG = 1, /* NULL pointer, C/D <= 0, N < 0, size overflow */
-  EQL_ERR_UNSUPPORTED = 2, /* T outside [2, 16] or unknown dtype */
+  EQL_ERR_UNSUPPORTED = 2, /* group, group order or dtype without kernels */
   EQL_ERR_NO_WEIGHT = 3,   /* forward/backward before set_weight */
   EQL_ERR_MISALIGNED = 4,  /* a buffer is not 16-byte aligned */
   EQL_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
@@ -79,6 +102,18 @@ eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T,
                                        eqlinear_dtype_t dtype,
                                        eqlinear_plan_t* out);
 
+/* Create a plan for a given symmetry group: EQL_GROUP_CYCLIC with n = T (as
+ * eqlinear_plan_create), or EQL_GROUP_DIHEDRAL with n rotations, 2 <= n <= 8,
+ * whose tensors then have T = 2n group values per channel (index m*n + r of
+ * rho^r sigma^m).  The dihedral groups run the generic group kernels (their
+ * group Fourier transform is the length-n DFT of the rotation and of the
+ * reflection half of each group vector, combined into the one- and
+ * two-dimensional representations).  Other groups or orders return
+ * EQL_ERR_UNSUPPORTED.  Host-only, as eqlinear_plan_create. */
+eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_group_t group,
+                                             int64_t n, eqlinear_dtype_t dtype,
+                                             eqlinear_plan_t* out);
+
 /* Destroy a plan and free its device spectra (NULL is a no-op).  The caller
  * must ensure no call using the plan is still in flight. */
 eqlinear_status_t eqlinear_plan_destroy(eqlinear_plan_t plan);
@@ -87,8 +122,10 @@ eqlinear_status_t eqlinear_plan_destroy(eqlinear_plan_t plan);
  * bias[D] (NULL = no bias) in the plan dtype and writes the plan's spectra:
  * the length-T real DFT of every W[d,c,:], frequencies k <= T/2 only (real
  * and imaginary parts as T real planes; the others are conjugates,
- * "Approccio Algoritmico": conjugate symmetry of the real DFT) in the layouts
- * the forward and backward kernels read.  On the first call it allocates the
+ * "Approccio Algoritmico": conjugate symmetry of the real DFT), or for a
+ * dihedral plan its group Fourier transform (T real planes: the
+ * one-dimensional representations and the 2 x 2 blocks), in the layouts the
+ * forward and backward kernels read.  On the first call it allocates the
  * spectra on the current device (EQL_ERR_ALLOC on failure); later calls
  * must run on the same device. */
 eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t plan, const void* W,
@@ -124,8 +161,10 @@ eqlinear_status_t eqlinear_forward_act(eqlinear_plan_t plan, const void* x, void
                                        int64_t N, eqlinear_act_t act, void* stream);
 
 /* Backward with respect to the input ("Implementazione": forward and backward
- * passes): dx[n,c,s] = sum_{d,t} W[d,c,(t-s) mod T] * dy[n,d,t], i.e. the
- * transpose of the forward map, computed with the conjugate weight spectra.
+ * passes): dx[n,c,s] = sum_{d,t} W[d,c,(t-s) mod T] * dy[n,d,t] (dihedral:
+ * dx[n,c,h] = sum_{d,g} W[d,c,h^-1 g] * dy[n,d,g]), i.e. the transpose of
+ * the forward map, computed with the adjoint weight spectra (conjugate, or
+ * with the 2 x 2 blocks transposed).
  * dx has the plan dtype.  N = 0 is a successful no-op. */
 eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t plan, const void* dy,
                                           void* dx, int64_t N, void* stream);
@@ -137,6 +176,7 @@ size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t N);
 /* Backward with respect to the weight and bias:
  *     dW[d,c,r] = sum_{n,t} dy[n,d,t] * x[n,c,(t-r) mod T]   (binary32)
  *     dbias[d]  = sum_{n,t} dy[n,d,t]                          (binary32)
+ * (dihedral: dW[d,c,u] = sum_{n,h} dy[n,d,h u] * x[n,c,h])
  * i.e. the gradient of every replica of a shared weight summed back onto it.
  * dW and dbias (NULL = not wanted) are overwritten, not accumulated into.
  * The reduction over N runs in binary32 in a fixed order (deterministic).
@@ -157,9 +197,10 @@ const char* eqlinear_last_error(void);
 
 /* Real multiply-accumulates of one forward over N rows as computed by the
  * library ((2T - 2)*N*C*D for even T, (2T - 1)*N*C*D for odd T; 6*N*C*D for
- * p4) and of the dense unrolled product (T*T*N*C*D); for even T the ratio is
- * 2(T-1)/T^2, 3/8 at T = 4 (authors' abstract).  Either pointer may be
- * NULL. */
+ * p4; dihedral D_n: (4n - 4)*N*C*D for even n, (4n - 2)*N*C*D for odd n,
+ * 12*N*C*D for p4m) and of the dense unrolled product (T*T*N*C*D); for even
+ * cyclic T the ratio is 2(T-1)/T^2, 3/8 at T = 4 (authors' abstract).
+ * Either pointer may be NULL. */
 eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t plan, int64_t N,
                                       int64_t* spectral_macs, int64_t* dense_macs);
 

@@ -164,3 +164,66 @@ def test_workspace_grows_with_rows():
             assert sizes[0] == 0 and 0 < sizes[1] <= sizes[2] <= sizes[3]
         finally:
             eq.eqlinear_plan_destroy(p)
+
+
+def _raw_group_plan(lib, group, n, C=8, D=8, dtype=eq.EQL_F32):
+    h = ctypes.c_void_p()
+    st = lib.eqlinear_plan_create_group(C, D, group, n, dtype, ctypes.byref(h))
+    return st, h.value
+
+
+def test_plan_create_group_validation():
+    lib = _lib()
+    for n in (-1, 0, 1, 9, 16):                 # EQL_ERR_UNSUPPORTED: dihedral D_2 .. D_8
+        assert _raw_group_plan(lib, eq.EQL_GROUP_DIHEDRAL, n)[0] == 2
+    for n in (2, 3, 4, 8):
+        st, h = _raw_group_plan(lib, eq.EQL_GROUP_DIHEDRAL, n)
+        assert st == 0 and h
+        assert lib.eqlinear_plan_destroy(h) == 0
+    st, h = _raw_group_plan(lib, eq.EQL_GROUP_CYCLIC, 16)   # the cyclic group through the same call
+    assert st == 0 and h
+    assert lib.eqlinear_plan_destroy(h) == 0
+    assert _raw_group_plan(lib, eq.EQL_GROUP_CYCLIC, 17)[0] == 2
+    assert _raw_group_plan(lib, 5, 4)[0] == 2          # unknown group
+    assert _raw_group_plan(lib, eq.EQL_GROUP_DIHEDRAL, 4, dtype=3)[0] == 2
+    assert _raw_group_plan(lib, eq.EQL_GROUP_DIHEDRAL, 4, C=0)[0] == 1
+    assert lib.eqlinear_plan_create_group(8, 8, eq.EQL_GROUP_DIHEDRAL, 4, 0, None) == 1
+
+
+def test_mac_counts_dihedral():
+    # D_n's real irreducible representations: the one-dimensional ones are
+    # the sign patterns a^r b^m (a = -1 needs n even), and the rest of the
+    # group order 2n = sum of dim^2 is made of two-dimensional ones; a
+    # dim x dim block product costs dim^3 real products per (n, c, d).
+    _lib()
+    for n in range(2, 9):
+        one = 4 if n % 2 == 0 else 2
+        two = (2 * n - one) // 4
+        assert one + 4 * two == 2 * n
+        p = eq.eqlinear_plan_create_group(5, 7, eq.EQL_GROUP_DIHEDRAL, n, eq.EQL_F16)
+        try:
+            s, d = eq.eqlinear_mac_counts(p, 3)
+            assert s == (one + 8 * two) * 3 * 5 * 7 and d == 4 * n * n * 3 * 5 * 7, n
+        finally:
+            eq.eqlinear_plan_destroy(p)
+    p = eq.eqlinear_plan_create_group(96, 384, eq.EQL_GROUP_DIHEDRAL, 4, eq.EQL_F16)
+    try:
+        s, d = eq.eqlinear_mac_counts(p, 10)
+        assert s * 64 == d * 12        # p4m: 12 of 64
+    finally:
+        eq.eqlinear_plan_destroy(p)
+
+
+def test_dihedral_workspace_and_python_plan():
+    _lib()
+    p = eq.eqlinear_plan_create_group(48, 96, eq.EQL_GROUP_DIHEDRAL, 4, eq.EQL_F16)
+    try:
+        sizes = [eq.eqlinear_backward_weight_workspace(p, n) for n in (0, 1, 600, 12608)]
+        assert sizes[0] == 0 and 0 < sizes[1] <= sizes[2] <= sizes[3]
+    finally:
+        eq.eqlinear_plan_destroy(p)
+    with pytest.raises(ValueError):
+        eq.Plan(8, 8, "f16", T=7, group="dihedral")
+    pl = eq.Plan(8, 8, "f16", T=8, group="dihedral")
+    assert pl.T == 8 and pl.group == "dihedral"
+    pl.close()
