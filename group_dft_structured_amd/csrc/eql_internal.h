@@ -49,6 +49,12 @@ struct eqlinear_plan {
   void* spec_adj;     // device, plan dtype
   float* bias_f32;    // device, [fwd.n_pad], zeros where no bias
   float* zeros_f32;   // device, [adj.n_pad] zeros (bias of backward_input)
+  // p4m (D_4) in binary16 at widths the p4 producer/consumer kernels take:
+  // served by this p4 plan on paired channels (2C -> 2D, k_p4m_pairs.hip);
+  // nullptr otherwise.  pair_w holds the paired weight [2D][2C][4] and bias
+  // [2D] (plan dtype) between set_weight's two launches.
+  eqlinear_plan* inner;
+  void* pair_w;
 };
 
 namespace eql {
@@ -101,6 +107,14 @@ hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* d
                                  hipStream_t s);
 hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
                                   float* dbias, int64_t N, void* ws, hipStream_t s);
+
+// p4m on the p4 kernels (k_p4m_pairs.hip): paired weight and bias from W
+// [D][C][8], and the fold of the paired weight gradient [2D][2C][4] (+ bias
+// gradient [2D]) back into dW [D][C][8] (+ dbias [D]).
+hipError_t launch_p4m_pair_weight(const void* W, const void* bias, void* Wp, void* bp, int64_t C,
+                                  int64_t D, hipStream_t s);
+hipError_t launch_p4m_fold(const float* dWp, const float* dbp, float* dW, float* dbias, int64_t C,
+                           int64_t D, hipStream_t s);
 
 // Cyclic-group kernels (k_cyclic.hip), any group size 2 <= T <= 16.
 namespace cyc {

@@ -42,6 +42,32 @@ eqlinear_status_t check_device(const eqlinear_plan* p) {
   return EQL_OK;
 }
 
+// p4m in binary16 runs on the p4 producer/consumer kernels with paired
+// channels (2C -> 2D) when they take that width: twice the matrix products of
+// the group Fourier transform, on kernels that are bound by HBM bytes, not
+// by the matrix cores, at these widths (measured on MI355X at C = 48,
+// D = 192: forward 20.9 us on the generic kernels against the p4 kernel's
+// 11.7 us at the paired width).  EQL_P4M_PAIRS=0 selects the generic
+// kernels.
+bool use_p4m_pairs(eqlinear_group_t group, int64_t n, eqlinear_dtype_t dtype, int64_t C,
+                   int64_t D) {
+  if (group != EQL_GROUP_DIHEDRAL || n != 4 || dtype != EQL_F16) return false;
+  const char* env = getenv("EQL_P4M_PAIRS");
+  if (env != nullptr && atoi(env) == 0) return false;
+  const int64_t k = 2 * C;  // reduction width of the paired forward
+  const bool ws_width = k % 32 == 0 && (k <= 192 || k == 256 || k == 384);
+  return ws_width && (2 * D) % 4 == 0 && 2 * C <= MAX_CHANNELS && 2 * D <= MAX_CHANNELS;
+}
+
+// Workspace of a paired plan: the p4 plan's, then the paired weight gradient
+// [2D][2C][4] and bias gradient [2D] (fp32), each 256-byte aligned.
+size_t pair_ws_inner(const eqlinear_plan* p, int64_t N) {
+  return eql::round_up((int64_t)eqlinear_backward_weight_workspace(p->inner, N), 256);
+}
+size_t pair_ws_dw(const eqlinear_plan* p) {
+  return eql::round_up(16 * p->C * p->D * (int64_t)sizeof(float), 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,6 +135,16 @@ eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_grou
   p->fwd.k_pad = eql::round_up(C, eql::KPAD);
   p->adj.n_pad = eql::round_up(C, eql::NPAD);
   p->adj.k_pad = eql::round_up(D, eql::KPAD);
+  p->inner = nullptr;
+  p->pair_w = nullptr;
+  if (use_p4m_pairs(group, n, dtype, C, D)) {
+    eqlinear_status_t st = eqlinear_plan_create_group(2 * C, 2 * D, EQL_GROUP_CYCLIC, 4, dtype,
+                                                      &p->inner);
+    if (st != EQL_OK) {
+      delete p;
+      return st;
+    }
+  }
   *out = p;
   return EQL_OK;
 }
@@ -116,6 +152,14 @@ eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_grou
 eqlinear_status_t eqlinear_plan_destroy(eqlinear_plan_t p) {
   if (p == nullptr) return EQL_OK;
   eqlinear_status_t st = EQL_OK;
+  if (p->inner != nullptr) st = eqlinear_plan_destroy(p->inner);
+  if (p->pair_w != nullptr) {
+    hipError_t e = hipFree(p->pair_w);
+    if (e != hipSuccess) {
+      set_error("hipFree", e);
+      st = EQL_ERR_HIP;
+    }
+  }
   if (p->spec_fwd != nullptr) {
     int prev = -1;
     hipGetDevice(&prev);
@@ -137,6 +181,31 @@ eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t p, const void* W, const vo
   if (!aligned16(W) || !aligned16(bias)) return EQL_ERR_MISALIGNED;
   eqlinear_status_t st = check_device(p);
   if (st != EQL_OK) return st;
+  if (p->inner != nullptr) {
+    // paired weight and bias, then the p4 plan's spectra of them
+    const size_t wbytes = eql::round_up(16 * p->C * p->D * (int64_t)p->esize, 256);
+    if (p->pair_w == nullptr) {
+      hipError_t e = hipMalloc(&p->pair_w, wbytes + 2 * p->D * p->esize);
+      if (e != hipSuccess) {
+        p->pair_w = nullptr;
+        set_error("hipMalloc(paired weight)", e);
+        return EQL_ERR_ALLOC;
+      }
+      int dev = -1;
+      hipGetDevice(&dev);
+      p->device = dev;
+    }
+    void* bp = (char*)p->pair_w + wbytes;
+    hipError_t e = eql::launch_p4m_pair_weight(W, bias, p->pair_w, bp, p->C, p->D,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) {
+      set_error("paired weight launch", e);
+      return EQL_ERR_HIP;
+    }
+    st = eqlinear_set_weight(p->inner, p->pair_w, bias != nullptr ? bp : nullptr, stream);
+    if (st == EQL_OK) p->has_weight = true;
+    return st;
+  }
   if (p->spec_fwd == nullptr) {
     const size_t fwd_bytes = (size_t)p->T * p->fwd.plane_elems() * p->esize;
     const size_t adj_bytes = (size_t)p->T * p->adj.plane_elems() * p->esize;
@@ -188,6 +257,7 @@ eqlinear_status_t eqlinear_forward_act(eqlinear_plan_t p, const void* x, void* y
     return EQL_ERR_INVALID_ARG;
   eqlinear_status_t st = check_gemm_args(p, x, y, N);
   if (st != EQL_OK || N == 0) return st;
+  if (p->inner != nullptr) return eqlinear_forward_act(p->inner, x, y, N, act, stream);
   st = check_device(p);
   if (st != EQL_OK) return st;
   hipError_t e = eql::launch_forward(p, x, y, N, (int)act, (hipStream_t)stream);
@@ -202,6 +272,7 @@ eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t p, const void* dy, voi
                                           void* stream) {
   eqlinear_status_t st = check_gemm_args(p, dy, dx, N);
   if (st != EQL_OK || N == 0) return st;
+  if (p->inner != nullptr) return eqlinear_backward_input(p->inner, dy, dx, N, stream);
   st = check_device(p);
   if (st != EQL_OK) return st;
   hipError_t e = eql::launch_backward_input(p, dy, dx, N, (hipStream_t)stream);
@@ -214,6 +285,8 @@ eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t p, const void* dy, voi
 
 size_t eqlinear_backward_weight_workspace(eqlinear_plan_t p, int64_t N) {
   if (p == nullptr || N < 0 || N > MAX_ROWS) return 0;
+  if (p->inner != nullptr)
+    return N == 0 ? 0 : pair_ws_inner(p, N) + pair_ws_dw(p) + 2 * p->D * sizeof(float);
   return eql::bwd_weight_workspace_bytes(p, N);
 }
 
@@ -226,10 +299,26 @@ eqlinear_status_t eqlinear_backward_weight(eqlinear_plan_t p, const void* x, con
   if (!aligned16(x) || !aligned16(dy) || !aligned16(dW) || !aligned16(dbias) ||
       !aligned16(workspace))
     return EQL_ERR_MISALIGNED;
-  const size_t need = eql::bwd_weight_workspace_bytes(p, N);
+  const size_t need = eqlinear_backward_weight_workspace(p, N);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return EQL_ERR_WORKSPACE;
   eqlinear_status_t st = check_device(p);
   if (st != EQL_OK) return st;
+  if (p->inner != nullptr && N > 0) {
+    // the p4 plan's weight gradient of the paired layer, then the fold
+    // (N = 0 takes the common path below, which writes zeros)
+    const size_t inner_bytes = pair_ws_inner(p, N);
+    float* dWp = (float*)((char*)workspace + inner_bytes);
+    float* dbp = (float*)((char*)dWp + pair_ws_dw(p));
+    st = eqlinear_backward_weight(p->inner, x, dy, dWp, dbias != nullptr ? dbp : nullptr, N,
+                                  workspace, inner_bytes, stream);
+    if (st != EQL_OK) return st;
+    hipError_t e = eql::launch_p4m_fold(dWp, dbp, dW, dbias, p->C, p->D, (hipStream_t)stream);
+    if (e != hipSuccess) {
+      set_error("weight-gradient fold launch", e);
+      return EQL_ERR_HIP;
+    }
+    return EQL_OK;
+  }
   hipError_t e = eql::launch_backward_weight(p, x, dy, dW, dbias, N, workspace, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("backward_weight launch", e);
@@ -251,6 +340,8 @@ eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t p, int64_t N, int64_t* spe
   if (p->group == EQL_GROUP_DIHEDRAL) {
     const int64_t n = T / 2;
     products = (n % 2 == 0 ? 4 : 2) + 8 * ((n - 1) / 2);
+    // p4m on the p4 kernels: six products per paired channel pair, 24 per (c, d)
+    if (p->inner != nullptr) products = 24;
   }
   const int64_t ncd = N * p->C * p->D;
   if (spectral_macs) *spectral_macs = products * ncd;

@@ -108,8 +108,17 @@ eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T,
  * rho^r sigma^m).  The dihedral groups run the generic group kernels (their
  * group Fourier transform is the length-n DFT of the rotation and of the
  * reflection half of each group vector, combined into the one- and
- * two-dimensional representations).  Other groups or orders return
- * EQL_ERR_UNSUPPORTED.  Host-only, as eqlinear_plan_create. */
+ * two-dimensional representations).  One exception: p4m (n = 4) in EQL_F16
+ * at widths the p4 producer/consumer kernels take (2C a multiple of 32 up
+ * to 192, or 256 or 384) runs as the p4 layer on paired channels: a p4m
+ * tensor [N][C][8] is the p4 tensor [N][2C][4] with channel 2c + m holding
+ * coset m, and the layer is a p4 layer with a rearranged weight.  That
+ * path spends 24 real products per (n, c, d) instead of 12, on kernels
+ * bound by HBM bytes rather than by the matrix cores at these widths; the
+ * environment variable EQL_P4M_PAIRS=0, read at plan creation, selects the
+ * generic kernels instead.  Other groups or orders return
+ * EQL_ERR_UNSUPPORTED.  Host-only, as eqlinear_plan_create (a p4m plan on
+ * paired channels also creates its inner p4 plan). */
 eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_group_t group,
                                              int64_t n, eqlinear_dtype_t dtype,
                                              eqlinear_plan_t* out);
@@ -198,7 +207,8 @@ const char* eqlinear_last_error(void);
 /* Real multiply-accumulates of one forward over N rows as computed by the
  * library ((2T - 2)*N*C*D for even T, (2T - 1)*N*C*D for odd T; 6*N*C*D for
  * p4; dihedral D_n: (4n - 4)*N*C*D for even n, (4n - 2)*N*C*D for odd n,
- * 12*N*C*D for p4m) and of the dense unrolled product (T*T*N*C*D); for even
+ * 12*N*C*D for p4m, 24*N*C*D for p4m on paired channels) and of the dense
+ * unrolled product (T*T*N*C*D); for even
  * cyclic T the ratio is 2(T-1)/T^2, 3/8 at T = 4 (authors' abstract).
  * Either pointer may be NULL. */
 eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t plan, int64_t N,

@@ -206,10 +206,32 @@ def test_mac_counts_dihedral():
             assert s == (one + 8 * two) * 3 * 5 * 7 and d == 4 * n * n * 3 * 5 * 7, n
         finally:
             eq.eqlinear_plan_destroy(p)
-    p = eq.eqlinear_plan_create_group(96, 384, eq.EQL_GROUP_DIHEDRAL, 4, eq.EQL_F16)
+    p = eq.eqlinear_plan_create_group(96, 384, eq.EQL_GROUP_DIHEDRAL, 4, eq.EQL_F32)
     try:
         s, d = eq.eqlinear_mac_counts(p, 10)
-        assert s * 64 == d * 12        # p4m: 12 of 64
+        assert s * 64 == d * 12        # p4m through the group Fourier transform: 12 of 64
+    finally:
+        eq.eqlinear_plan_destroy(p)
+
+
+def test_p4m_pairs_dispatch(monkeypatch):
+    # binary16 p4m at widths the p4 producer/consumer kernels take runs as p4
+    # on paired channels (2C -> 2D): 6 products per paired channel pair,
+    # 24 per (c, d); EQL_P4M_PAIRS=0 keeps the group Fourier transform (12)
+    _lib()
+    for C, paired in ((48, True), (96, True), (16, True), (192, True), (40, False), (5, False), (160, False)):
+        p = eq.eqlinear_plan_create_group(C, 64, eq.EQL_GROUP_DIHEDRAL, 4, eq.EQL_F16)
+        try:
+            s, d = eq.eqlinear_mac_counts(p, 1)
+            assert s == (24 if paired else 12) * C * 64 and d == 64 * C * 64, C
+            assert eq.eqlinear_backward_weight_workspace(p, 0) == 0
+            assert eq.eqlinear_backward_weight_workspace(p, 1000) > 0
+        finally:
+            eq.eqlinear_plan_destroy(p)
+    monkeypatch.setenv("EQL_P4M_PAIRS", "0")
+    p = eq.eqlinear_plan_create_group(48, 64, eq.EQL_GROUP_DIHEDRAL, 4, eq.EQL_F16)
+    try:
+        assert eq.eqlinear_mac_counts(p, 1)[0] == 12 * 48 * 64
     finally:
         eq.eqlinear_plan_destroy(p)
 

@@ -161,3 +161,37 @@ def test_dihedral_zero_rows_and_determinism():
     for a, b in zip(*outs):
         assert torch.equal(a, b)
     plan.close()
+
+
+# p4m in binary16 at widths the p4 producer/consumer kernels take runs as the
+# p4 layer on paired channels (2C -> 2D); the same shapes with
+# EQL_P4M_PAIRS=0 run the group Fourier transform.  Both against the oracle,
+# and against each other.
+@pytest.mark.parametrize("C,D,N", [(16, 32, 517), (48, 192, 1000), (96, 64, 301), (48, 192, 12608)])
+def test_p4m_paired_path(C, D, N, monkeypatch):
+    torch = torch_mod()
+    inp = make_inputs(C, D, N, 8, dtype="f16", seed=41, bias=True, dy=True)
+    outs = {}
+    for pairs in ("1", "0"):
+        monkeypatch.setenv("EQL_P4M_PAIRS", pairs)
+        plan = Plan(C, D, "f16", T=8, group=DIH)
+        assert plan.mac_counts(1)[0] == (24 if pairs == "1" else 12) * C * D
+        plan.set_weight(to_dev(inp["W"]), to_dev(inp["bias"]))
+        x, dy = to_dev(inp["x"]), to_dev(inp["dy"])
+        y = plan.forward(x)
+        yg = plan.forward(x, act="gelu")
+        dx = plan.backward_input(dy)
+        dW, db = plan.backward_weight(x, dy)
+        dW2, _ = plan.backward_weight(x, dy, want_bias=False)
+        _sync()
+        outs[pairs] = [to_np64(t) for t in (y, yg, dx, dW, db)]
+        assert torch.equal(dW, dW2)
+        plan.close()
+    refs = [oracle.forward(inp["x"], inp["W"], inp["bias"], group=DIH),
+            oracle.forward_act(inp["x"], inp["W"], inp["bias"], "gelu", group=DIH),
+            oracle.backward_input(inp["dy"], inp["W"], group=DIH),
+            *oracle.backward_weight(inp["x"], inp["dy"], group=DIH)]
+    for name, a, b, ref in zip(("y", "gelu", "dx", "dW", "dbias"), outs["1"], outs["0"], refs):
+        ea, eb = rel_err(a, ref), rel_err(b, ref)
+        print(f"p4m paired C={C} D={D} N={N} {name}: paired {ea:.2e} generic {eb:.2e}", flush=True)
+        assert ea <= TOL["f16"] and eb <= TOL["f16"], (name, ea, eb)
