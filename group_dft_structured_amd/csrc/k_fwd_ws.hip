@@ -25,6 +25,8 @@
 // so memory back-pressure never stalls the matrix cores.  Work-groups that
 // read the same x tiles (different channel ranges) sit on the same XCD and
 // share its L2.
+#include <type_traits>
+
 #include "eql_device.h"
 #include "eql_internal.h"
 
@@ -79,7 +81,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
 // channels 32s + 8g .. 32s + 8g + 7.
 template <int NC, int NP, int NB, int KS, int YP, bool G8, bool STAGGER, bool PST, bool PIPE,
-          bool ACT = false>
+          bool SPLIT, bool ACT = false>
 __device__ __forceinline__ void ws_body(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
@@ -117,6 +119,38 @@ __device__ __forceinline__ void ws_body(
   const int n_rt = (N + 15) / 16;
   const int n_my = q < n_rt ? (n_rt - 1 - q) / Q + 1 : 0;  // tiles of this worker
   if (n_my == 0) return;  // whole work-group
+
+  // PST: write rows [ROW0, ROW0 + NROWS) of this worker's staged output tile
+  // t (16 rows x BN channels, one 16-byte chunk = 2 channels x 4 group values
+  // per lane, whole rows per wave instruction) from staging buffer t % 2,
+  // spread over the TPR threads of one role (rt = thread index in the role).
+  // SPLIT: the producers write rows 0-7 and the consumers rows 8-15.
+  static_assert(!(SPLIT && (PIPE || !PST)), "split stores need producer-side staging, no lag");
+  auto store_rows = [&](auto row0_c, auto nrows_c, auto tpr_c, int t, int rt) {
+    constexpr int ROW0 = decltype(row0_c)::value, NROWS = decltype(nrows_c)::value;
+    constexpr int TPR = decltype(tpr_c)::value;
+    const int64_t r0 = (int64_t)(q + (int64_t)t * Q) * 16;
+    const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+    const __amdgpu_buffer_rsrc_t ry = rsrc(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 8));
+    const _Float16* const sb = obuf + (t & 1) * OBUF;
+    constexpr int LPR = BN / 2;                 // chunks per row
+    constexpr int CH = NROWS * LPR;             // chunks to write
+    constexpr int SPT = (CH + TPR - 1) / TPR;   // chunks per thread
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int u0 = k * TPR + rt;
+      const bool real = CH % TPR == 0 || u0 < CH;
+      const int u = real ? u0 : 0;
+      const int row = ROW0 + u / LPR, ch = u % LPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * OPITCH + 8 * ch);
+      const int col = j * BN + 2 * ch;
+      const uint32_t off = (real && col < n_out) ? (uint32_t)((row * n_out + col) * 8) : 0x7FFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, YP);
+    }
+  };
+  typedef std::integral_constant<int, 0> c0_t;
+  typedef std::integral_constant<int, 8> c8_t;
+  typedef std::integral_constant<int, SPLIT ? 8 : 16> cprod_rows_t;
 
   if (wave >= NC) {
     // =========================== producer waves ===========================
@@ -217,28 +251,9 @@ __device__ __forceinline__ void ws_body(
         }
       }
     };
-    // PST: write the staged output of this worker's tile t (16 rows x BN
-    // channels, one 16-byte chunk = 2 channels x 4 group values per lane,
-    // whole rows per wave instruction) from staging buffer t % 2
+    // PST: the producers' rows of staged output tile t
     auto store_out = [&](int t) {
-      const int64_t r0 = (int64_t)(q + (int64_t)t * Q) * 16;
-      const int64_t rows = N - r0 < 16 ? N - r0 : 16;
-      const __amdgpu_buffer_rsrc_t ry = rsrc(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 8));
-      const _Float16* const sb = obuf + (t & 1) * OBUF;
-      constexpr int LPR = BN / 2;                // chunks per row
-      constexpr int CH = 16 * LPR;               // chunks per tile
-      constexpr int SPT = (CH + PT - 1) / PT;    // chunks per producer thread
-#pragma unroll
-      for (int k = 0; k < SPT; ++k) {
-        const int u0 = k * PT + ptid;
-        const bool real = CH % PT == 0 || u0 < CH;
-        const int u = real ? u0 : 0;
-        const int row = u / LPR, ch = u % LPR;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * OPITCH + 8 * ch);
-        const int col = j * BN + 2 * ch;
-        const uint32_t off = (real && col < n_out) ? (uint32_t)((row * n_out + col) * 8) : 0x7FFFFFF0u;
-        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, YP);
-      }
+      store_rows(c0_t{}, cprod_rows_t{}, std::integral_constant<int, PT>{}, t, ptid);
     };
     // phase p (between barriers p and p + 1) first writes out the tile the
     // consumers staged in phase p - 1: tile p - 1, or p - 2 when their
@@ -441,14 +456,20 @@ __device__ __forceinline__ void ws_body(
     } else {
       int cur = 0;
       Acc A;
+      typedef std::integral_constant<int, NC * 64> ctpr_t;
       for (int i = 0; i < n_my; ++i) {
         products(A, xs + cur * BUF);
         epilogue(i, A);
+        // SPLIT: the consumers' rows of the tile staged in the previous
+        // phase, after this tile's products (the wait at the barrier would
+        // otherwise be idle)
+        if (SPLIT && i >= 1) store_rows(c8_t{}, c8_t{}, ctpr_t{}, i - 1, tid);
         cur ^= 1;
         // barrier i+1 (with PST also after the last tile: its staged output
         // is then complete for the producers)
         if (PST || i + 1 < n_my) __syncthreads();
       }
+      if (SPLIT) store_rows(c8_t{}, c8_t{}, ctpr_t{}, n_my - 1, tid);
     }
   }
 }
@@ -458,20 +479,21 @@ __device__ __forceinline__ void ws_body(
 // (conjugate-transposed spectra, zero bias).  PST selects the output path:
 // the producers write whole rows staged through LDS (the default), or the
 // consumers store their fragments directly.
-template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE, bool ACT = false>
+template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE, bool SPLIT,
+          bool ACT = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
-  ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE, ACT>(x, spec, bias, y, N, K, n_out, n_pad, n_ct, Qx,
-                                                        act);
+  ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE, SPLIT, ACT>(x, spec, bias, y, N, K, n_out, n_pad,
+                                                               n_ct, Qx, act);
 }
 
-template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE>
+template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE, bool SPLIT>
 __global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
     const _Float16* __restrict__ dy, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
-  ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct, Qx,
-                                                   ACT_NONE);
+  ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE, SPLIT>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct,
+                                                          Qx, ACT_NONE);
 }
 
 // ---------------------------------------------------------------------------
@@ -505,22 +527,22 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   // tile)
   const bool g8 = env_int("EQL_WS_G8", KS > 6 ? 1 : 0) != 0;
   const dim3 grid(blocks), block((NC + NP) * 64);
-#define EQL_WS_LAUNCH3(YP_, G8_, PST_, PIPE_)                                                       \
+#define EQL_WS_LAUNCH4(YP_, G8_, PST_, SPLIT_)                                                      \
   do {                                                                                              \
     if (adjoint)                                                                                    \
-      hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, PIPE_>), grid, block, 0, s, \
-                         (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
-                         n_pad, n_ct, qx);                                                          \
+      hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, false, SPLIT_>), grid, block, 0, \
+                         s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K,   \
+                         n_out, n_pad, n_ct, qx);                                                   \
     else if (act != ACT_NONE)                                                                       \
-      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, PIPE_, true>), grid, block, 0, s, \
-                         (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
-                         n_pad, n_ct, qx, act);                                                     \
+      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, false, SPLIT_, true>), grid, block, \
+                         0, s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, \
+                         n_out, n_pad, n_ct, qx, act);                                              \
     else                                                                                            \
-      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, PIPE_>), grid, block, 0, s,    \
-                         (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out, \
-                         n_pad, n_ct, qx, act);                                                     \
+      hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, false, SPLIT_>), grid, block, 0, \
+                         s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K,   \
+                         n_out, n_pad, n_ct, qx, act);                                              \
   } while (0)
-#define EQL_WS_LAUNCH(YP_, G8_, PST_) EQL_WS_LAUNCH3(YP_, G8_, PST_, false)
+#define EQL_WS_LAUNCH(YP_, G8_, PST_) EQL_WS_LAUNCH4(YP_, G8_, PST_, false)
   // A fused activation with an output inside the memory-side cache runs the
   // consumers' epilogue overlapped with the next tile's products (software
   // pipeline, two accumulator sets; measured on MI355X at C=96, D=384 with
@@ -530,9 +552,9 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   const bool pipe = act != ACT_NONE && !adjoint && small && env_int("EQL_WS_PIPE", 1) != 0;
   if (pipe) {
 #define EQL_WS_PIPE_ACT(G8_)                                                                          \
-  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_THROUGH, G8_, true, true, true>), grid, block, 0, \
-                     s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out,   \
-                     n_pad, n_ct, qx, act)
+  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_THROUGH, G8_, true, true, false, true>), grid, \
+                     block, 0, s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, \
+                     n_out, n_pad, n_ct, qx, act)
     if (g8) EQL_WS_PIPE_ACT(true);
     else EQL_WS_PIPE_ACT(false);
 #undef EQL_WS_PIPE_ACT
@@ -541,17 +563,26 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   // output mode: 0 producer stores (written through small outputs,
   // streamed large ones); 1 consumer stores, streaming
   const int mode = env_int("EQL_WS_OUT", 0);
+  // Outputs beyond the memory-side cache: the stores of each tile split
+  // between producers (rows 0-7) and consumers (rows 8-15).  There the
+  // producers set the pace and the consumers wait at the barrier (measured
+  // at C=192, D=768: consumers wait 31% of their time, producers 12%);
+  // measured 518 -> 499 us.
+  const bool split = !small && env_int("EQL_WS_SPLIT", 1) != 0;
   if (mode == 1) {
     if (g8) EQL_WS_LAUNCH(POLICY_STREAM, true, false);
     else EQL_WS_LAUNCH(POLICY_STREAM, false, false);
   } else if (small) {
     if (g8) EQL_WS_LAUNCH(POLICY_THROUGH, true, true);
     else EQL_WS_LAUNCH(POLICY_THROUGH, false, true);
+  } else if (split) {
+    if (g8) EQL_WS_LAUNCH4(POLICY_STREAM, true, true, true);
+    else EQL_WS_LAUNCH4(POLICY_STREAM, false, true, true);
   } else {
     if (g8) EQL_WS_LAUNCH(POLICY_STREAM, true, true);
     else EQL_WS_LAUNCH(POLICY_STREAM, false, true);
   }
-#undef EQL_WS_LAUNCH3
+#undef EQL_WS_LAUNCH4
 #undef EQL_WS_LAUNCH
   return hipGetLastError();
 }
