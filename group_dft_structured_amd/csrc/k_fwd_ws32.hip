@@ -15,7 +15,8 @@
 //    four planes to LDS in matrix-core fragment order (double buffered);
 //  * NC consumer waves keep the weight spectra of 16 output channels in
 //    VGPRs, run the products from LDS and store 64 contiguous bytes per lane
-//    (four output channels of one row).
+//    (four output channels of one row), or leave the tile in LDS for the
+//    producers to store (PST, below).
 // The reduction index is permuted identically for both operands so that a
 // lane's four consecutive k-steps read 16 contiguous bytes: within a block
 // of 16 channels, lane group g at k-step e handles channel 4g + e.  Its
@@ -57,7 +58,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc32(const void* base, uint3
 // LDS per buffer: plane p, channel block j (16 channels): 1 KB at
 // (p*KB + j)*256 floats; lane (i16, g) reads the 16 bytes at (g*16 + i16)*4
 // floats = row i16, channels 16j + 4g .. 16j + 4g + 3.
-template <int NC, int NP, int KB, int YP, bool ACT = false>
+//
+// PST: the consumers leave each output tile in LDS (rows of BN channels x 16
+// bytes, a 16-byte pad per row so that 8 consecutive lanes' 16-byte writes
+// of 8 rows land on distinct banks; double buffered) and the producers write
+// it out as whole rows during the next tile, so the consumers' matrix-core
+// stream never waits on a store.
+template <int NC, int NP, int KB, int YP, bool ACT = false, bool PST = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     const float* __restrict__ x, const float* __restrict__ spec, const float* __restrict__ bias,
     float* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
@@ -71,7 +78,10 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
   constexpr int UPT = (UNITS + PT - 1) / PT;  // per producer thread
   constexpr int LPT = 4 * UPT;                // 16-byte loads per producer thread
   constexpr int DUMMY = (UNITS % PT != 0) ? 4 * PT : 0;  // floats
-  __shared__ __attribute__((aligned(16))) float xs[2 * BUF + DUMMY];
+  constexpr int OPITCH = BN * 4 + 4;  // floats per staged output row
+  constexpr int OBUF = 16 * OPITCH;   // floats per staged output tile
+  __shared__ __attribute__((aligned(16))) float xs[2 * BUF + DUMMY + (PST ? 2 * OBUF : 0)];
+  float* const obuf = xs + 2 * BUF + DUMMY;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -129,12 +139,35 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
         *reinterpret_cast<f32x4*>(real ? dst + 3 * PS : dummy) = pi;
       }
     };
+    // PST: write staged output tile t (16 rows x BN channels, 16 bytes = one
+    // channel's four group values per lane, whole rows per wave instruction)
+    auto store_out = [&](int t) {
+      const int64_t r0 = (int64_t)(q + (int64_t)t * Q) * 16;
+      const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+      const __amdgpu_buffer_rsrc_t ry = rsrc32(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 16));
+      const float* const sb = obuf + (t & 1) * OBUF;
+      constexpr int CH = 16 * BN;              // 16-byte chunks per tile
+      constexpr int SPT = (CH + PT - 1) / PT;  // per producer thread
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) {
+        const int u0 = k * PT + ptid;
+        const bool real = CH % PT == 0 || u0 < CH;
+        const int u = real ? u0 : 0;
+        const int row = u / BN, ch = u % BN;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * OPITCH + 4 * ch);
+        const int col = j * BN + ch;
+        const uint32_t off = (real && col < n_out) ? (uint32_t)((row * n_out + col) * 16) : 0x7FFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, YP);
+      }
+    };
+    // phase p first writes out the tile the consumers staged in phase p - 1
+    auto out_step = [&](int p) {
+      if (PST && p >= 1) store_out(p - 1);
+    };
     // Ring: tile i sits in slot i % 3 from its load until its transform;
     // between barriers i and i+1 the producers transform tile i+1 and load
-    // tile i+4 into the slot it frees.  Only loads are in flight here, so
-    // the wait before each transform leaves exactly the two younger tiles
-    // outstanding.  Tiles past the end load as zeros.  Every work-group's
-    // first tile is requested before any later one.
+    // tile i+4 into the slot it frees.  Tiles past the end load as zeros.
+    // Every work-group's first tile is requested before any later one.
     f32x4 ra[LPT], rb[LPT], rc[LPT];
     load_tile(ra, 0);
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): expcnt, lgkmcnt not waited
@@ -147,18 +180,21 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     int cur = 1;
     int i = 0;
     for (; i + 3 <= n_my - 1; i += 3) {
+      out_step(i);
       store_tile(rb, xs + cur * BUF);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(rb, i + 4);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       cur ^= 1;
+      out_step(i + 1);
       store_tile(rc, xs + cur * BUF);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(rc, i + 5);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       cur ^= 1;
+      out_step(i + 2);
       store_tile(ra, xs + cur * BUF);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(ra, i + 6);
@@ -168,13 +204,20 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     }
     const int rest = n_my - 1 - i;  // 0, 1 or 2 transforms left
     if (rest > 0) {
+      out_step(i);
       store_tile(rb, xs + cur * BUF);
       __syncthreads();
       cur ^= 1;
       if (rest > 1) {
+        out_step(i + 1);
         store_tile(rc, xs + cur * BUF);
         __syncthreads();
       }
+    }
+    if (PST) {
+      out_step(n_my - 1);
+      __syncthreads();  // barrier n_my: the last tile is staged
+      store_out(n_my - 1);
     }
   } else {
     // =========================== consumer waves ===========================
@@ -203,11 +246,11 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
       for (int r = 0; r < 4; ++r)
         bc[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (d0 + 4 * g + r) * 4, 0, 0));
     }
-    auto compute_tile = [&](int i, const float* buf) {
-      const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
-      const int64_t rows = N - r0 < 16 ? N - r0 : 16;
-      const __amdgpu_buffer_rsrc_t ry = rsrc32(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 16));
-      f32x4 c0 = {}, c2 = {}, cr = {}, ci = {};
+    struct Acc {
+      f32x4 c0, c2, cr, ci;
+    };
+    auto products = [&](Acc& a, const float* buf) {
+      a.c0 = a.c2 = a.cr = a.ci = f32x4{};
 #pragma unroll
       for (int jb = 0; jb < KB; ++jb) {
         const float* f = buf + jb * FRAG + lane * 4;
@@ -218,33 +261,47 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
         const f32x4 xq = -xi;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          c0 = mma4(w0[jb][e], x0[e], c0);
-          cr = mma4(wr[jb][e], xr[e], cr);
-          c2 = mma4(w2[jb][e], x2[e], c2);
-          ci = mma4(wi[jb][e], xr[e], ci);
-          cr = mma4(wi[jb][e], xq[e], cr);
-          ci = mma4(wr[jb][e], xi[e], ci);
+          a.c0 = mma4(w0[jb][e], x0[e], a.c0);
+          a.cr = mma4(wr[jb][e], xr[e], a.cr);
+          a.c2 = mma4(w2[jb][e], x2[e], a.c2);
+          a.ci = mma4(wi[jb][e], xr[e], a.ci);
+          a.cr = mma4(wi[jb][e], xq[e], a.cr);
+          a.ci = mma4(wr[jb][e], xi[e], a.ci);
         }
       }
-      // lane holds channels d0 + 4g + r of row r0 + i16: 64 contiguous bytes
+    };
+    // lane holds channels d0 + 4g + r of row r0 + i16: 64 contiguous bytes
+    auto epilogue = [&](int i, const Acc& a) {
+      const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
+      const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+      const __amdgpu_buffer_rsrc_t ry = rsrc32(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 16));
       const int col = d0 + 4 * g;
       const uint32_t off = col < n_out ? (uint32_t)((i16 * n_out + col) * 16) : 0x7FFFFFF0u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        f32x4 v = epi4_32(c0[r], c2[r], cr[r], ci[r], bc[r]);
+        f32x4 v = epi4_32(a.c0[r], a.c2[r], a.cr[r], a.ci[r], bc[r]);
         if constexpr (ACT) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) v[t] = activate(v[t], act);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry, off + 16 * r, 0, YP);
+        if (PST) {
+          // row i16, work-group channel wave*16 + 4g + r
+          *reinterpret_cast<f32x4*>(obuf + (i & 1) * OBUF + i16 * OPITCH + (wave * 16 + 4 * g + r) * 4) = v;
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry, off + 16 * r, 0, YP);
+        }
       }
     };
     __syncthreads();  // barrier 0
     int cur = 0;
+    Acc A;
     for (int i = 0; i < n_my; ++i) {
-      compute_tile(i, xs + cur * BUF);
+      products(A, xs + cur * BUF);
+      epilogue(i, A);
       cur ^= 1;
-      if (i + 1 < n_my) __syncthreads();  // barrier i+1
+      // barrier i+1 (with PST also after the last tile: its staged output is
+      // then complete for the producers)
+      if (PST || i + 1 < n_my) __syncthreads();
     }
   }
 }
@@ -269,20 +326,27 @@ static hipError_t launch_ws32_t(const void* x, const void* spec, const float* bi
   const unsigned blocks = (unsigned)(8 * n_ct * qx);
   const int64_t y_bytes = N * (int64_t)n_out * 16;
   const bool stream = env_int("EQL_WS32_STREAM", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
-  if (act != ACT_NONE && stream)  // fused activation
-    hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 2, true>), dim3(blocks), dim3((NC + NP) * 64), 0, s,
-                       (const float*)x, (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad,
-                       n_ct, qx, act);
-  else if (act != ACT_NONE)
-    hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 0, true>), dim3(blocks), dim3((NC + NP) * 64), 0, s,
-                       (const float*)x, (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad,
-                       n_ct, qx, act);
-  else if (stream)
-    hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 2>), dim3(blocks), dim3((NC + NP) * 64), 0, s, (const float*)x,
-                       (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx, act);
-  else
-    hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, 0>), dim3(blocks), dim3((NC + NP) * 64), 0, s, (const float*)x,
-                       (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx, act);
+  // Output path (measured on MI355X): outputs inside the memory-side cache
+  // are stored by the producers from LDS (C=96, D=96, N=12608: 26.1 us
+  // against 30.4 with the consumers storing; 30.8 against 36.0 with GELU);
+  // larger ones by the consumers (C=192, D=768: producer stores measured
+  // 4038 us against 3690).
+  const bool pst = env_int("EQL_WS32_PST", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
+  const dim3 grid(blocks), block((NC + NP) * 64);
+#define EQL_WS32_LAUNCH(YP_, ACT_, PST_)                                                              \
+  hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, YP_, ACT_, PST_>), grid, block, 0, s, (const float*)x,  \
+                     (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx, act)
+#define EQL_WS32_MODES(YP_, ACT_)                      \
+  do {                                                 \
+    if (pst) EQL_WS32_LAUNCH(YP_, ACT_, true);         \
+    else EQL_WS32_LAUNCH(YP_, ACT_, false);            \
+  } while (0)
+  if (act != ACT_NONE && stream) EQL_WS32_MODES(2, true);
+  else if (act != ACT_NONE) EQL_WS32_MODES(0, true);
+  else if (stream) EQL_WS32_MODES(2, false);
+  else EQL_WS32_MODES(0, false);
+#undef EQL_WS32_MODES
+#undef EQL_WS32_LAUNCH
   return hipGetLastError();
 }
 
