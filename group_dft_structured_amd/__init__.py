@@ -1,11 +1,12 @@
 """Python binding of libeqlinear, the EQ-Linear layer of the cyclic rotation
-groups (p4 and C_2 .. C_16) and of the dihedral groups (p4m and D_2 .. D_8)
-on MI355X (gfx950).
+groups (p4 and C_2 .. C_16) and of the dihedral groups (p4m and D_2 .. D_8),
+and the p4 group convolution on the plane, on MI355X (gfx950).
 
 Argument marshalling only: every step of the layer runs in the HIP kernels of
 ``libeqlinear.so``.  PyTorch supplies device memory and streams; the functions
 below take torch tensors (or raw integer pointers) and pass their addresses to
-the C ABI declared in ``include/eqlinear.h``, under the same names.
+the C ABI declared in ``include/eqlinear.h`` and ``include/eqconv.h``, under
+the same names.
 
 There is no fallback: if the library is missing, importing the binding's
 functions raises ``EqlinearUnavailable`` on first use.
@@ -53,6 +54,14 @@ EXPORTED = (
     "eqlinear_status_string",
     "eqlinear_last_error",
     "eqlinear_mac_counts",
+    "eqconv_plan_create",
+    "eqconv_plan_destroy",
+    "eqconv_set_weight",
+    "eqconv_forward",
+    "eqconv_backward_input",
+    "eqconv_backward_weight_workspace",
+    "eqconv_backward_weight",
+    "eqconv_mac_counts",
 )
 
 
@@ -108,6 +117,23 @@ def load_library(path=LIB_PATH):
     lib.eqlinear_last_error.restype = ctypes.c_char_p
     lib.eqlinear_mac_counts.argtypes = [vp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.eqlinear_mac_counts.restype = st
+    lib.eqconv_plan_create.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(vp)]
+    lib.eqconv_plan_create.restype = st
+    lib.eqconv_plan_destroy.argtypes = [vp]
+    lib.eqconv_plan_destroy.restype = st
+    lib.eqconv_set_weight.argtypes = [vp, vp, vp, vp]
+    lib.eqconv_set_weight.restype = st
+    lib.eqconv_forward.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.eqconv_forward.restype = st
+    lib.eqconv_backward_input.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.eqconv_backward_input.restype = st
+    lib.eqconv_backward_weight_workspace.argtypes = [vp, i64, i64, i64]
+    lib.eqconv_backward_weight_workspace.restype = ctypes.c_size_t
+    lib.eqconv_backward_weight.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t,
+                                           vp]
+    lib.eqconv_backward_weight.restype = st
+    lib.eqconv_mac_counts.argtypes = [vp, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.eqconv_mac_counts.restype = st
     _lib = lib
     return lib
 
@@ -201,6 +227,50 @@ def eqlinear_mac_counts(plan, N):
     s, d = ctypes.c_int64(), ctypes.c_int64()
     _check(load_library().eqlinear_mac_counts(plan, N, ctypes.byref(s), ctypes.byref(d)),
            "eqlinear_mac_counts")
+    return s.value, d.value
+
+
+def eqconv_plan_create(C, D, k, dtype=EQL_F32):
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.eqconv_plan_create(C, D, k, dtype, ctypes.byref(h)), "eqconv_plan_create")
+    return h.value
+
+
+def eqconv_plan_destroy(plan):
+    _check(load_library().eqconv_plan_destroy(plan), "eqconv_plan_destroy")
+
+
+def eqconv_set_weight(plan, psi, bias=None, stream=None):
+    _check(load_library().eqconv_set_weight(plan, _ptr(psi), _ptr(bias), _stream(stream)),
+           "eqconv_set_weight")
+
+
+def eqconv_forward(plan, f, y, N, H, W, act=EQL_ACT_NONE, stream=None):
+    _check(load_library().eqconv_forward(plan, _ptr(f), _ptr(y), N, H, W, act, _stream(stream)),
+           "eqconv_forward")
+
+
+def eqconv_backward_input(plan, dy, df, N, H, W, stream=None):
+    _check(load_library().eqconv_backward_input(plan, _ptr(dy), _ptr(df), N, H, W,
+                                                _stream(stream)), "eqconv_backward_input")
+
+
+def eqconv_backward_weight_workspace(plan, N, H, W):
+    return int(load_library().eqconv_backward_weight_workspace(plan, N, H, W))
+
+
+def eqconv_backward_weight(plan, f, dy, dpsi, dbias, N, H, W, workspace, workspace_bytes,
+                           stream=None):
+    _check(load_library().eqconv_backward_weight(
+        plan, _ptr(f), _ptr(dy), _ptr(dpsi), _ptr(dbias), N, H, W, _ptr(workspace),
+        workspace_bytes, _stream(stream)), "eqconv_backward_weight")
+
+
+def eqconv_mac_counts(plan, N, H, W):
+    s, d = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().eqconv_mac_counts(plan, N, H, W, ctypes.byref(s), ctypes.byref(d)),
+           "eqconv_mac_counts")
     return s.value, d.value
 
 
@@ -302,3 +372,78 @@ class Plan:
 
     def mac_counts(self, N):
         return eqlinear_mac_counts(self.handle, N)
+
+
+class ConvPlan:
+    """p4 group convolution plan (k x k kernel, zero padding, stride 1);
+    calls take contiguous torch CUDA tensors: f [N, H, W, C, 4],
+    y [N, H, W, D, 4], psi [D, C, k, k, 4], bias [D]."""
+
+    def __init__(self, C, D, k=3, dtype="f16"):
+        self.C, self.D, self.k, self.dtype = C, D, k, dtype
+        self.handle = eqconv_plan_create(C, D, k, _DTYPE_CODE[dtype])
+
+    def close(self):
+        if self.handle:
+            eqconv_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 -- interpreter shutdown
+            pass
+
+    _torch_dtype = Plan._torch_dtype
+    _expect = Plan._expect
+
+    def set_weight(self, psi, bias=None, stream=None):
+        self._expect(psi, (self.D, self.C, self.k, self.k, 4))
+        if bias is not None:
+            self._expect(bias, (self.D,))
+        eqconv_set_weight(self.handle, psi, bias, stream)
+
+    def forward(self, f, y=None, stream=None, act=None):
+        import torch
+        N, H, W = f.shape[:3]
+        self._expect(f, (N, H, W, self.C, 4))
+        if y is None:
+            y = torch.empty((N, H, W, self.D, 4), dtype=f.dtype, device=f.device)
+        self._expect(y, (N, H, W, self.D, 4))
+        eqconv_forward(self.handle, f, y, N, H, W, ACTIVATIONS[act], stream)
+        return y
+
+    def backward_input(self, dy, df=None, stream=None):
+        import torch
+        N, H, W = dy.shape[:3]
+        self._expect(dy, (N, H, W, self.D, 4))
+        if df is None:
+            df = torch.empty((N, H, W, self.C, 4), dtype=dy.dtype, device=dy.device)
+        self._expect(df, (N, H, W, self.C, 4))
+        eqconv_backward_input(self.handle, dy, df, N, H, W, stream)
+        return df
+
+    def workspace_bytes(self, N, H, W):
+        return eqconv_backward_weight_workspace(self.handle, N, H, W)
+
+    def backward_weight(self, f, dy, dpsi=None, dbias=None, workspace=None, stream=None,
+                        want_bias=True):
+        import torch
+        N, H, W = f.shape[:3]
+        self._expect(f, (N, H, W, self.C, 4))
+        self._expect(dy, (N, H, W, self.D, 4))
+        dev = f.device
+        if dpsi is None:
+            dpsi = torch.empty((self.D, self.C, self.k, self.k, 4), dtype=torch.float32,
+                               device=dev)
+        if dbias is None and want_bias:
+            dbias = torch.empty((self.D,), dtype=torch.float32, device=dev)
+        need = self.workspace_bytes(N, H, W)
+        if workspace is None:
+            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+        eqconv_backward_weight(self.handle, f, dy, dpsi, dbias, N, H, W, workspace,
+                               workspace.numel() * workspace.element_size(), stream)
+        return dpsi, dbias
+
+    def mac_counts(self, N, H, W):
+        return eqconv_mac_counts(self.handle, N, H, W)

@@ -16,7 +16,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["eqlinear_api.hip", "k_spectra.hip", "k_spectral_gemm.hip", "k_fwd_stream.hip", "k_fwd_coop.hip", "k_fwd_ws.hip", "k_fwd_ws32.hip",
            "k_bwd_weight.hip", "k_bwd_weight_mfma.hip", "k_bwd_weight_ws.hip",
-           "k_gemm_kstream.hip", "k_cyclic.hip", "k_p4m_pairs.hip"]
+           "k_gemm_kstream.hip", "k_cyclic.hip", "k_p4m_pairs.hip",
+           "k_conv.hip", "eqconv_api.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -116,6 +116,21 @@ hipError_t launch_p4m_pair_weight(const void* W, const void* bias, void* Wp, voi
 hipError_t launch_p4m_fold(const float* dWp, const float* dbp, float* dW, float* dbias, int64_t C,
                            int64_t D, hipStream_t s);
 
+// p4 group convolution through rotation-aware patches (k_conv.hip).  launch_conv
+// runs the patch layer whose spectra [n_pad][k_pad] are given, gathering from
+// a field [P][Cs][4] of H x W images with a k x k kernel; launch_conv_gather
+// writes the patches [P][k^2 Cs][4]; launch_conv_patch_weights writes the
+// forward [D][k^2 C][4] and adjoint [C][k^2 D][4] patch weights of psi
+// [D][C][k][k][4]; launch_conv_fold takes dpsi from the patch-weight gradient.
+hipError_t launch_conv(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs, int k, int64_t P,
+                       const void* spec, const float* bias, void* out, int k_pad, int n_out,
+                       int n_pad, int act, hipStream_t s);
+hipError_t launch_conv_gather(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs, int k,
+                              int64_t P, void* xp, hipStream_t s);
+hipError_t launch_conv_patch_weights(eqlinear_dtype_t dt, const void* psi, void* wf, void* wa,
+                                     int C, int D, int k, hipStream_t s);
+hipError_t launch_conv_fold(const float* dwp, float* dpsi, int C, int D, int k, hipStream_t s);
+
 // Cyclic-group kernels (k_cyclic.hip), any group size 2 <= T <= 16.
 namespace cyc {
 size_t workspace_bytes(const eqlinear_plan* p, int64_t N);

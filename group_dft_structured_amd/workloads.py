@@ -1,5 +1,5 @@
 """Seeded synthetic workloads for the EQ-Linear layer (p4, other cyclic groups,
-and p4m).
+and p4m) and for the p4 group convolution.
 
 This module holds the workload shapes and the seeded input generators, and
 nothing of the layer's arithmetic.  It is the one module shared by the oracle
@@ -14,6 +14,11 @@ counted per group element (a row holds C*T input and D*T output features).
 The C8 and p4m workloads keep the ViT-S-like MLP widths (384 -> 1536
 features) on a group of order 8 (rotations by 45 degrees; rotations by 90
 degrees and reflections), so C and D are half of the p4 ones.
+
+The convolution workloads stand in for an equivariant convolution at the
+first stage of a Swin-like network (64 images at 56 x 56, 192 features = 48
+channels per rotation, 3 x 3 kernel); the pages name such convolutions as the
+next operator and give no shapes ("Limitazioni e Lavoro Futuro").
 
 Drawing rule: numpy PCG64 seeded with ``seed``, draws in the order x, W, bias,
 dy, each in fp64, then cast to fp32 and, for fp16 runs, from fp32 to fp16 with
@@ -90,3 +95,49 @@ def workload_inputs(name, dtype=None, seed=0):
     w = WORKLOADS[name]
     dt = dtype or w.dtypes[0]
     return make_inputs(w.C, w.D, w.N, w.T, dt, seed, bias=w.bias, dy="backward" in w.passes)
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    N: int
+    H: int
+    W: int
+    C: int
+    D: int
+    k: int
+    dtypes: tuple
+    bias: bool
+    desc: str
+
+
+CONV_WORKLOADS = {
+    "p4conv_tiny": ConvWorkload("p4conv_tiny", 2, 8, 8, 8, 8, 3, ("f32", "f16"), True,
+                                "tiny p4 group convolution, 2 images at 8 x 8, 32->32 features"),
+    "p4conv_stage": ConvWorkload("p4conv_stage", 64, 56, 56, 48, 48, 3, ("f16", "f32"), True,
+                                 "p4 group convolution 3 x 3 at a Swin-like first stage, "
+                                 "64 images at 56 x 56, 192->192 features"),
+}
+
+
+def make_conv_inputs(N, H, W, C, D, k, dtype="f32", seed=0, bias=True, dy=False):
+    """Seeded synthetic tensors {f, psi, bias, dy} as numpy arrays in ``dtype``.
+
+    f: [N, H, W, C, 4] ~ N(0, 1); psi: [D, C, k, k, 4] ~ N(0, 1/(4 C k^2))
+    (fan-in); bias: [D] ~ N(0, 0.02) or None; dy: [N, H, W, D, 4] ~ N(0, 1) or
+    None.  Drawn in that order, as make_inputs."""
+    if dtype not in _NP_DTYPE:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    out = {}
+    out["f"] = _cast(rng.standard_normal((N, H, W, C, 4)), dtype)
+    out["psi"] = _cast(rng.standard_normal((D, C, k, k, 4)) * np.sqrt(1.0 / (4 * C * k * k)), dtype)
+    out["bias"] = _cast(rng.standard_normal(D) * np.sqrt(0.02), dtype) if bias else None
+    out["dy"] = _cast(rng.standard_normal((N, H, W, D, 4)), dtype) if dy else None
+    return out
+
+
+def conv_workload_inputs(name, dtype=None, seed=0, dy=False):
+    w = CONV_WORKLOADS[name]
+    dt = dtype or w.dtypes[0]
+    return make_conv_inputs(w.N, w.H, w.W, w.C, w.D, w.k, dt, seed, bias=w.bias, dy=dy)

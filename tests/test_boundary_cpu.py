@@ -10,7 +10,7 @@ import pytest
 import group_dft_structured_amd as eq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "eqlinear.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("eqlinear.h", "eqconv.h")]
 
 
 def _lib():
@@ -20,15 +20,19 @@ def _lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(eqlinear_[a-z_]+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names |= set(re.findall(r"\b(eq(?:linear|conv)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary_calls():
     names = declared_functions()
     for n in ("eqlinear_plan_create", "eqlinear_set_weight", "eqlinear_forward",
-              "eqlinear_backward_input", "eqlinear_backward_weight"):
+              "eqlinear_backward_input", "eqlinear_backward_weight", "eqconv_plan_create",
+              "eqconv_set_weight", "eqconv_forward", "eqconv_backward_input",
+              "eqconv_backward_weight"):
         assert n in names
     assert sorted(eq.EXPORTED) == names
 

@@ -1,0 +1,157 @@
+"""GPU parity of the p4 group convolution (include/eqconv.h) against the fp64
+oracle, through the C ABI: forward (with and without the fused GELU),
+backward input and backward filter, on ragged pixel counts, kernel sizes 1, 3
+and 5, both tile shapes, degenerate images, equivariance on the device, and
+the full Swin-like stage shape on sampled images."""
+import numpy as np
+import pytest
+
+import oracle
+from group_dft_structured_amd import ConvPlan, EqlinearError
+from group_dft_structured_amd.workloads import CONV_WORKLOADS, make_conv_inputs
+from tests.gpu_helpers import TOL, gpu_available, rel_err, to_dev, to_np64, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+# (N, H, W, C, D, k): pixel counts off the 64-row tile, output widths on both
+# tile shapes (D <= 64 and D > 64), patch widths of several chunks with a
+# ragged last one, kernel sizes 1, 3 and 5, non-square images
+SHAPES = [
+    (2, 7, 9, 8, 12, 3),
+    (1, 13, 11, 4, 68, 3),
+    (2, 6, 5, 16, 8, 5),
+    (3, 4, 4, 12, 4, 1),
+    (1, 20, 20, 32, 40, 3),
+    (1, 9, 12, 20, 132, 3),
+]
+
+
+def _case(shape, dtype, seed=5, bias=True):
+    N, H, W, C, D, k = shape
+    inp = make_conv_inputs(N, H, W, C, D, k, dtype=dtype, seed=seed, bias=bias, dy=True)
+    plan = ConvPlan(C, D, k, dtype)
+    plan.set_weight(to_dev(inp["psi"]), to_dev(inp["bias"]))
+    return inp, plan
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward(shape, dtype):
+    inp, plan = _case(shape, dtype)
+    y = plan.forward(to_dev(inp["f"]))
+    ref = oracle.conv_forward(inp["f"], inp["psi"], inp["bias"])
+    assert rel_err(to_np64(y), ref) <= TOL[dtype]
+    plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+def test_forward_act(act, dtype):
+    inp, plan = _case((2, 7, 9, 8, 12, 3), dtype)
+    y = plan.forward(to_dev(inp["f"]), act=act)
+    ref = oracle.conv_forward_act(inp["f"], inp["psi"], inp["bias"], act)
+    assert rel_err(to_np64(y), ref) <= TOL[dtype]
+    plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_input(shape, dtype):
+    inp, plan = _case(shape, dtype)
+    df = plan.backward_input(to_dev(inp["dy"]))
+    ref = oracle.conv_backward_input(inp["dy"], inp["psi"])
+    assert rel_err(to_np64(df), ref) <= TOL[dtype]
+    plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_weight(shape, dtype):
+    inp, plan = _case(shape, dtype)
+    dpsi, dbias = plan.backward_weight(to_dev(inp["f"]), to_dev(inp["dy"]))
+    rpsi, rbias = oracle.conv_backward_weight(inp["f"], inp["dy"], shape[5])
+    assert rel_err(to_np64(dpsi), rpsi) <= TOL[dtype]
+    assert rel_err(to_np64(dbias), rbias) <= TOL[dtype]
+    plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_equivariance_on_device(dtype):
+    """Turning the input a quarter turn with the group shift turns the output
+    the same way; compared on the device outputs themselves."""
+    torch = torch_mod()
+    inp, plan = _case((2, 10, 10, 8, 12, 3), dtype)
+    f = to_dev(inp["f"])
+    y = plan.forward(f)
+    for r in (1, 2, 3):
+        fr = torch.roll(torch.rot90(f, r, dims=(1, 2)), r, dims=4).contiguous()
+        yr = plan.forward(fr)
+        want = torch.roll(torch.rot90(y, r, dims=(1, 2)), r, dims=4)
+        assert rel_err(to_np64(yr), to_np64(want)) <= TOL[dtype], r
+    plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_degenerate_images(dtype):
+    """Single-row, single-column and single-pixel images: every neighbour of
+    some pixels lies outside the image."""
+    for shape in [(3, 1, 9, 8, 8, 3), (2, 7, 1, 8, 8, 3), (5, 1, 1, 8, 8, 5)]:
+        inp, plan = _case(shape, dtype)
+        y = plan.forward(to_dev(inp["f"]))
+        assert rel_err(to_np64(y), oracle.conv_forward(inp["f"], inp["psi"], inp["bias"])) \
+            <= TOL[dtype], shape
+        df = plan.backward_input(to_dev(inp["dy"]))
+        assert rel_err(to_np64(df), oracle.conv_backward_input(inp["dy"], inp["psi"])) \
+            <= TOL[dtype], shape
+        plan.close()
+
+
+def test_zero_pixels_and_errors():
+    torch = torch_mod()
+    inp, plan = _case((2, 4, 4, 8, 8, 3), "f32")
+    y = torch.empty((0, 4, 4, 8, 4), device="cuda")
+    plan.forward(torch.empty((0, 4, 4, 8, 4), device="cuda"), y)
+    dpsi, dbias = plan.backward_weight(torch.empty((2, 0, 4, 8, 4), device="cuda"),
+                                       torch.empty((2, 0, 4, 8, 4), device="cuda"))
+    torch.cuda.synchronize()
+    assert float(dpsi.abs().max()) == 0.0 and float(dbias.abs().max()) == 0.0
+    fresh = ConvPlan(8, 8, 3, "f32")
+    with pytest.raises(EqlinearError):
+        fresh.forward(to_dev(inp["f"]))  # no weight set
+    fresh.close()
+    plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_stage_shape_sampled_images(dtype):
+    """The Swin-like stage shape (64 images at 56 x 56, 48 -> 48 channels,
+    3 x 3) in the launch configuration the benchmark times.  Images are
+    independent, so the oracle checks the first and the last image of the
+    forward and backward-input outputs; for the filter gradient dy is zero
+    outside those two images, which makes the full-size reduction's answer the
+    oracle's on them."""
+    w = CONV_WORKLOADS["p4conv_stage"]
+    inp = make_conv_inputs(w.N, w.H, w.W, w.C, w.D, w.k, dtype=dtype, seed=0, bias=True, dy=True)
+    plan = ConvPlan(w.C, w.D, w.k, dtype)
+    plan.set_weight(to_dev(inp["psi"]), to_dev(inp["bias"]))
+    idx = [0, w.N - 1]
+    y = to_np64(plan.forward(to_dev(inp["f"])))
+    ref = oracle.conv_forward(inp["f"][idx], inp["psi"], inp["bias"])
+    assert rel_err(y[idx], ref) <= TOL[dtype]
+    df = to_np64(plan.backward_input(to_dev(inp["dy"])))
+    ref = oracle.conv_backward_input(inp["dy"][idx], inp["psi"])
+    assert rel_err(df[idx], ref) <= TOL[dtype]
+    dy = np.zeros_like(inp["dy"])
+    dy[idx] = inp["dy"][idx]
+    dpsi, dbias = plan.backward_weight(to_dev(inp["f"]), to_dev(dy))
+    rpsi, rbias = oracle.conv_backward_weight(inp["f"][idx], inp["dy"][idx], w.k)
+    assert rel_err(to_np64(dpsi), rpsi) <= TOL[dtype]
+    assert rel_err(to_np64(dbias), rbias) <= TOL[dtype]
+    plan.close()
