@@ -321,8 +321,9 @@ def all_configs(args):
     eq.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
-    names = args.configs.split(",") if args.configs else list(WORKLOADS)
-    for w in (WORKLOADS[n] for n in names):
+    from group_dft_structured_amd.workloads import CONV_WORKLOADS
+    names = args.configs.split(",") if args.configs else list(WORKLOADS) + list(CONV_WORKLOADS)
+    for w in (WORKLOADS[n] for n in names if n in WORKLOADS):
         for dtype in w.dtypes:
             N, C, D, T = w.N, w.C, w.D, w.T
             esz = 2 if dtype == "f16" else 4
@@ -370,6 +371,61 @@ def all_configs(args):
             plan.close()
             del t, passes
             torch.cuda.empty_cache()
+    for w in (CONV_WORKLOADS[n] for n in names if n in CONV_WORKLOADS):
+        for dtype in w.dtypes:
+            all_configs_conv(w, dtype, stream, dev)
+
+
+def conv_pass_line(w, dtype, name, us, flops, nbytes):
+    tf = flops / (us * 1e-6) / 1e12
+    gbps = nbytes / (us * 1e-6) / 1e9
+    ridge = PEAK_MFMA_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    bound = "hbm" if flops / nbytes < ridge else "mfma"
+    frac = gbps / PEAK_HBM_GBPS if bound == "hbm" else tf / PEAK_MFMA_TFLOPS[dtype]
+    return {"workload": w.name, "group": "p4 convolution", "N": w.N, "H": w.H, "W": w.W,
+            "C": w.C, "D": w.D, "k": w.k, "dtype": dtype, "pass": name, "us": round(us, 3),
+            "tflops_actual": round(tf, 2), "tflops_dense_equiv": round(tf * 16 / 6, 2),
+            "mfma_peak_frac": round(tf / PEAK_MFMA_TFLOPS[dtype], 4),
+            "hbm_gbps": round(gbps, 1), "alg_bytes": nbytes,
+            "roofline": {"bound": bound, "frac": round(frac, 4)}}
+
+
+def all_configs_conv(w, dtype, stream, dev):
+    """The p4 group convolution: forward (plain and with GELU), backward
+    input and backward filter.  Algorithmic bytes: the field read once, the
+    output written once, the patch-weight spectra (and for the filter
+    gradient the binary32 dpsi and dbias); flops 12 k^2 C D per pixel."""
+    import torch
+    import group_dft_structured_amd as eq
+    from group_dft_structured_amd.workloads import make_conv_inputs
+    esz = 2 if dtype == "f16" else 4
+    P = w.N * w.H * w.W
+    inp = make_conv_inputs(w.N, w.H, w.W, w.C, w.D, w.k, dtype=dtype, seed=0, bias=w.bias, dy=True)
+    t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items() if v is not None}
+    del inp
+    plan = eq.ConvPlan(w.C, w.D, w.k, dtype)
+    plan.set_weight(t["psi"], t.get("bias"))
+    flops = 12.0 * w.k * w.k * w.C * w.D * P
+    spec = 4 * w.k * w.k * w.C * w.D * esz
+    io = P * 4 * (w.C + w.D) * esz
+    y = torch.empty((w.N, w.H, w.W, w.D, 4), dtype=t["f"].dtype, device=dev)
+    df = torch.empty_like(t["f"])
+    dpsi = torch.empty((w.D, w.C, w.k, w.k, 4), dtype=torch.float32, device=dev)
+    db = torch.empty((w.D,), dtype=torch.float32, device=dev)
+    ws = torch.empty((plan.workspace_bytes(w.N, w.H, w.W),), dtype=torch.uint8, device=dev)
+    passes = {
+        "forward": (lambda: plan.forward(t["f"], y), io + spec + 4 * w.D),
+        "forward_gelu": (lambda: plan.forward(t["f"], y, act="gelu"), io + spec + 4 * w.D),
+        "backward_input": (lambda: plan.backward_input(t["dy"], df), io + spec),
+        "backward_weight": (lambda: plan.backward_weight(t["f"], t["dy"], dpsi, db, ws),
+                            io + 4 * w.k * w.k * w.C * w.D * 4 + 4 * w.D),
+    }
+    for name, (fn, nbytes) in passes.items():
+        us = time_graph(fn, stream, 5, 5)
+        print(json.dumps(conv_pass_line(w, dtype, name, us, flops, nbytes)), flush=True)
+    plan.close()
+    del t, passes, ws
+    torch.cuda.empty_cache()
 
 
 COPY_BYTES = 512 << 20  # calibration copy: 512 MiB read + 512 MiB written

@@ -60,6 +60,14 @@ size_t ws_dwp(const eqconv_plan* p) {
   return ru256((size_t)(p->D * p->k * p->k * p->C) * 4 * sizeof(float));
 }
 
+// A kernel reads the rows of one tile and a halo of h image rows and h
+// pixels on each side through one buffer resource (offsets below 2^31).
+bool span_fits(const eqconv_plan* p, int64_t Cs, int64_t W) {
+  const int64_t h = p->k / 2;
+  const int64_t span = 2 * h * W + 2 * h + 128;  // pixels, largest tile
+  return span * Cs * 4 * (int64_t)p->esize < ((int64_t)1 << 31) - 64;
+}
+
 eqlinear_status_t hip_status(const char* what, hipError_t e) {
   if (e == hipSuccess) return EQL_OK;
   fprintf(stderr, "eqconv: %s: %s\n", what, hipGetErrorString(e));
@@ -148,6 +156,7 @@ static eqlinear_status_t run_conv(const eqlinear_plan* inner, const eqconv_plan*
   if (P == 0) return EQL_OK;
   if (src == nullptr || out == nullptr) return EQL_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned16(out)) return EQL_ERR_MISALIGNED;
+  if (!span_fits(p, Cs, W)) return EQL_ERR_UNSUPPORTED;
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != inner->device) return EQL_ERR_INVALID_ARG;
   return hip_status("convolution launch",
@@ -191,6 +200,7 @@ eqlinear_status_t eqconv_backward_weight(eqconv_plan_t p, const void* f, const v
     return EQL_ERR_MISALIGNED;
   const size_t need = eqconv_backward_weight_workspace(p, N, H, W);
   if (workspace == nullptr || workspace_bytes < need) return EQL_ERR_WORKSPACE;
+  if (P > 0 && !span_fits(p, p->C, W)) return EQL_ERR_UNSUPPORTED;
   char* ws = (char*)workspace;
   void* xp = ws;
   void* inner_ws = ws + ws_patches(p, P);

@@ -111,6 +111,28 @@ struct PatchQuads {
   Q q[4];
 };
 
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): loads at an offset past the end
+// return zeros, which gives the zero padding of the image border without a
+// branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t conv_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t OOB = 0x7FFFFFF0u;
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::quad load_q(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ half4 load_q<_Float16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ floatx4 load_q<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 template <typename T>
 __device__ __forceinline__ void patch_mode(const PatchSrc& s, int cp, int& mode, int& c, int& ua,
                                            int& ub) {
@@ -129,32 +151,30 @@ __device__ __forceinline__ void patch_mode(const PatchSrc& s, int cp, int& mode,
   }
 }
 
+// The four quads of a pixel's patch channels, read through the resource r
+// whose first pixel is pix0 (pix = -1: a row past the end, zeros).
 template <typename T>
-__device__ __forceinline__ PatchQuads<T> patch_load(const PatchSrc& s, int pix, int pi, int pj,
-                                                    int mode, int c, int ua, int ub) {
-  typedef typename Elem<T>::quad Q;
-  const T* f = (const T*)s.f;
-  PatchQuads<T> r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r.q[j] = Q{};
-  if (pix < 0 || mode == 2) return r;
-  if (mode == 0) {
-    const T* base = f + ((int64_t)pix * s.Cs + c) * 4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.q[j] = *reinterpret_cast<const Q*>(base + 4 * j);
-    return r;
-  }
+__device__ __forceinline__ PatchQuads<T> patch_load(const PatchSrc& s, __amdgpu_buffer_rsrc_t r,
+                                                    int pix0, int pix, int pi, int pj, int mode, int c,
+                                                    int ua, int ub) {
+  constexpr int QB = 4 * (int)sizeof(T);  // bytes per quad
+  PatchQuads<T> out;
+  const bool live = pix >= 0 && mode != 2;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int va, vb;
-    turn(ua, ub, j, va, vb);
-    const int ii = pi + va, jj = pj + vb;
-    if (ii >= 0 && ii < s.H && jj >= 0 && jj < s.W) {
-      const int64_t q = (int64_t)pix + (int64_t)va * s.W + vb;
-      r.q[j] = *reinterpret_cast<const Q*>(f + (q * s.Cs + c) * 4);
+    uint32_t off = OOB;
+    if (mode == 0) {
+      off = (uint32_t)(((pix - pix0) * s.Cs + c + j) * QB);
+    } else {
+      int va, vb;
+      turn(ua, ub, j, va, vb);
+      const int ii = pi + va, jj = pj + vb;
+      if (ii >= 0 && ii < s.H && jj >= 0 && jj < s.W)
+        off = (uint32_t)(((pix + va * s.W + vb - pix0) * s.Cs + c) * QB);
     }
+    out.q[j] = load_q<T>(r, live ? off : OOB);
   }
-  return r;
+  return out;
 }
 
 // Group vector e (0..3) of the four patch channels.
@@ -212,6 +232,15 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void k_conv_gemm(
   const int wr = wave / WAVES_N, wc = wave % WAVES_N;
   const int64_t plane = (int64_t)n_pad * k_pad;
 
+  // the field rows this tile reads: its pixels and a halo of h image rows
+  // and h pixels on each side
+  const int halo = src.h * src.W + src.h;
+  const int pix0 = m0 - halo > 0 ? m0 - halo : 0;
+  const int pix1 = m0 + BM + halo < src.P ? m0 + BM + halo : src.P;
+  const __amdgpu_buffer_rsrc_t rf =
+      conv_rsrc((const T*)src.f + (int64_t)pix0 * src.Cs * 4,
+                (uint32_t)((int64_t)(pix1 - pix0) * src.Cs * 4 * (int)sizeof(T)));
+
   // staging rows of this thread and their image coordinates
   const int cg = (tid % TPR) * 4;
   int pix[PASSES], pi[PASSES], pj[PASSES];
@@ -226,21 +255,22 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void k_conv_gemm(
   }
 
   PatchQuads<T> qa[PASSES];
-  uint4 qb[UPT];
+  u32x4v qb[UPT];
   int mode = 2;
   auto load_chunk = [&](int k0) {
     int c = 0, ua = 0, ub = 0;
     patch_mode<T>(src, k0 + cg, mode, c, ua, ub);
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) qa[ps] = patch_load<T>(src, pix[ps], pi[ps], pj[ps], mode, c, ua, ub);
+    for (int ps = 0; ps < PASSES; ++ps)
+      qa[ps] = patch_load<T>(src, rf, pix0, pix[ps], pi[ps], pj[ps], mode, c, ua, ub);
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = i * NT + tid;
       if (UNITS % NT == 0 || u < UNITS) {
         const int p = u / (BN * 4), rem = u % (BN * 4);
         const int j = rem / 4, q = rem % 4;
-        qb[i] = *reinterpret_cast<const uint4*>(spec + p * plane + (int64_t)(n0 + j) * k_pad + k0 +
-                                                q * EPU);
+        qb[i] = *reinterpret_cast<const u32x4v*>(spec + p * plane + (int64_t)(n0 + j) * k_pad + k0 +
+                                                 q * EPU);
       }
     }
   };
@@ -272,7 +302,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void k_conv_gemm(
       if (UNITS % NT == 0 || u < UNITS) {
         const int p = u / (BN * 4), rem = u % (BN * 4);
         const int j = rem / 4, q = rem % 4;
-        *reinterpret_cast<uint4*>(Bs + p * B_PLANE + j * SK + q * EPU) = qb[i];
+        *reinterpret_cast<u32x4v*>(Bs + p * B_PLANE + j * SK + q * EPU) = qb[i];
       }
     }
   };
@@ -359,8 +389,14 @@ __global__ __launch_bounds__(256) void k_conv_gather(const PatchSrc src, T* __re
   const int cp = (int)(i % blocks4) * 4;
   int mode = 2, c = 0, ua = 0, ub = 0;
   patch_mode<T>(src, cp, mode, c, ua, ub);
+  const int halo = src.h * src.W + src.h;
+  const int pix0 = pix - halo > 0 ? pix - halo : 0;
+  const int pix1 = pix + 1 + halo < src.P ? pix + 1 + halo : src.P;
+  const __amdgpu_buffer_rsrc_t rf =
+      conv_rsrc((const T*)src.f + (int64_t)pix0 * src.Cs * 4,
+                (uint32_t)((int64_t)(pix1 - pix0) * src.Cs * 4 * (int)sizeof(T)));
   const PatchQuads<T> r =
-      patch_load<T>(src, pix, (pix / src.W) % src.H, pix % src.W, mode, c, ua, ub);
+      patch_load<T>(src, rf, pix0, pix, (pix / src.W) % src.H, pix % src.W, mode, c, ua, ub);
   T* out = xp + ((int64_t)pix * src.K + cp) * 4;
 #pragma unroll
   for (int e = 0; e < 4; ++e)

@@ -80,7 +80,10 @@ eqlinear_status_t eqconv_set_weight(eqconv_plan_t plan, const void* psi, const v
  * the patch gather, the group DFT, the real products on the matrix cores with
  * fp32 accumulation, the inverse DFT, bias and activation.  N*H*W = 0 is a
  * successful no-op; N, H, W < 0 or N*H*W >= 2^31 return
- * EQL_ERR_INVALID_ARG; before set_weight, EQL_ERR_NO_WEIGHT. */
+ * EQL_ERR_INVALID_ARG; before set_weight, EQL_ERR_NO_WEIGHT.  A tile of
+ * pixels and its halo of k/2 image rows on each side must span under 2 GiB
+ * of the field ((k - 1) * W * C * 4 elements, roughly), else
+ * EQL_ERR_UNSUPPORTED. */
 eqlinear_status_t eqconv_forward(eqconv_plan_t plan, const void* f, void* y, int64_t N,
                                  int64_t H, int64_t W, eqlinear_act_t act, void* stream);
 
