@@ -51,13 +51,13 @@ eqlinear_status_t make_inner(int64_t K, int64_t n_out, eqlinear_dtype_t dt, eqli
 }
 
 size_t ws_patches(const eqconv_plan* p, int64_t P) {
-  return ru256((size_t)P * (size_t)(p->k * p->k * p->C) * 4 * p->esize);
+  return ru256((size_t)P * (size_t)eql::conv_patch_width((int)p->C, (int)p->k) * 4 * p->esize);
 }
 size_t ws_inner(const eqconv_plan* p, int64_t P) {
   return ru256(eqlinear_backward_weight_workspace(p->fwd, P));
 }
 size_t ws_dwp(const eqconv_plan* p) {
-  return ru256((size_t)(p->D * p->k * p->k * p->C) * 4 * sizeof(float));
+  return ru256((size_t)p->D * eql::conv_patch_width((int)p->C, (int)p->k) * 4 * sizeof(float));
 }
 
 // A kernel reads the rows of one tile and a halo of h image rows and h
@@ -86,7 +86,10 @@ eqlinear_status_t eqconv_plan_create(int64_t C, int64_t D, int64_t k, eqlinear_d
   if (dtype != EQL_F32 && dtype != EQL_F16) return EQL_ERR_UNSUPPORTED;
   if (k < 1 || k > MAX_K || k % 2 == 0) return EQL_ERR_UNSUPPORTED;
   if (C % 4 != 0 || D % 4 != 0) return EQL_ERR_UNSUPPORTED;
-  if (k * k * C > MAX_PATCH_CHANNELS || k * k * D > MAX_PATCH_CHANNELS) return EQL_ERR_UNSUPPORTED;
+  if (C > MAX_PATCH_CHANNELS || D > MAX_PATCH_CHANNELS) return EQL_ERR_UNSUPPORTED;
+  if (eql::conv_patch_width((int)C, (int)k) > MAX_PATCH_CHANNELS ||
+      eql::conv_patch_width((int)D, (int)k) > MAX_PATCH_CHANNELS)
+    return EQL_ERR_UNSUPPORTED;
   eqconv_plan* p = new (std::nothrow) eqconv_plan;
   if (p == nullptr) return EQL_ERR_ALLOC;
   memset(p, 0, sizeof(*p));
@@ -95,8 +98,8 @@ eqlinear_status_t eqconv_plan_create(int64_t C, int64_t D, int64_t k, eqlinear_d
   p->k = k;
   p->dtype = dtype;
   p->esize = dtype == EQL_F16 ? 2 : 4;
-  eqlinear_status_t st = make_inner(k * k * C, D, dtype, &p->fwd);
-  if (st == EQL_OK) st = make_inner(k * k * D, C, dtype, &p->adj);
+  eqlinear_status_t st = make_inner(eql::conv_patch_width((int)C, (int)k), D, dtype, &p->fwd);
+  if (st == EQL_OK) st = make_inner(eql::conv_patch_width((int)D, (int)k), C, dtype, &p->adj);
   if (st != EQL_OK) {
     eqlinear_plan_destroy(p->fwd);
     eqlinear_plan_destroy(p->adj);
@@ -124,8 +127,10 @@ eqlinear_status_t eqconv_set_weight(eqconv_plan_t p, const void* psi, const void
                                     void* stream) {
   if (p == nullptr || psi == nullptr) return EQL_ERR_INVALID_ARG;
   if (!aligned16(psi) || !aligned16(bias)) return EQL_ERR_MISALIGNED;
-  const size_t wf_bytes = ru256((size_t)(p->D * p->k * p->k * p->C) * 4 * p->esize);
-  const size_t wa_bytes = ru256((size_t)(p->C * p->k * p->k * p->D) * 4 * p->esize);
+  const size_t wf_bytes =
+      ru256((size_t)p->D * eql::conv_patch_width((int)p->C, (int)p->k) * 4 * p->esize);
+  const size_t wa_bytes =
+      ru256((size_t)p->C * eql::conv_patch_width((int)p->D, (int)p->k) * 4 * p->esize);
   if (p->wbuf == nullptr) {
     hipError_t e = hipMalloc(&p->wbuf, wf_bytes + wa_bytes);
     if (e != hipSuccess) {

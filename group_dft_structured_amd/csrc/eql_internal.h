@@ -122,6 +122,14 @@ hipError_t launch_p4m_fold(const float* dWp, const float* dbp, float* dW, float*
 // writes the patches [P][k^2 Cs][4]; launch_conv_patch_weights writes the
 // forward [D][k^2 C][4] and adjoint [C][k^2 D][4] patch weights of psi
 // [D][C][k][k][4]; launch_conv_fold takes dpsi from the patch-weight gradient.
+// Patch channel layout of a field of Cs channels and a k x k kernel: the
+// centre channels padded to a multiple of 32 (a 32-channel reduction step is
+// then either centre or orbit channels), then 4 Cs channels per orbit of
+// offsets under the quarter turn, (k^2 - 1) / 4 orbits.
+__host__ __device__ inline int conv_centre_width(int Cs) { return (Cs + 31) / 32 * 32; }
+__host__ __device__ inline int conv_patch_width(int Cs, int k) {
+  return conv_centre_width(Cs) + (k * k - 1) * Cs;
+}
 hipError_t launch_conv(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs, int k, int64_t P,
                        const void* spec, const float* bias, void* out, int k_pad, int n_out,
                        int n_pad, int act, hipStream_t s);

@@ -42,6 +42,8 @@
 // weight spectra of the chunk are copied beside them.  The loads of chunk
 // i + 1 are issued before the matrix-core work of chunk i.  The epilogue
 // applies the inverse butterfly, bias and activation in fp32.
+#include <utility>
+
 #include "eql_device.h"
 #include "eql_internal.h"
 #include "gemm_tile.h"
@@ -59,6 +61,9 @@ __host__ __device__ __forceinline__ void turn(int a, int b, int j, int& ra, int&
     default: ra = b; rb = -a; break;
   }
 }
+
+__host__ __device__ __forceinline__ int centre_width(int Cs) { return conv_centre_width(Cs); }
+__host__ __device__ __forceinline__ int patch_width(int Cs, int k) { return conv_patch_width(Cs, k); }
 
 // Place of the filter entry psi[., c, w, r] (w = (wa, wb) a centred offset)
 // in the patch weight W'[., cp, m] for a field of Cs channels.
@@ -84,7 +89,7 @@ __host__ __device__ __forceinline__ void patch_place(int c, int wa, int wb, int 
   }
   const int o = (ua - 1) * (h + 1) + ub;
   const int e = (m - r) & 3;
-  cp = Cs + o * 4 * Cs + 4 * c + e;
+  cp = centre_width(Cs) + o * 4 * Cs + 4 * c + e;
 }
 
 }  // namespace
@@ -94,9 +99,10 @@ __host__ __device__ __forceinline__ void patch_place(int c, int wa, int wb, int 
 struct PatchSrc {
   const void* f;  // [P][Cs][4]
   int H, W, Cs;
-  int h;  // kernel half-width (k = 2h + 1)
-  int K;  // patch channels, k^2 Cs
-  int P;  // pixels, N*H*W
+  int h;   // kernel half-width (k = 2h + 1)
+  int Cc;  // centre width, Cs rounded up to 32
+  int K;   // patch channels, Cc + (k^2 - 1) Cs
+  int P;   // pixels, N*H*W
 };
 
 // Four patch channels starting at cp (a multiple of 4) of one pixel, as four
@@ -104,7 +110,7 @@ struct PatchSrc {
 //   mode 0: centre channels cp..cp+3 of the pixel itself, vector e = quad e;
 //   mode 1: orbit channels (c, e = 0..3), quad j = f[p + R^j u, c, 0..3],
 //           vector e = (quad j element (j + e) mod 4)_j;
-//   mode 2: beyond the patch width, zeros.
+//   mode 2: the centre padding or beyond the patch width, zeros.
 template <typename T>
 struct PatchQuads {
   typedef typename Elem<T>::quad Q;
@@ -136,14 +142,14 @@ __device__ __forceinline__ floatx4 load_q<float>(__amdgpu_buffer_rsrc_t r, uint3
 template <typename T>
 __device__ __forceinline__ void patch_mode(const PatchSrc& s, int cp, int& mode, int& c, int& ua,
                                            int& ub) {
-  if (cp >= s.K) {
+  if (cp >= s.K || (cp >= s.Cs && cp < s.Cc)) {
     mode = 2;
-  } else if (cp < s.Cs) {
+  } else if (cp < s.Cc) {
     mode = 0;
     c = cp;
   } else {
     mode = 1;
-    const int rem = cp - s.Cs;
+    const int rem = cp - s.Cc;
     const int o = rem / (4 * s.Cs);
     c = (rem - o * 4 * s.Cs) >> 2;
     ua = 1 + o / (s.h + 1);
@@ -403,39 +409,71 @@ __global__ __launch_bounds__(256) void k_conv_gather(const PatchSrc src, T* __re
     if (cp + e < src.K) *reinterpret_cast<Q*>(out + 4 * e) = Elem<T>::pack(patch_vector<T>(r, mode, e));
 }
 
-// Patch weights of the forward (W' [D][k^2 C][4]) and of the adjoint layer
-// (W*' [C][k^2 D][4], from psi*[c, d, w, r] = psi[d, c, -R^r w, (-r) mod 4]),
-// one thread per filter entry psi[d][c][a][b][q]; and the bias copy is left
-// to the inner plans.
+// Orbit representative o (row-major over rows 1..h, columns 0..h).
+__device__ __forceinline__ void orbit_rep(int o, int h, int& ua, int& ub) {
+  ua = 1 + o / (h + 1);
+  ub = o % (h + 1);
+}
+
+// Patch weights of the forward layer, W'[d, cp, m] over [D][Kf][4], and of
+// the adjoint layer, W*'[c, cp, m] over [C][Ka][4], one thread per entry:
+//     centre:  W'[d, c, m] = psi[d, c, 0, m]
+//     orbit:   W'[d, (u, c, e), m] = psi[d, c, R^-m u, (m - e) mod 4]
+// and the same for the adjoint filter psi*[c, d, w, r] = psi[d, c, -R^r w,
+// (-r) mod 4].  The centre padding gets zeros.
 template <typename T>
 __global__ __launch_bounds__(256) void k_conv_patch_weights(const T* __restrict__ psi,
                                                             T* __restrict__ wf, T* __restrict__ wa,
                                                             int C, int D, int k) {
-  const int64_t total = (int64_t)D * C * k * k * 4;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
   const int h = k / 2;
-  const int q = (int)(i & 3);
-  int64_t rest = i >> 2;
-  const int b = (int)(rest % k) - h;
-  rest /= k;
-  const int a = (int)(rest % k) - h;
-  rest /= k;
-  const int c = (int)(rest % C);
-  const int d = (int)(rest / C);
-  const T v = psi[i];
-  int cp, m;
-  patch_place(c, a, b, q, C, h, cp, m);
-  wf[((int64_t)d * (k * k * C) + cp) * 4 + m] = v;
-  // position in the adjoint filter: r = -q, w = -R^q (a, b)
-  int ta, tb;
-  turn(a, b, q, ta, tb);
-  patch_place(d, -ta, -tb, (-q) & 3, D, h, cp, m);
-  wa[((int64_t)c * (k * k * D) + cp) * 4 + m] = v;
+  const int Kf = patch_width(C, k), Ka = patch_width(D, k);
+  const int64_t nf = (int64_t)D * Kf * 4, na = (int64_t)C * Ka * 4;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool adj = i >= nf;
+  if (adj) i -= nf;
+  if (i >= (adj ? na : nf)) return;
+  const int m = (int)(i & 3);
+  const int K = adj ? Ka : Kf, Cs = adj ? D : C;  // patch width, gathered channels
+  const int cp = (int)((i >> 2) % K);
+  const int o_ch = (int)((i >> 2) / K);           // output channel of the patch layer
+  int src_ch = 0, wa_ = 0, wb_ = 0, r = 0;
+  bool zero = false;
+  if (cp < centre_width(Cs)) {
+    src_ch = cp;
+    zero = cp >= Cs;
+    r = m;
+  } else {
+    const int rem = cp - centre_width(Cs);
+    const int o = rem / (4 * Cs);
+    src_ch = (rem - o * 4 * Cs) >> 2;
+    const int e = rem & 3;
+    int ua, ub;
+    orbit_rep(o, h, ua, ub);
+    turn(ua, ub, (-m) & 3, wa_, wb_);
+    r = (m - e) & 3;
+  }
+  T v = (T)0.f;
+  if (!zero) {
+    // forward: psi[d = o_ch, c = src_ch, w, r];
+    // adjoint: psi*[c = o_ch, d = src_ch, w, r] = psi[d, c, -R^r w, -r]
+    int d = o_ch, c = src_ch, pa = wa_, pb = wb_, q = r;
+    if (adj) {
+      d = src_ch;
+      c = o_ch;
+      int ta, tb;
+      turn(wa_, wb_, r, ta, tb);
+      pa = -ta;
+      pb = -tb;
+      q = (-r) & 3;
+    }
+    v = psi[((((int64_t)d * C + c) * k + (pa + h)) * k + (pb + h)) * 4 + q];
+  }
+  (adj ? wa : wf)[i] = v;
 }
 
-// Filter gradient from the patch-weight gradient dW' [D][k^2 C][4] (fp32):
-// each entry has one place in W' (the map of k_conv_patch_weights).
+// Filter gradient from the patch-weight gradient dW' [D][Kf][4] (fp32):
+// each filter entry has one place in W' (the inverse of the map of
+// k_conv_patch_weights).
 __global__ __launch_bounds__(256) void k_conv_fold(const float* __restrict__ dwp,
                                                    float* __restrict__ dpsi, int C, int D, int k) {
   const int64_t total = (int64_t)D * C * k * k * 4;
@@ -452,7 +490,386 @@ __global__ __launch_bounds__(256) void k_conv_fold(const float* __restrict__ dwp
   const int d = (int)(rest / C);
   int cp, m;
   patch_place(c, a, b, q, C, h, cp, m);
-  dpsi[i] = dwp[((int64_t)d * (k * k * C) + cp) * 4 + m];
+  dpsi[i] = dwp[((int64_t)d * patch_width(C, k) + cp) * 4 + m];
+}
+
+// ---------------------------------------------------------------------------
+// Register-direct binary16 kernel.  A work-group of four waves (one per
+// SIMD) owns NB blocks of 16 output channels and walks 16-pixel tiles.  The
+// reduction steps (32 patch channels each) are split over the four waves;
+// each wave keeps the weight-spectrum fragments of its steps for all NB
+// blocks in VGPRs (A operand of v_mfma_f32_16x16x32_f16).  The x operand
+// needs no staging: lane (i16, g) of the B fragment of a step is pixel i16
+// and 8 consecutive patch channels, whose four group values it loads itself
+// (four 16-byte loads: 8 channels of the pixel for a centre step, or 2
+// channels of each of the four turned neighbours for an orbit step), so the
+// group DFT along the group axis is a butterfly inside the lane.  Loads run
+// one step ahead.  At the end of a tile the waves combine their partial
+// spectra through LDS; wave b finishes block b (inverse butterfly, bias,
+// activation, store).
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mma16(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  const f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+}  // namespace
+
+template <int NB, int KSW>
+__global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
+    const PatchSrc src, const _Float16* __restrict__ spec, const float* __restrict__ bias,
+    _Float16* __restrict__ y, int KS, int k_pad, int n_out, int n_pad, int n_ranges, int n_tiles,
+    int Qx, int act) {
+  constexpr int RED = 4 * NB * 4 * 64;  // f32x4 per partial buffer: wave x block x plane x lane
+  __shared__ __attribute__((aligned(16))) f32x4 red[2 * RED];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, g = lane >> 4;
+  // work-group -> (channel range j, XCD x, worker w); the XCD's workers take
+  // interleaved tiles of one contiguous run, so the halo rows they share
+  // stay in that XCD's L2
+  const int wgid = blockIdx.x, xcd = wgid & 7, slot = wgid >> 3;
+  const int j = slot % n_ranges, w = slot / n_ranges;
+  const int per = (n_tiles + 7) / 8;
+  const int t_begin = xcd * per + w;
+  const int t_end = (xcd + 1) * per < n_tiles ? (xcd + 1) * per : n_tiles;
+  const int n_my = t_begin < t_end ? (t_end - t_begin - 1) / Qx + 1 : 0;
+  if (n_my == 0) return;  // whole work-group
+
+  // this wave's reduction steps [ks0, ks0 + cnt), cnt >= 1 (the host
+  // launches this kernel for four steps or more)
+  const int ks0 = KS * wave / 4, cnt = KS * (wave + 1) / 4 - ks0;
+  const int d0 = j * NB * 16;
+
+  // weight fragments: channel d0 + 16nb + i16, patch channels 32s + 8g .. + 7
+  half8 w0[NB][KSW], w2[NB][KSW], wr[NB][KSW], wi[NB][KSW];
+  {
+    const uint32_t plane_bytes = (uint32_t)n_pad * k_pad * 2;
+    const int64_t plane = (int64_t)n_pad * k_pad;
+    const __amdgpu_buffer_rsrc_t r0 = conv_rsrc(spec, plane_bytes), r2 = conv_rsrc(spec + plane, plane_bytes);
+    const __amdgpu_buffer_rsrc_t rr = conv_rsrc(spec + 2 * plane, plane_bytes);
+    const __amdgpu_buffer_rsrc_t ri = conv_rsrc(spec + 3 * plane, plane_bytes);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < KSW; ++s) {
+        const int row = d0 + nb * 16 + i16;
+        const uint32_t off = s < cnt && row < n_pad
+                                 ? (uint32_t)(row * k_pad + 32 * (ks0 + s) + 8 * g) * 2
+                                 : OOB;
+        w0[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r0, off, 0, 0));
+        w2[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r2, off, 0, 0));
+        wr[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
+        wi[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ri, off, 0, 0));
+      }
+  }
+
+  // per-step constants of this lane's 8 patch channels, packed in one
+  // register per step: the source channel (centre steps: first of 8; orbit
+  // steps: first of 2) in bits 0-15, the orbit representative in bits 16-18
+  // and 19-21, and in bit 22 whether the channels exist (past the patch
+  // width they read zeros)
+  uint32_t kst[KSW];
+#pragma unroll
+  for (int s = 0; s < KSW; ++s) {
+    const int cp = 32 * (ks0 + s) + 8 * g;
+    int ch = 0, ra = 0, rb = 0;
+    const bool lv = s < cnt && cp < src.K;
+    if (cp < src.Cc) {
+      ch = cp;
+    } else if (lv) {
+      const int rem = cp - src.Cc;
+      const int o = rem / (4 * src.Cs);
+      ch = (rem - o * 4 * src.Cs) >> 2;  // even
+      orbit_rep(o, src.h, ra, rb);
+    }
+    kst[s] = (uint32_t)ch | ((uint32_t)ra << 16) | ((uint32_t)rb << 19) | ((lv ? 1u : 0u) << 22);
+  }
+
+  // tile state of the gather (the gather runs ahead of the products)
+  int g_ti = -1, p = 0, pi = 0, pj = 0, lo = 0;
+  bool pix_ok = false;
+  __amdgpu_buffer_rsrc_t rf = conv_rsrc(src.f, 0);
+  const int halo = src.h * src.W + src.h;
+
+  // loads of step S of this worker's tile ti; tiles past the end load zeros
+  // (an empty resource)
+  auto gather = [&](u32x4v (&raw)[4], int ti, auto s_c) {
+    constexpr int S = decltype(s_c)::value;
+    if (ti != g_ti) {
+      g_ti = ti;
+      const int t = t_begin + ti * Qx;
+      const bool tile_ok = ti < n_my;
+      p = t * 16 + i16;
+      pix_ok = tile_ok && p < src.P;
+      pj = p % src.W;
+      pi = (p / src.W) % src.H;
+      lo = t * 16 - halo > 0 ? t * 16 - halo : 0;
+      const int hi = t * 16 + 16 + halo < src.P ? t * 16 + 16 + halo : src.P;
+      rf = conv_rsrc((const _Float16*)src.f + (int64_t)(tile_ok ? lo : 0) * src.Cs * 4,
+                     tile_ok && hi > lo ? (uint32_t)((int64_t)(hi - lo) * src.Cs * 8) : 0u);
+    }
+    const int c = (int)(kst[S] & 0xFFFFu);
+    const int ua = (int)((kst[S] >> 16) & 7u), ub = (int)((kst[S] >> 19) & 7u);
+    const bool lv = (kst[S] >> 22) & 1u;
+    const uint32_t base = (uint32_t)(((p - lo) * src.Cs + c) * 8);
+    uint32_t off[4];
+    if (32 * (ks0 + S) < src.Cc) {
+      // centre step: channel pairs c + 2e of the pixel; pairs past Cs are zeros
+#pragma unroll
+      for (int e = 0; e < 4; ++e) off[e] = pix_ok && c + 2 * e < src.Cs ? base + 16 * e : OOB;
+    } else {
+      // orbit step: channels c, c + 1 of the four turned neighbours
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        int va, vb;
+        turn(ua, ub, jj, va, vb);
+        const bool in = (unsigned)(pi + va) < (unsigned)src.H && (unsigned)(pj + vb) < (unsigned)src.W;
+        off[jj] = pix_ok && lv && in ? base + (uint32_t)((va * src.W + vb) * src.Cs * 8) : OOB;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) raw[e] = __builtin_amdgcn_raw_buffer_load_b128(rf, off[e], 0, 0);
+  };
+
+  // butterfly of two channels' group vectors (a0..a3, b0..b3) into packed
+  // binary16 pairs (X0, X2, Xr, -Xi): X0, X2 from fp32 pair sums rounded
+  // once; Xr and -Xi = x1 - x3 from one packed subtraction
+  float one = 1.0f;
+  asm volatile("" : "+v"(one));
+  auto bfly = [&](const half8& w, uint32_t& o0, uint32_t& o2, uint32_t& orr, uint32_t& oi) {
+    const float sa = __builtin_fmaf((float)w[0], one, (float)w[2]);
+    const float ta = __builtin_fmaf((float)w[1], one, (float)w[3]);
+    const float sb = __builtin_fmaf((float)w[4], one, (float)w[6]);
+    const float tb = __builtin_fmaf((float)w[5], one, (float)w[7]);
+    o0 = pack2h(sa + ta, sb + tb);
+    o2 = pack2h(sa - ta, sb - tb);
+    const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};
+    const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};
+    const f16x2 da = a01 - a23, db = b01 - b23;
+    orr = __builtin_bit_cast(uint32_t, f16x2{da[0], db[0]});
+    oi = __builtin_bit_cast(uint32_t, f16x2{da[1], db[1]});
+  };
+
+  struct Frag {
+    half8 x0, x2, xr, xn;
+  };
+  // group DFT of step S's loads into the four B fragments
+  auto transform = [&](const u32x4v (&raw)[4], auto s_c) {
+    constexpr int S = decltype(s_c)::value;
+    u32x4v v0, v2, vr, vi;
+    if (32 * (ks0 + S) < src.Cc) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t t0, t2, tr, tq;
+        bfly(__builtin_bit_cast(half8, raw[e]), t0, t2, tr, tq);
+        v0[e] = t0;
+        v2[e] = t2;
+        vr[e] = tr;
+        vi[e] = tq;
+      }
+    } else {
+      // orbit step: patch channels (c, e = 0..3), (c + 1, e = 0..3); the
+      // group vector of (ch, e) over the turns jj is neighbour jj's value
+      // (jj + e) mod 4 of channel c + ch
+      const half8 L0 = __builtin_bit_cast(half8, raw[0]), L1 = __builtin_bit_cast(half8, raw[1]);
+      const half8 L2 = __builtin_bit_cast(half8, raw[2]), L3 = __builtin_bit_cast(half8, raw[3]);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int ch = e2 >> 1, ea = 2 * (e2 & 1), eb = ea + 1;
+        half8 wv;
+        wv[0] = L0[4 * ch + ((0 + ea) & 3)];
+        wv[1] = L1[4 * ch + ((1 + ea) & 3)];
+        wv[2] = L2[4 * ch + ((2 + ea) & 3)];
+        wv[3] = L3[4 * ch + ((3 + ea) & 3)];
+        wv[4] = L0[4 * ch + ((0 + eb) & 3)];
+        wv[5] = L1[4 * ch + ((1 + eb) & 3)];
+        wv[6] = L2[4 * ch + ((2 + eb) & 3)];
+        wv[7] = L3[4 * ch + ((3 + eb) & 3)];
+        uint32_t t0, t2, tr, tq;
+        bfly(wv, t0, t2, tr, tq);
+        v0[e2] = t0;
+        v2[e2] = t2;
+        vr[e2] = tr;
+        vi[e2] = tq;
+      }
+    }
+    Frag F;
+    F.x0 = __builtin_bit_cast(half8, v0);
+    F.x2 = __builtin_bit_cast(half8, v2);
+    F.xr = __builtin_bit_cast(half8, vr);
+    F.xn = __builtin_bit_cast(half8, vi);
+    return F;
+  };
+
+  struct Acc {
+    f32x4 c0[NB], c2[NB], cr[NB], cq[NB], ci[NB], cn[NB];
+  };
+  Acc acc;
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      acc.c0[nb] = acc.c2[nb] = acc.cr[nb] = acc.cq[nb] = acc.ci[nb] = acc.cn[nb] = f32x4{};
+  };
+
+  // products of step S
+  auto products = [&](const Frag& F, auto s_c) {
+    constexpr int S = decltype(s_c)::value;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc.c0[nb] = mma16(w0[nb][S], F.x0, acc.c0[nb]);
+      acc.cr[nb] = mma16(wr[nb][S], F.xr, acc.cr[nb]);
+      acc.c2[nb] = mma16(w2[nb][S], F.x2, acc.c2[nb]);
+      acc.ci[nb] = mma16(wi[nb][S], F.xr, acc.ci[nb]);
+      acc.cq[nb] = mma16(wi[nb][S], F.xn, acc.cq[nb]);
+      acc.cn[nb] = mma16(wr[nb][S], F.xn, acc.cn[nb]);
+    }
+  };
+
+  // end of a tile: combine the four waves' partial spectra; wave nb < NB
+  // finishes channel block nb
+  auto finish = [&](int ti) {
+    f32x4* const buf = red + (ti & 1) * RED;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4* const q = buf + ((wave * NB + nb) * 4) * 64 + lane;
+      q[0 * 64] = acc.c0[nb];
+      q[1 * 64] = acc.c2[nb];
+      q[2 * 64] = acc.cr[nb] + acc.cq[nb];
+      q[3 * 64] = acc.ci[nb] - acc.cn[nb];
+    }
+    zero_acc();
+    __syncthreads();
+    if (wave < NB) {
+      const int nb = wave;
+      f32x4 Y[4];
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl) {
+        Y[pl] = buf[((0 * NB + nb) * 4 + pl) * 64 + lane];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) Y[pl] += buf[((ww * NB + nb) * 4 + pl) * 64 + lane];
+      }
+      // lane (i16, g), register r: output channel d0 + 16nb + 4g + r, pixel
+      // 16t + i16; the four channels' group vectors are 32 contiguous bytes
+      const int t = t_begin + ti * Qx;
+      const int px = t * 16 + i16;
+      const int col = d0 + nb * 16 + 4 * g;
+      if (px < src.P && col < n_out) {
+        uint32_t o[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float b = bias[col + r];
+          const float u = __builtin_fmaf(Y[0][r], 0.25f, b);
+          const float pp = __builtin_fmaf(Y[1][r], 0.25f, u);
+          const float mm = __builtin_fmaf(Y[1][r], -0.25f, u);
+          float v0 = __builtin_fmaf(Y[2][r], 0.5f, pp), v1 = __builtin_fmaf(Y[3][r], -0.5f, mm);
+          float v2 = __builtin_fmaf(Y[2][r], -0.5f, pp), v3 = __builtin_fmaf(Y[3][r], 0.5f, mm);
+          v0 = activate(v0, act);
+          v1 = activate(v1, act);
+          v2 = activate(v2, act);
+          v3 = activate(v3, act);
+          o[2 * r] = pack2h(v0, v1);
+          o[2 * r + 1] = pack2h(v2, v3);
+        }
+        u32x4v* const dst = reinterpret_cast<u32x4v*>(y + ((int64_t)px * n_out + col) * 4);
+        dst[0] = u32x4v{o[0], o[1], o[2], o[3]};
+        dst[1] = u32x4v{o[4], o[5], o[6], o[7]};
+      }
+    }
+  };
+
+  // Software pipeline over this wave's items (tile-major, CNT steps per
+  // tile, CNT = cnt fixed at compile time): the products of item i are
+  // issued before the butterfly of item i + 1, so the matrix cores work
+  // while the same wave runs the butterfly's VALU instructions; loads run
+  // two items ahead.  Before item i: F holds its fragments, ring[(i+1)%2]
+  // the loads of item i+1 and ring[i%2] those of item i+2.  Tiles are
+  // unrolled in pairs so that every ring slot and step index is a
+  // compile-time index.
+  auto run = [&](auto cnt_c) {
+    constexpr int CNT = decltype(cnt_c)::value;
+    typedef std::integral_constant<int, 0> s0_t;
+    typedef std::integral_constant<int, 1 % CNT> s1_t;
+    typedef std::integral_constant<int, 2 % CNT> s2_t;
+    zero_acc();
+    u32x4v ring[2][4];
+    gather(ring[0], 0, s0_t{});
+    gather(ring[1], 1 / CNT, s1_t{});
+    Frag F = transform(ring[0], s0_t{});
+    gather(ring[0], 2 / CNT, s2_t{});
+    auto body = [&](int ti, auto par_c) {
+      constexpr int PAR = decltype(par_c)::value;
+      static_for<CNT>([&](auto s_c) {
+        constexpr int S = decltype(s_c)::value;
+        constexpr int I = PAR * CNT + S;  // item index mod 2
+        products(F, s_c);
+        F = transform(ring[(I + 1) % 2], std::integral_constant<int, (S + 1) % CNT>{});
+        if (S == CNT - 1) finish(ti);
+        gather(ring[(I + 1) % 2], ti + (S + 3) / CNT, std::integral_constant<int, (S + 3) % CNT>{});
+      });
+    };
+    for (int ti = 0; ti < n_my; ti += 2) {
+      body(ti, std::integral_constant<int, 0>{});
+      if (ti + 1 < n_my) body(ti + 1, std::integral_constant<int, 1>{});
+    }
+  };
+  if (cnt == KSW)
+    run(std::integral_constant<int, KSW>{});
+  else
+    run(std::integral_constant<int, (KSW > 1 ? KSW - 1 : 1)>{});
+}
+
+template <int NB, int KSW>
+static hipError_t launch_rd_t(const PatchSrc& src, const _Float16* spec, const float* bias,
+                              _Float16* out, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
+  const int KS = (src.K + 31) / 32;
+  const int n_ranges = (n_out + NB * 16 - 1) / (NB * 16);
+  const int n_tiles = (src.P + 15) / 16;
+  const int per = (n_tiles + 7) / 8;
+  const int Qx = per < 32 ? per : 32;  // workers per XCD and channel range
+  const int64_t grid = (int64_t)8 * Qx * n_ranges;
+  hipLaunchKernelGGL((k_conv_rd_f16<NB, KSW>), dim3((unsigned)grid), dim3(256), 0, s, src, spec, bias,
+                     out, KS, k_pad, n_out, n_pad, n_ranges, n_tiles, Qx, act);
+  return hipGetLastError();
+}
+
+// Register-direct kernel when the steps of a wave fit its weight registers
+// (at least four reduction steps, at most 24); hipErrorNotSupported
+// otherwise.  A wave takes ceil(KS/4) or floor(KS/4) steps.
+static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const float* bias,
+                            _Float16* out, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
+  const char* env = getenv("EQL_CONV_RD");
+  if (env != nullptr && atoi(env) == 0) return hipErrorNotSupported;
+  const int KS = (src.K + 31) / 32;
+  const int ksw = (KS + 3) / 4;
+  switch (KS < 4 ? 0 : ksw) {
+    case 1: return launch_rd_t<3, 1>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 2: return launch_rd_t<3, 2>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 3: return launch_rd_t<3, 3>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 4: return launch_rd_t<3, 4>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 5: return launch_rd_t<2, 5>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 6: return launch_rd_t<2, 6>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -484,13 +901,19 @@ hipError_t launch_conv(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs,
                        const void* spec, const float* bias, void* out, int k_pad, int n_out,
                        int n_pad, int act, hipStream_t s) {
   if (P <= 0) return hipSuccess;
-  PatchSrc src{f, H, W, Cs, k / 2, k * k * Cs, (int)P};
+  PatchSrc src{f, H, W, Cs, k / 2, centre_width(Cs), patch_width(Cs, k), (int)P};
   int cfg = n_out <= 64 ? 0 : 1;
   const char* env = getenv("EQL_CONV_TILE");
   if (env != nullptr && *env) cfg = atoi(env);
-  if (dt == EQL_F16)
+  if (dt == EQL_F16) {
+    if (env == nullptr || !*env) {
+      const hipError_t e =
+          launch_rd(src, (const _Float16*)spec, bias, (_Float16*)out, k_pad, n_out, n_pad, act, s);
+      if (e != hipErrorNotSupported) return e;
+    }
     return launch_conv_cfg<_Float16>(cfg, src, (const _Float16*)spec, bias, (_Float16*)out, k_pad,
                                      n_out, n_pad, act, s);
+  }
   return launch_conv_cfg<float>(cfg, src, (const float*)spec, bias, (float*)out, k_pad, n_out, n_pad,
                                 act, s);
 }
@@ -498,7 +921,7 @@ hipError_t launch_conv(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs,
 hipError_t launch_conv_gather(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs, int k,
                               int64_t P, void* xp, hipStream_t s) {
   if (P <= 0) return hipSuccess;
-  PatchSrc src{f, H, W, Cs, k / 2, k * k * Cs, (int)P};
+  PatchSrc src{f, H, W, Cs, k / 2, centre_width(Cs), patch_width(Cs, k), (int)P};
   const int64_t n = P * ((src.K + 3) / 4);
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (dt == EQL_F16)
@@ -510,7 +933,7 @@ hipError_t launch_conv_gather(eqlinear_dtype_t dt, const void* f, int H, int W, 
 
 hipError_t launch_conv_patch_weights(eqlinear_dtype_t dt, const void* psi, void* wf, void* wa,
                                      int C, int D, int k, hipStream_t s) {
-  const int64_t n = (int64_t)D * C * k * k * 4;
+  const int64_t n = ((int64_t)D * patch_width(C, k) + (int64_t)C * patch_width(D, k)) * 4;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (dt == EQL_F16)
     hipLaunchKernelGGL(k_conv_patch_weights<_Float16>, dim3(blocks), dim3(256), 0, s,

@@ -58,9 +58,10 @@ typedef struct eqconv_plan* eqconv_plan_t; /* opaque */
 
 /* Create a plan for C input and D output channels per group element and an
  * odd kernel size k (1 <= k <= 7).  C and D must be multiples of 4 (a gather
- * of four patch channels reads four whole group vectors) and k*k*max(C, D)
- * at most 65536; otherwise EQL_ERR_UNSUPPORTED (k even or out of range,
- * channel counts) or EQL_ERR_INVALID_ARG (C, D <= 0, out == NULL).
+ * of four patch channels reads four whole group vectors), and the patch
+ * width of each (the channel count rounded up to 32, plus k^2 - 1 times the
+ * channel count) at most 65536; otherwise EQL_ERR_UNSUPPORTED (k even or out
+ * of range, channel counts) or EQL_ERR_INVALID_ARG (C, D <= 0, out == NULL).
  * Host-only: allocates no device memory. */
 eqlinear_status_t eqconv_plan_create(int64_t C, int64_t D, int64_t k, eqlinear_dtype_t dtype,
                                      eqconv_plan_t* out);
@@ -97,8 +98,8 @@ eqlinear_status_t eqconv_backward_input(eqconv_plan_t plan, const void* dy, void
                                         int64_t H, int64_t W, void* stream);
 
 /* Bytes of device workspace eqconv_backward_weight needs (0 for an invalid
- * plan or size): the patches of f (N*H*W*k*k*C*4 elements of the plan
- * dtype), the EQ-Linear weight-gradient workspace of the patch layer and
+ * plan or size): the patches of f (N*H*W times the patch width times 4
+ * elements of the plan dtype), the EQ-Linear weight-gradient workspace of the patch layer and
  * the patch-weight gradient (binary32). */
 size_t eqconv_backward_weight_workspace(eqconv_plan_t plan, int64_t N, int64_t H, int64_t W);
 

@@ -20,9 +20,12 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-# (N, H, W, C, D, k): pixel counts off the 64-row tile, output widths on both
-# tile shapes (D <= 64 and D > 64), patch widths of several chunks with a
-# ragged last one, kernel sizes 1, 3 and 5, non-square images
+# (N, H, W, C, D, k): pixel counts off the 16- and 64-pixel tiles, output
+# widths on both LDS tile shapes (D <= 64 and D > 64), patch widths of
+# several steps with a ragged last one, kernel sizes 1, 3 and 5, non-square
+# images.  Patch widths of 4 to 24 reduction steps run the register-direct
+# binary16 kernel (every variant of it: 1 to 6 steps per wave, three or two
+# channel blocks per work-group); the others the LDS-tiled one.
 SHAPES = [
     (2, 7, 9, 8, 12, 3),
     (1, 13, 11, 4, 68, 3),
@@ -30,6 +33,10 @@ SHAPES = [
     (3, 4, 4, 12, 4, 1),
     (1, 20, 20, 32, 40, 3),
     (1, 9, 12, 20, 132, 3),
+    (1, 10, 9, 64, 40, 3),
+    (1, 6, 7, 128, 20, 3),
+    (1, 7, 6, 12, 24, 3),
+    (1, 5, 6, 80, 16, 3),
 ]
 
 
