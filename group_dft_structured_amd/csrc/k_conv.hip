@@ -538,7 +538,10 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     const PatchSrc src, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int KS, int k_pad, int n_out, int n_pad, int n_ranges, int n_tiles,
     int Qx, int act) {
-  constexpr int RED = 4 * NB * 4 * 64;  // f32x4 per partial buffer: wave x block x plane x lane
+  // partial spectra of every wave: wave x block x plane x lane (f32x4),
+  // double buffered
+  constexpr int WAVES = 4;
+  constexpr int RED = WAVES * NB * 4 * 64;
   __shared__ __attribute__((aligned(16))) f32x4 red[2 * RED];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
 
   // this wave's reduction steps [ks0, ks0 + cnt), cnt >= 1 (the host
   // launches this kernel for four steps or more)
-  const int ks0 = KS * wave / 4, cnt = KS * (wave + 1) / 4 - ks0;
+  const int ks0 = KS * wave / WAVES, cnt = KS * (wave + 1) / WAVES - ks0;
   const int d0 = j * NB * 16;
 
   // weight fragments: channel d0 + 16nb + i16, patch channels 32s + 8g .. + 7
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
   };
 
   struct Frag {
-    half8 x0, x2, xr, xn;
+    half8 x0, x2, xr, xn, xi;  // xn = -Xi, xi = Xi
   };
   // group DFT of step S's loads into the four B fragments
   auto transform = [&](const u32x4v (&raw)[4], auto s_c) {
@@ -718,17 +721,19 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     F.x2 = __builtin_bit_cast(half8, v2);
     F.xr = __builtin_bit_cast(half8, vr);
     F.xn = __builtin_bit_cast(half8, vi);
+    F.xi = __builtin_bit_cast(half8, vi ^ 0x80008000u);
     return F;
   };
 
+  // four accumulators per block: Y0, Y2, Yr = Wr Xr + Wi (-Xi) and
+  // Yi = Wi Xr + Wr Xi; the two products into Yr (and Yi) are issued apart
   struct Acc {
-    f32x4 c0[NB], c2[NB], cr[NB], cq[NB], ci[NB], cn[NB];
+    f32x4 c0[NB], c2[NB], cr[NB], ci[NB];
   };
   Acc acc;
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc.c0[nb] = acc.c2[nb] = acc.cr[nb] = acc.cq[nb] = acc.ci[nb] = acc.cn[nb] = f32x4{};
+    for (int nb = 0; nb < NB; ++nb) acc.c0[nb] = acc.c2[nb] = acc.cr[nb] = acc.ci[nb] = f32x4{};
   };
 
   // products of step S
@@ -740,12 +745,15 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       acc.cr[nb] = mma16(wr[nb][S], F.xr, acc.cr[nb]);
       acc.c2[nb] = mma16(w2[nb][S], F.x2, acc.c2[nb]);
       acc.ci[nb] = mma16(wi[nb][S], F.xr, acc.ci[nb]);
-      acc.cq[nb] = mma16(wi[nb][S], F.xn, acc.cq[nb]);
-      acc.cn[nb] = mma16(wr[nb][S], F.xn, acc.cn[nb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc.cr[nb] = mma16(wi[nb][S], F.xn, acc.cr[nb]);
+      acc.ci[nb] = mma16(wr[nb][S], F.xi, acc.ci[nb]);
     }
   };
 
-  // end of a tile: combine the four waves' partial spectra; wave nb < NB
+  // end of a tile: combine the waves' partial spectra; wave nb < NB
   // finishes channel block nb
   auto finish = [&](int ti) {
     f32x4* const buf = red + (ti & 1) * RED;
@@ -754,8 +762,8 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       f32x4* const q = buf + ((wave * NB + nb) * 4) * 64 + lane;
       q[0 * 64] = acc.c0[nb];
       q[1 * 64] = acc.c2[nb];
-      q[2 * 64] = acc.cr[nb] + acc.cq[nb];
-      q[3 * 64] = acc.ci[nb] - acc.cn[nb];
+      q[2 * 64] = acc.cr[nb];
+      q[3 * 64] = acc.ci[nb];
     }
     zero_acc();
     __syncthreads();
@@ -766,7 +774,7 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       for (int pl = 0; pl < 4; ++pl) {
         Y[pl] = buf[((0 * NB + nb) * 4 + pl) * 64 + lane];
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) Y[pl] += buf[((ww * NB + nb) * 4 + pl) * 64 + lane];
+        for (int ww = 1; ww < WAVES; ++ww) Y[pl] += buf[((ww * NB + nb) * 4 + pl) * 64 + lane];
       }
       // lane (i16, g), register r: output channel d0 + 16nb + 4g + r, pixel
       // 16t + i16; the four channels' group vectors are 32 contiguous bytes
@@ -860,8 +868,11 @@ static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const flo
   const char* env = getenv("EQL_CONV_RD");
   if (env != nullptr && atoi(env) == 0) return hipErrorNotSupported;
   const int KS = (src.K + 31) / 32;
-  const int ksw = (KS + 3) / 4;
-  switch (KS < 4 ? 0 : ksw) {
+  if (KS < 4) return hipErrorNotSupported;
+  // Eight waves (two per SIMD, fewer weight registers each) measured 7x
+  // slower at the 448-channel patch width: the compiler spills to scratch
+  // within 256 registers.  Four waves, one per SIMD.
+  switch ((KS + 3) / 4) {
     case 1: return launch_rd_t<3, 1>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
     case 2: return launch_rd_t<3, 2>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
     case 3: return launch_rd_t<3, 3>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
