@@ -1,4 +1,4 @@
-"""The layer's calls captured in a HIP graph and replayed.
+"""The layer's calls (and the group convolution's) captured in a HIP graph and replayed.
 
 Every call is stream-ordered, allocates nothing after the plan's first
 set_weight and records no memset, so it can be captured.  Each case captures
@@ -91,5 +91,72 @@ def test_graph_replays_match_eager(C, D, N, T, group, dtype):
         plan.set_weight(W2, b)
         plan.forward(other)
         plan.set_weight(W, b)
+        torch.cuda.synchronize()
+    plan.close()
+
+
+CONV_CASES = [
+    # (N, H, W, C, D, k, dtype): the register-direct binary16 kernel, the
+    # LDS-tiled binary32 one
+    (2, 12, 10, 48, 48, 3, "f16"),
+    (1, 9, 11, 8, 12, 3, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,H,W,C,D,k,dtype", CONV_CASES)
+def test_conv_graph_replays_match_eager(N, H, W, C, D, k, dtype):
+    """The convolution's calls captured in a graph and replayed between
+    eager work, bit-identical to eager and within the oracle bar."""
+    from group_dft_structured_amd import ConvPlan
+    from group_dft_structured_amd.workloads import make_conv_inputs
+    torch = torch_mod()
+    inp = make_conv_inputs(N, H, W, C, D, k, dtype=dtype, seed=52, bias=True, dy=True)
+    plan = ConvPlan(C, D, k, dtype)
+    psi, b = to_dev(inp["psi"]), to_dev(inp["bias"])
+    plan.set_weight(psi, b)
+    f, dy = to_dev(inp["f"]), to_dev(inp["dy"])
+    y = torch.empty((N, H, W, D, 4), dtype=f.dtype, device="cuda")
+    yg = torch.empty_like(y)
+    df = torch.empty_like(f)
+    dpsi = torch.empty((D, C, k, k, 4), dtype=torch.float32, device="cuda")
+    db = torch.empty((D,), dtype=torch.float32, device="cuda")
+    ws = torch.empty((plan.workspace_bytes(N, H, W),), dtype=torch.uint8, device="cuda")
+
+    def step(stream):
+        plan.forward(f, y, stream=stream)
+        plan.forward(f, yg, stream=stream, act="gelu")
+        plan.backward_input(dy, df, stream=stream)
+        plan.backward_weight(f, dy, dpsi, db, ws, stream=stream)
+
+    step(None)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (y, yg, df, dpsi, db)]
+    refs = [oracle.conv_forward(inp["f"], inp["psi"], inp["bias"]),
+            oracle.conv_forward_act(inp["f"], inp["psi"], inp["bias"], "gelu"),
+            oracle.conv_backward_input(inp["dy"], inp["psi"]),
+            *oracle.conv_backward_weight(inp["f"], inp["dy"], k)]
+    for name, got, ref in zip(("y", "gelu", "df", "dpsi", "dbias"), eager, refs):
+        assert rel_err(to_np64(got), ref) <= TOL[dtype], name
+
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step(s)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+    other = torch.randn_like(f.float()).to(f.dtype)
+    psi2 = (psi.float() * 0.5).to(psi.dtype)
+    for rep in range(4):
+        for t in (y, yg, df, dpsi, db):
+            t.fill_(7)
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("y", "gelu", "df", "dpsi", "dbias"), (y, yg, df, dpsi, db), eager):
+            assert torch.equal(got, ref), (rep, name)
+        plan.forward(other, torch.empty_like(y))
+        plan.set_weight(psi2, b)
+        plan.forward(other)
+        plan.set_weight(psi, b)
         torch.cuda.synchronize()
     plan.close()
