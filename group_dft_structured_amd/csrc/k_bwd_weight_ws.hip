@@ -338,8 +338,13 @@ static const BwsCfg kBwsCfgs[] = {
 
 bool bws_supported(const eqlinear_plan* p) {
   if (env_int("EQL_NO_BWS", 0) || p->dtype != EQL_F16) return false;
-  // whole column pairs (16-byte units) and one column tile of at most 96
-  return p->C % 2 == 0 && p->D % 2 == 0 && p->C <= 96;
+  // whole column pairs (16-byte units), column tiles of 96.  Wider layers
+  // re-read dy once per column tile and still beat the symmetric
+  // matrix-core kernel (measured on MI355X, binary16: 168 -> 45 us at
+  // N = 12608, C = 192, D = 384; 5252 -> 911 us at N = 200704, C = 192,
+  // D = 768; 1527 -> 496 us for the 448-channel patch layer of the 3 x 3
+  // group convolution at 64 x 56 x 56, C = D = 48)
+  return p->C % 2 == 0 && p->D % 2 == 0;
 }
 
 static int bws_sel() {
