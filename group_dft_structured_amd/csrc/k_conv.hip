@@ -533,11 +533,16 @@ __device__ __forceinline__ uint32_t pack2h(float a, float b) {
 
 }  // namespace
 
+// First reduction step of each of the four waves (and the step count).
+struct WaveSplit {
+  int start[5];
+};
+
 template <int NB, int KSW>
 __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     const PatchSrc src, const _Float16* __restrict__ spec, const float* __restrict__ bias,
-    _Float16* __restrict__ y, int KS, int k_pad, int n_out, int n_pad, int n_ranges, int n_tiles,
-    int Qx, int act) {
+    _Float16* __restrict__ y, const WaveSplit split, int k_pad, int n_out, int n_pad, int n_ranges,
+    int n_tiles, int Qx, int act) {
   // partial spectra of every wave: wave x block x plane x lane (f32x4),
   // double buffered
   constexpr int WAVES = 4;
@@ -558,9 +563,9 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
   const int n_my = t_begin < t_end ? (t_end - t_begin - 1) / Qx + 1 : 0;
   if (n_my == 0) return;  // whole work-group
 
-  // this wave's reduction steps [ks0, ks0 + cnt), cnt >= 1 (the host
-  // launches this kernel for four steps or more)
-  const int ks0 = KS * wave / WAVES, cnt = KS * (wave + 1) / WAVES - ks0;
+  // this wave's reduction steps [ks0, ks0 + cnt), 1 <= cnt <= KSW (host
+  // split; the waves that finish channel blocks may take fewer)
+  const int ks0 = split.start[wave], cnt = split.start[wave + 1] - ks0;
   const int d0 = j * NB * 16;
 
   // weight fragments: channel d0 + 16nb + i16, patch channels 32s + 8g .. + 7
@@ -840,10 +845,9 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       if (ti + 1 < n_my) body(ti + 1, std::integral_constant<int, 1>{});
     }
   };
-  if (cnt == KSW)
-    run(std::integral_constant<int, KSW>{});
-  else
-    run(std::integral_constant<int, (KSW > 1 ? KSW - 1 : 1)>{});
+  static_for<KSW>([&](auto c_c) {
+    if (cnt == decltype(c_c)::value + 1) run(std::integral_constant<int, decltype(c_c)::value + 1>{});
+  });
 }
 
 template <int NB, int KSW>
@@ -855,8 +859,29 @@ static hipError_t launch_rd_t(const PatchSrc& src, const _Float16* spec, const f
   const int per = (n_tiles + 7) / 8;
   const int Qx = per < 32 ? per : 32;  // workers per XCD and channel range
   const int64_t grid = (int64_t)8 * Qx * n_ranges;
+  // Steps per wave.  With three channel blocks the fourth wave finishes no
+  // block at the end of a tile, so it takes up to KSW steps and the three
+  // that do share the rest; otherwise the steps are split evenly.
+  WaveSplit sp;
+  const int rest_waves = 4 - NB;
+  int tail = 0;
+  if (NB == 3) tail = KSW < KS - 3 ? KSW : KS - 3;
+  const int head = KS - rest_waves * tail;  // steps of the NB finishing waves
+  int k = 0;
+  for (int w = 0; w < 4; ++w) {
+    sp.start[w] = k;
+    if (NB == 3)
+      k += w < NB ? head * (w + 1) / NB - head * w / NB : tail;
+    else
+      k = KS * (w + 1) / 4;
+  }
+  sp.start[4] = k;
+  for (int w = 0; w < 4; ++w) {
+    const int c = sp.start[w + 1] - sp.start[w];
+    if (c < 1 || c > KSW) return hipErrorNotSupported;
+  }
   hipLaunchKernelGGL((k_conv_rd_f16<NB, KSW>), dim3((unsigned)grid), dim3(256), 0, s, src, spec, bias,
-                     out, KS, k_pad, n_out, n_pad, n_ranges, n_tiles, Qx, act);
+                     out, sp, k_pad, n_out, n_pad, n_ranges, n_tiles, Qx, act);
   return hipGetLastError();
 }
 
@@ -872,11 +897,13 @@ static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const flo
   // Eight waves (two per SIMD, fewer weight registers each) measured 7x
   // slower at the 448-channel patch width: the compiler spills to scratch
   // within 256 registers.  Four waves, one per SIMD.
+  // three channel blocks up to 16 steps, with one step more for the wave
+  // that finishes no block; two blocks and an even split up to 24
   switch ((KS + 3) / 4) {
-    case 1: return launch_rd_t<3, 1>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 2: return launch_rd_t<3, 2>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 3: return launch_rd_t<3, 3>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 4: return launch_rd_t<3, 4>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 1: return launch_rd_t<3, 2>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 2: return launch_rd_t<3, 3>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 3: return launch_rd_t<3, 4>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 4: return launch_rd_t<3, 5>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
     case 5: return launch_rd_t<2, 5>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
     case 6: return launch_rd_t<2, 6>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
     default: return hipErrorNotSupported;
