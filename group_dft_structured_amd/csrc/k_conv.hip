@@ -910,6 +910,72 @@ static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const flo
   }
 }
 
+// Patches of a binary16 field written out, x'[P][K][4], one thread per
+// (pixel, 8 patch channels): the four 16-byte loads of the register-direct
+// kernel's gather and four 16-byte stores.
+__global__ __launch_bounds__(256) void k_conv_gather8_f16(const PatchSrc src,
+                                                          _Float16* __restrict__ xp) {
+  const int units = src.K / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)src.P * units) return;
+  const int p = (int)(i / units);
+  const int cp = (int)(i - (int64_t)p * units) * 8;
+  const int halo = src.h * src.W + src.h;
+  const int lo = p - halo > 0 ? p - halo : 0;
+  const int hi = p + 1 + halo < src.P ? p + 1 + halo : src.P;
+  const __amdgpu_buffer_rsrc_t r = conv_rsrc((const _Float16*)src.f + (int64_t)lo * src.Cs * 4,
+                                             (uint32_t)((int64_t)(hi - lo) * src.Cs * 8));
+  const bool centre = cp < src.Cc;
+  uint32_t off[4];
+  if (centre) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      off[e] = cp + 2 * e < src.Cs ? (uint32_t)(((p - lo) * src.Cs + cp + 2 * e) * 8) : OOB;
+  } else {
+    const int rem = cp - src.Cc;
+    const int o = rem / (4 * src.Cs);
+    const int c = (rem - o * 4 * src.Cs) >> 2;
+    int ua, ub;
+    orbit_rep(o, src.h, ua, ub);
+    const int pj = p % src.W, pi = (p / src.W) % src.H;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      int va, vb;
+      turn(ua, ub, jj, va, vb);
+      const bool in = (unsigned)(pi + va) < (unsigned)src.H && (unsigned)(pj + vb) < (unsigned)src.W;
+      off[jj] = in ? (uint32_t)(((p + va * src.W + vb - lo) * src.Cs + c) * 8) : OOB;
+    }
+  }
+  u32x4v raw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) raw[e] = __builtin_amdgcn_raw_buffer_load_b128(r, off[e], 0, 0);
+  u32x4v* const dst = reinterpret_cast<u32x4v*>(xp + ((int64_t)p * src.K + cp) * 4);
+  if (centre) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = raw[e];
+    return;
+  }
+  // patch channels (c, e = 0..3), (c + 1, e = 0..3): the group vector of
+  // (ch, e) over the turns jj is neighbour jj's value (jj + e) mod 4 of
+  // channel c + ch
+  const half8 L0 = __builtin_bit_cast(half8, raw[0]), L1 = __builtin_bit_cast(half8, raw[1]);
+  const half8 L2 = __builtin_bit_cast(half8, raw[2]), L3 = __builtin_bit_cast(half8, raw[3]);
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const int ch = e2 >> 1, ea = 2 * (e2 & 1), eb = ea + 1;
+    half8 wv;
+    wv[0] = L0[4 * ch + ((0 + ea) & 3)];
+    wv[1] = L1[4 * ch + ((1 + ea) & 3)];
+    wv[2] = L2[4 * ch + ((2 + ea) & 3)];
+    wv[3] = L3[4 * ch + ((3 + ea) & 3)];
+    wv[4] = L0[4 * ch + ((0 + eb) & 3)];
+    wv[5] = L1[4 * ch + ((1 + eb) & 3)];
+    wv[6] = L2[4 * ch + ((2 + eb) & 3)];
+    wv[7] = L3[4 * ch + ((3 + eb) & 3)];
+    dst[e2] = __builtin_bit_cast(u32x4v, wv);
+  }
+}
+
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int WM_, int WN_>
 static hipError_t launch_conv_t(const PatchSrc& src, const T* spec, const float* bias, T* out,
@@ -962,9 +1028,11 @@ hipError_t launch_conv_gather(eqlinear_dtype_t dt, const void* f, int H, int W, 
   PatchSrc src{f, H, W, Cs, k / 2, centre_width(Cs), patch_width(Cs, k), (int)P};
   const int64_t n = P * ((src.K + 3) / 4);
   const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (dt == EQL_F16)
-    hipLaunchKernelGGL(k_conv_gather<_Float16>, dim3(blocks), dim3(256), 0, s, src, (_Float16*)xp);
-  else
+  if (dt == EQL_F16) {
+    const int64_t n8 = P * (src.K / 8);
+    hipLaunchKernelGGL(k_conv_gather8_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, src,
+                       (_Float16*)xp);
+  } else
     hipLaunchKernelGGL(k_conv_gather<float>, dim3(blocks), dim3(256), 0, s, src, (float*)xp);
   return hipGetLastError();
 }
