@@ -55,6 +55,9 @@ def parse_args():
                     help="time every workload/dtype pass and print one JSON line per pass")
     ap.add_argument("--configs", default=None,
                     help="with --all-configs: comma-separated workload names to time")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="print per-kernel matrix-core utilisation from a rocprofv3 --pmc run "
+                         "of MFMA_COUNTERS under DIR, then exit")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run found under DIR")
     return ap.parse_args()
@@ -105,6 +108,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload)
         return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
@@ -112,6 +118,8 @@ def main():
         copy_calibration()
         return
     if args.all_configs:
+        global EAGER
+        EAGER = args.no_graph
         all_configs(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -287,10 +295,24 @@ def main():
     plan.close()
 
 
+EAGER = False  # --no-graph with --all-configs: eager launches (counter collection)
+
+
 def time_graph(fn, stream, reps, replays):
     """Mean launch duration (us) of fn, from HIP events around replays of a
-    graph holding `reps` back-to-back launches."""
+    graph holding `reps` back-to-back launches (eager launches when EAGER)."""
     import torch
+    if EAGER:
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps * replays):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * replays)
     with torch.cuda.stream(stream):
         fn()
         torch.cuda.synchronize()
@@ -508,6 +530,42 @@ def summarize_counters(root, workload):
     for role, b in sorted(per_role.items()):
         lines.append(f"traffic_bytes_per_launch {workload}.{dtype}.{role} {b:.0f}")
     print("\n".join(lines))
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32")
+
+
+def summarize_mfma(root):
+    """Matrix-core utilisation per kernel from one rocprofv3 --pmc run of
+    MFMA_COUNTERS, averaged over the kernel's dispatches:
+    util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs), with
+    GRBM_GUI_ACTIVE summed over the 8 XCDs and 1024 SIMDs (256 CUs x 4), the
+    ratio rocprofv3's own MfmaUtil metric takes; MFMA flops = MOPS * 512."""
+    import collections
+    import csv
+    import glob
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] in MFMA_COUNTERS:
+                per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("# MFMA utilisation per kernel from rocprofv3 counters (MI355X)")
+    print(f"sources_sha256 all {kernel_sources_hash()}")
+    print(f"{'mfma_util':>9} {'mfma_gflop':>10} {'dispatch_us':>11} {'calls':>5}  kernel")
+    for k, c in sorted(per.items()):
+        if not c["GRBM_GUI_ACTIVE"] or "eql" not in k:
+            continue
+        avg = {n: sum(v) / len(v) for n, v in c.items()}
+        busy = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        gui = avg["GRBM_GUI_ACTIVE"] / 8.0
+        util = busy / (gui * 1024.0) if gui > 0 else 0.0
+        mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+        d = sorted(dur[k])[len(dur[k]) // 2]
+        print(f"{util:9.4f} {mops * 512 / 1e9:10.3f} {d:11.2f} {len(c['GRBM_GUI_ACTIVE']):5d}  {k[:100]}")
 
 
 def summarize_trace(root):
