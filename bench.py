@@ -374,6 +374,12 @@ def all_configs(args):
                 passes["backward_weight"] = (lambda: plan.backward_weight(t["x"], t["dy"], dW, db, ws),
                                              N * T * (C + D) * esz + 4 * D * C * T + 4 * D)
             big = N * (C + D) * T * esz > (1 << 30)
+            import oracle
+            rows = min(N, 2048)
+            cpu = oracle_rate(lambda: oracle.forward(inp["x"][:rows], inp["W"], inp.get("bias"),
+                                                     group=w.group),
+                              2.0 * real_products(T, w.group) * rows * C * D,
+                              f"oracle.forward (fp64 dense group matrix) on {rows} of the {N} rows")
             for name, (fn, nbytes) in passes.items():
                 us = time_graph(fn, stream, 3 if big else 20, 3 if big else 10)
                 tf = flops / (us * 1e-6) / 1e12
@@ -388,7 +394,8 @@ def all_configs(args):
                                   "tflops_dense_equiv": round(tf * T * T / real_products(T, w.group), 2),
                                   "mfma_peak_frac": round(tf / PEAK_MFMA_TFLOPS[dtype], 4),
                                   "hbm_gbps": round(gbps, 1), "alg_bytes": nbytes,
-                                  "roofline": {"bound": bound, "frac": round(frac, 4)}}),
+                                  "roofline": {"bound": bound, "frac": round(frac, 4)},
+                                  "cpu_oracle": cpu if name == "forward" else None}),
                       flush=True)
             plan.close()
             del t, passes
@@ -424,6 +431,7 @@ def all_configs_conv(w, dtype, stream, dev):
     P = w.N * w.H * w.W
     inp = make_conv_inputs(w.N, w.H, w.W, w.C, w.D, w.k, dtype=dtype, seed=0, bias=w.bias, dy=True)
     t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items() if v is not None}
+    inp_f1, psi_np, bias_np = inp["f"][:1].copy(), inp["psi"], inp["bias"]
     del inp
     plan = eq.ConvPlan(w.C, w.D, w.k, dtype)
     plan.set_weight(t["psi"], t.get("bias"))
@@ -442,9 +450,16 @@ def all_configs_conv(w, dtype, stream, dev):
         "backward_weight": (lambda: plan.backward_weight(t["f"], t["dy"], dpsi, db, ws),
                             io + 4 * w.k * w.k * w.C * w.D * 4 + 4 * w.D),
     }
+    import oracle
+    f1 = inp_f1
+    cpu = oracle_rate(lambda: oracle.conv_forward(f1, psi_np, bias_np),
+                      12.0 * w.k * w.k * w.C * w.D * w.H * w.W,
+                      f"oracle.conv_forward (fp64 dense tap matrices) on 1 of the {w.N} images")
     for name, (fn, nbytes) in passes.items():
         us = time_graph(fn, stream, 5, 5)
-        print(json.dumps(conv_pass_line(w, dtype, name, us, flops, nbytes)), flush=True)
+        line = conv_pass_line(w, dtype, name, us, flops, nbytes)
+        line["cpu_oracle"] = cpu if name == "forward" else None
+        print(json.dumps(line), flush=True)
     plan.close()
     del t, passes, ws
     torch.cuda.empty_cache()
@@ -587,17 +602,36 @@ WORKLOAD_DTYPE = {"vit_s_mlp": "f16", "vit_s_proj": "f16", "swin_stage": "f16", 
                   "vit_s_mlp_bwd": "f16"}
 
 
+def _blas_threads():
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        return int(max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"),
+                       default=1))
+    except Exception:  # noqa: BLE001
+        return os.cpu_count() or 1
+
+
+def oracle_rate(fn, flops, what, budget_s=1.0):
+    """The fp64 oracle timed beside a GPU line: fn() (one oracle forward on a
+    bounded sample of the workload) repeated within budget_s; its rate in the
+    method's actual flops of that sample."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(flops * reps / el / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"{what}, {reps} repetitions in {el:.2f} s"}
+
+
 def cpu_baseline(inp, flops_per_forward, N, budget_s):
     """The fp64 oracle's forward on the full batch, repeated within a time
     budget, on the host cores (BLAS threads reported)."""
     import oracle
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"),
-                    default=1)
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
+    cores = _blas_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.forward(inp["x"], inp["W"], inp["bias"])
