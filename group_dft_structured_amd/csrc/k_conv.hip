@@ -383,6 +383,218 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void k_conv_gemm(
   }
 }
 
+// Binary32 variant with 16x16x4 matrix-core steps: output tiles of 64
+// pixels x 16*NBN channels (NBN = 3 fits 48 channels exactly, where 32x32
+// steps would pad to 64), four waves of 16 pixels each.  Within a 16-channel
+// chunk the reduction index is permuted the same way for both operands: in
+// step s lane group g supplies channel 4g + s, so a lane reads its four
+// steps' operands as one 16-byte LDS read per plane.
+template <int NBN>
+__global__ __launch_bounds__(256) void k_conv_gemm32(
+    const PatchSrc src,
+    const float* __restrict__ spec,  // 4 planes [n_pad][k_pad]
+    const float* __restrict__ bias,  // [n_pad]
+    float* __restrict__ y,           // [P][n_out][4]
+    int k_pad, int n_out, int n_pad, int n_col_tiles, int n_tiles, int act) {
+  typedef float T;
+  constexpr int BM = 64, BN = 16 * NBN, NT = 256;
+  constexpr int BK = Tile<T>::BK, SK = Tile<T>::SK;  // 16 channels, 20-float rows
+  constexpr int A_PLANE = BM * SK, B_PLANE = BN * SK;
+  constexpr int TPR = BK / 4;                 // staging threads per row
+  constexpr int RPP = NT / TPR;               // rows per staging pass
+  constexpr int PASSES = (BM + RPP - 1) / RPP;
+  constexpr int UNITS = 4 * BN * 4;           // 16-byte weight units per chunk
+  constexpr int UPT = (UNITS + NT - 1) / NT;
+  static_assert(BK == 16 && SK % 4 == 0, "16-channel chunks, 16-byte aligned rows");
+
+  __shared__ __attribute__((aligned(16))) T lds[4 * A_PLANE + 4 * B_PLANE];
+  T* As = lds;
+  T* Bs = lds + 4 * A_PLANE;
+
+  const int per_xcd = (n_tiles + 7) / 8;
+  const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (tile >= n_tiles) return;
+  const int col_tile = tile % n_col_tiles;
+  const int row_tile = tile / n_col_tiles;
+  const int m0 = row_tile * BM;
+  const int n0 = col_tile * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, g = lane >> 4;
+  const int64_t plane = (int64_t)n_pad * k_pad;
+
+  const int halo = src.h * src.W + src.h;
+  const int pix0 = m0 - halo > 0 ? m0 - halo : 0;
+  const int pix1 = m0 + BM + halo < src.P ? m0 + BM + halo : src.P;
+  const __amdgpu_buffer_rsrc_t rf =
+      conv_rsrc((const T*)src.f + (int64_t)pix0 * src.Cs * 4,
+                (uint32_t)((int64_t)(pix1 - pix0) * src.Cs * 4 * (int)sizeof(T)));
+
+  const int cg = (tid % TPR) * 4;
+  int pix[PASSES], pi[PASSES], pj[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int row = ps * RPP + tid / TPR;
+    const int m = m0 + row;
+    const bool ok = row < BM && m < src.P;
+    pix[ps] = ok ? m : -1;
+    pj[ps] = ok ? m % src.W : 0;
+    pi[ps] = ok ? (m / src.W) % src.H : 0;
+  }
+
+  PatchQuads<T> qa[PASSES];
+  u32x4v qb[UPT];
+  int mode = 2;
+  auto load_chunk = [&](int k0) {
+    int c = 0, ua = 0, ub = 0;
+    patch_mode<T>(src, k0 + cg, mode, c, ua, ub);
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+      qa[ps] = patch_load<T>(src, rf, pix0, pix[ps], pi[ps], pj[ps], mode, c, ua, ub);
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = i * NT + tid;
+      qb[i] = u32x4v{};
+      if (UNITS % NT == 0 || u < UNITS) {
+        const int p = u / (BN * 4), rem = u % (BN * 4);
+        const int j = rem / 4, q = rem % 4;
+        // output tiles of 48 channels can reach past the padded planes
+        if (n0 + j < n_pad)
+          qb[i] = *reinterpret_cast<const u32x4v*>(spec + p * plane + (int64_t)(n0 + j) * k_pad + k0 +
+                                                   q * 4);
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+    typedef typename Elem<T>::quad Q;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int row = ps * RPP + tid / TPR;
+      if (BM % RPP != 0 && row >= BM) break;
+      T o0[4], o2[4], orr[4], oi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const floatx4 v = patch_vector<T>(qa[ps], mode, e);
+        const Spec4 sp = dft4(v[0], v[1], v[2], v[3]);
+        o0[e] = sp.f0;
+        o2[e] = sp.f2;
+        orr[e] = sp.fr;
+        oi[e] = sp.fi;
+      }
+      T* d = As + row * SK + cg;
+      *reinterpret_cast<Q*>(d + 0 * A_PLANE) = Q{o0[0], o0[1], o0[2], o0[3]};
+      *reinterpret_cast<Q*>(d + 1 * A_PLANE) = Q{o2[0], o2[1], o2[2], o2[3]};
+      *reinterpret_cast<Q*>(d + 2 * A_PLANE) = Q{orr[0], orr[1], orr[2], orr[3]};
+      *reinterpret_cast<Q*>(d + 3 * A_PLANE) = Q{oi[0], oi[1], oi[2], oi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = i * NT + tid;
+      if (UNITS % NT == 0 || u < UNITS) {
+        const int p = u / (BN * 4), rem = u % (BN * 4);
+        const int j = rem / 4, q = rem % 4;
+        *reinterpret_cast<u32x4v*>(Bs + p * B_PLANE + j * SK + q * 4) = qb[i];
+      }
+    }
+  };
+
+  // acc[nb][plane]: lane (i16, g) register r is pixel m0 + 16 wave + 4g + r,
+  // channel n0 + 16nb + i16 (16x16x4 result layout)
+  floatx4 acc[NBN][4];
+#pragma unroll
+  for (int nb = 0; nb < NBN; ++nb)
+#pragma unroll
+    for (int pl = 0; pl < 4; ++pl) acc[nb][pl] = floatx4{};
+
+  load_chunk(0);
+  for (int k0 = 0; k0 < k_pad; k0 += BK) {
+    store_chunk();
+    __syncthreads();
+    if (k0 + BK < k_pad) load_chunk(k0 + BK);  // in flight during the products
+
+    floatx4 a[4];
+#pragma unroll
+    for (int pl = 0; pl < 4; ++pl)
+      a[pl] = *reinterpret_cast<const floatx4*>(As + pl * A_PLANE + (wave * 16 + i16) * SK + 4 * g);
+    floatx4 b[NBN][4];
+#pragma unroll
+    for (int nb = 0; nb < NBN; ++nb)
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl)
+        b[nb][pl] = *reinterpret_cast<const floatx4*>(Bs + pl * B_PLANE + (nb * 16 + i16) * SK + 4 * g);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      // Y0 = X0 W0, Y2 = X2 W2, Yr = Xr Wr - Xi Wi, Yi = Xr Wi + Xi Wr; the
+      // two products into Yr (and Yi) are issued apart
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) {
+        acc[nb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0][st], b[nb][0][st], acc[nb][0], 0, 0, 0);
+        acc[nb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1][st], b[nb][1][st], acc[nb][1], 0, 0, 0);
+        acc[nb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2][st], b[nb][2][st], acc[nb][2], 0, 0, 0);
+        acc[nb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2][st], b[nb][3][st], acc[nb][3], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) {
+        acc[nb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3][st], -b[nb][3][st], acc[nb][2], 0, 0, 0);
+        acc[nb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3][st], b[nb][2][st], acc[nb][3], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NBN; ++nb) {
+    const int col = n0 + nb * 16 + i16;
+    if (col >= n_out) continue;
+    const float bcol = bias[col];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wave * 16 + 4 * g + r;
+      if (row < src.P) {
+        floatx4 o = idft4(acc[nb][0][r], acc[nb][1][r], acc[nb][2][r], acc[nb][3][r]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = activate(o[t] + bcol, act);
+        *reinterpret_cast<floatx4*>(y + ((int64_t)row * n_out + col) * 4) = o;
+      }
+    }
+  }
+}
+
+template <int NBN>
+static hipError_t launch_conv32_t(const PatchSrc& src, const float* spec, const float* bias, float* out,
+                                  int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
+  constexpr int BN = 16 * NBN;
+  const int ncol = (n_out + BN - 1) / BN;
+  const int64_t nrow = ((int64_t)src.P + 63) / 64;
+  const int64_t tiles = nrow * ncol;
+  if (tiles > (int64_t)0x7fffffff / 2) return hipErrorInvalidValue;
+  const int64_t grid = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_conv_gemm32<NBN>), dim3((unsigned)grid), dim3(256), 0, s, src, spec, bias, out,
+                     k_pad, n_out, n_pad, ncol, (int)tiles, act);
+  return hipGetLastError();
+}
+
+// Output tiles of 16, 32, 48 or 64 channels: the fewest padded channels,
+// then the widest tile.
+static hipError_t launch_conv32(const PatchSrc& src, const float* spec, const float* bias, float* out,
+                                int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
+  int best = 4, waste = 1 << 30;
+  for (int nbn = 4; nbn >= 1; --nbn) {
+    const int bn = 16 * nbn, wst = (n_out + bn - 1) / bn * bn - n_out;
+    if (wst < waste) {
+      waste = wst;
+      best = nbn;
+    }
+  }
+  switch (best) {
+    case 1: return launch_conv32_t<1>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 2: return launch_conv32_t<2>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 3: return launch_conv32_t<3>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    default: return launch_conv32_t<4>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+  }
+}
+
 // Patches of a field written out, x'[P][K][4] (the weight-gradient operand).
 // One thread per (pixel, four patch channels).
 template <typename T>
@@ -1017,6 +1229,11 @@ hipError_t launch_conv(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs,
     }
     return launch_conv_cfg<_Float16>(cfg, src, (const _Float16*)spec, bias, (_Float16*)out, k_pad,
                                      n_out, n_pad, act, s);
+  }
+  if (env == nullptr || !*env) {
+    const char* e32 = getenv("EQL_CONV_F32_16");
+    if (e32 == nullptr || atoi(e32) != 0)
+      return launch_conv32(src, (const float*)spec, bias, (float*)out, k_pad, n_out, n_pad, act, s);
   }
   return launch_conv_cfg<float>(cfg, src, (const float*)spec, bias, (float*)out, k_pad, n_out, n_pad,
                                 act, s);
