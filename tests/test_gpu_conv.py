@@ -162,3 +162,20 @@ def test_stage_shape_sampled_images(dtype):
     assert rel_err(to_np64(dpsi), rpsi) <= TOL[dtype]
     assert rel_err(to_np64(dbias), rbias) <= TOL[dtype]
     plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_determinism_bitwise(dtype):
+    """Repeat calls give bit-identical results: the reductions (over patch
+    channels inside a tile, over pixel splits for the filter gradient) run in
+    a fixed order."""
+    torch = torch_mod()
+    inp, plan = _case((2, 21, 19, 48, 48, 3), dtype)
+    f, dy = to_dev(inp["f"]), to_dev(inp["dy"])
+    first = [plan.forward(f), plan.backward_input(dy), *plan.backward_weight(f, dy)]
+    for _ in range(2):
+        again = [plan.forward(f), plan.backward_input(dy), *plan.backward_weight(f, dy)]
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+    plan.close()
