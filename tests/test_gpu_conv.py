@@ -179,3 +179,20 @@ def test_determinism_bitwise(dtype):
         for a, b in zip(first, again):
             assert torch.equal(a, b)
     plan.close()
+
+
+@pytest.mark.parametrize("dtype,env", [("f16", "EQL_CONV_RD"), ("f32", "EQL_CONV_F32_16")])
+def test_lds_tiled_kernel_on_default_shapes(monkeypatch, dtype, env):
+    """The LDS-tiled kernel (32x32 matrix-core steps) also serves the shapes
+    whose default is the register-direct (binary16) or 16x16x4 (binary32)
+    kernel when those are switched off; it stays at the oracle bar there."""
+    monkeypatch.setenv(env, "0")
+    for shape in [(2, 7, 9, 48, 48, 3), (1, 9, 12, 20, 132, 3)]:
+        inp, plan = _case(shape, dtype)
+        y = plan.forward(to_dev(inp["f"]))
+        assert rel_err(to_np64(y), oracle.conv_forward(inp["f"], inp["psi"], inp["bias"])) \
+            <= TOL[dtype], shape
+        df = plan.backward_input(to_dev(inp["dy"]))
+        assert rel_err(to_np64(df), oracle.conv_backward_input(inp["dy"], inp["psi"])) \
+            <= TOL[dtype], shape
+        plan.close()
