@@ -196,3 +196,34 @@ def test_lds_tiled_kernel_on_default_shapes(monkeypatch, dtype, env):
         assert rel_err(to_np64(df), oracle.conv_backward_input(inp["dy"], inp["psi"])) \
             <= TOL[dtype], shape
         plan.close()
+
+
+def _random_shapes(n, seed=7):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        k = int(rng.choice([1, 3, 5, 7]))
+        C = 4 * int(rng.integers(1, 25))
+        D = 4 * int(rng.integers(1, 41))
+        H, W = int(rng.integers(1, 14)), int(rng.integers(1, 14))
+        out.append((int(rng.integers(1, 3)), H, W, C, D, k))
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_random_shapes(dtype):
+    """Seeded random shapes across every kernel and split the library picks
+    (kernel sizes 1 to 7, channel counts 4 to 160, images 1 to 13 wide)."""
+    for shape in _random_shapes(14):
+        inp, plan = _case(shape, dtype, seed=11)
+        y = plan.forward(to_dev(inp["f"]))
+        assert rel_err(to_np64(y), oracle.conv_forward(inp["f"], inp["psi"], inp["bias"])) \
+            <= TOL[dtype], shape
+        df = plan.backward_input(to_dev(inp["dy"]))
+        assert rel_err(to_np64(df), oracle.conv_backward_input(inp["dy"], inp["psi"])) \
+            <= TOL[dtype], shape
+        dpsi, db = plan.backward_weight(to_dev(inp["f"]), to_dev(inp["dy"]))
+        rpsi, rb = oracle.conv_backward_weight(inp["f"], inp["dy"], shape[5])
+        assert rel_err(to_np64(dpsi), rpsi) <= TOL[dtype], shape
+        assert rel_err(to_np64(db), rb) <= TOL[dtype], shape
+        plan.close()
