@@ -35,13 +35,20 @@
 // (K(v)^T shifted to -v is again of the group-convolution form), and runs the
 // same kernel on dy.
 //
-// Forward kernel: an LDS-tiled spectral GEMM over (pixels x output channels)
-// whose reduction operand is gathered from the field.  Per chunk of BK patch
-// channels each thread loads the quads of four channels for its rows,
-// butterflies them in fp32 and writes the four spectral planes to LDS; the
-// weight spectra of the chunk are copied beside them.  The loads of chunk
-// i + 1 are issued before the matrix-core work of chunk i.  The epilogue
-// applies the inverse butterfly, bias and activation in fp32.
+// Kernels in this file (each is described where it is defined):
+//  * k_conv_rd_f16: binary16 forward and backward input for 4 to 24
+//    reduction steps: weights in VGPRs, every lane gathering and
+//    transforming its own matrix-core fragment, the steps split over four
+//    waves that combine their partial spectra through LDS;
+//  * k_conv_gemm32: binary32, an LDS-tiled spectral GEMM with 16x16x4
+//    steps and output tiles of 16 to 64 channels;
+//  * k_conv_gemm: the LDS-tiled spectral GEMM with 32x32 steps for the
+//    binary16 shapes outside the register-direct range;
+//  * k_conv_gather8_f16 / k_conv_gather: the patches written out for the
+//    filter gradient; k_conv_patch_weights and k_conv_fold: the permutation
+//    between the filter and the patch weight, both ways.
+// All of them share the gather rule below: four 4-value loads give four
+// patch channels, a centre pixel's own channels or (c, e = 0..3) of an orbit.
 #include <utility>
 
 #include "eql_device.h"
