@@ -810,6 +810,15 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       }
   }
 
+  // bias of the four output channels this lane finishes (wave nb < NB
+  // finishes block nb), loaded once instead of in every tile's epilogue
+  float bl[4] = {0.f, 0.f, 0.f, 0.f};
+  if (wave < NB) {
+    const int col = d0 + wave * 16 + 4 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bl[r] = col + r < n_out ? bias[col + r] : 0.f;
+  }
+
   // per-step constants of this lane's 8 patch channels, packed in one
   // register per step: the source channel (centre steps: first of 8; orbit
   // steps: first of 2) in bits 0-15, the orbit representative in bits 16-18
@@ -1009,7 +1018,7 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
         uint32_t o[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float b = bias[col + r];
+          const float b = bl[r];
           const float u = __builtin_fmaf(Y[0][r], 0.25f, b);
           const float pp = __builtin_fmaf(Y[1][r], 0.25f, u);
           const float mm = __builtin_fmaf(Y[1][r], -0.25f, u);
