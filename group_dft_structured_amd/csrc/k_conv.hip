@@ -757,7 +757,7 @@ struct WaveSplit {
   int start[5];
 };
 
-template <int NB, int KSW>
+template <int NB, int KSW, bool UNI>
 __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     const PatchSrc src, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, const WaveSplit split, int k_pad, int n_out, int n_pad, int n_ranges,
@@ -783,7 +783,7 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
   if (n_my == 0) return;  // whole work-group
 
   // this wave's reduction steps [ks0, ks0 + cnt), 1 <= cnt <= KSW (host
-  // split; the waves that finish channel blocks may take fewer)
+  // split, balanced against the end-of-tile work of the finishing waves)
   const int ks0 = split.start[wave], cnt = split.start[wave + 1] - ks0;
   const int d0 = j * NB * 16;
 
@@ -840,9 +840,31 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     }
     kst[s] = (uint32_t)ch | ((uint32_t)ra << 16) | ((uint32_t)rb << 19) | ((lv ? 1u : 0u) << 22);
   }
+  // With a channel count that is a multiple of 8 (UNI) the patch width is a
+  // whole number of steps and every step lies inside the centre segment or
+  // inside one orbit for all lanes: its first channel and orbit
+  // representative are the same for the whole wave, kept per step in one
+  // scalar (channel in bits 0-15, representative in bits 16-19 and 20-23),
+  // and the neighbour offsets are scalar arithmetic
+  uint32_t ust[KSW];
+  if constexpr (UNI) {
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) {
+      const int cp0 = 32 * (ks0 + s);
+      int cst = cp0, ua = 0, ub = 0;
+      if (cp0 >= src.Cc) {
+        const int rem = cp0 - src.Cc;
+        const int o = rem / (4 * src.Cs);
+        cst = (rem - o * 4 * src.Cs) >> 2;
+        orbit_rep(o, src.h, ua, ub);
+      }
+      ust[s] = (uint32_t)cst | ((uint32_t)ua << 16) | ((uint32_t)ub << 20);
+    }
+  }
 
   // tile state of the gather (the gather runs ahead of the products)
   int g_ti = -1, p = 0, pi = 0, pj = 0, lo = 0;
+  uint32_t cbase = 0, obase = 0;  // UNI: byte offsets of the lane's centre / orbit channels
   bool pix_ok = false;
   __amdgpu_buffer_rsrc_t rf = conv_rsrc(src.f, 0);
   const int halo = src.h * src.W + src.h;
@@ -863,12 +885,40 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       const int hi = t * 16 + 16 + halo < src.P ? t * 16 + 16 + halo : src.P;
       rf = conv_rsrc((const _Float16*)src.f + (int64_t)(tile_ok ? lo : 0) * src.Cs * 4,
                      tile_ok && hi > lo ? (uint32_t)((int64_t)(hi - lo) * src.Cs * 8) : 0u);
+      if constexpr (UNI) {
+        obase = (uint32_t)(((p - lo) * src.Cs + 2 * g) * 8);
+        cbase = obase + 48u * (uint32_t)g;
+        if (!pix_ok) pi = -(1 << 20);  // every neighbour out of range
+      }
+    }
+    uint32_t off[4];
+    if constexpr (UNI) {
+      const int cst = (int)(ust[S] & 0xFFFFu);
+      if (32 * (ks0 + S) < src.Cc) {
+        const bool ok = pix_ok && cst + 8 * g < src.Cs;
+        const uint32_t base = cbase + (uint32_t)cst * 8u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) off[e] = ok ? base + 16 * e : OOB;
+      } else {
+        const int ua = (int)((ust[S] >> 16) & 15u), ub = (int)((ust[S] >> 20) & 15u);
+        const int row_b = src.W * src.Cs * 8, pix_b = src.Cs * 8;
+        const uint32_t base = obase + (uint32_t)cst * 8u;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          int va, vb;
+          turn(ua, ub, jj, va, vb);
+          const bool in = (unsigned)(pi + va) < (unsigned)src.H && (unsigned)(pj + vb) < (unsigned)src.W;
+          off[jj] = in ? base + (uint32_t)(va * row_b + vb * pix_b) : OOB;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[e] = __builtin_amdgcn_raw_buffer_load_b128(rf, off[e], 0, 0);
+      return;
     }
     const int c = (int)(kst[S] & 0xFFFFu);
     const int ua = (int)((kst[S] >> 16) & 7u), ub = (int)((kst[S] >> 19) & 7u);
     const bool lv = (kst[S] >> 22) & 1u;
     const uint32_t base = (uint32_t)(((p - lo) * src.Cs + c) * 8);
-    uint32_t off[4];
     if (32 * (ks0 + S) < src.Cc) {
       // centre step: channel pairs c + 2e of the pixel; pairs past Cs are zeros
 #pragma unroll
@@ -964,20 +1014,17 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     f32x4 c0[NB], c2[NB], cr[NB], ci[NB];
   };
   Acc acc;
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc.c0[nb] = acc.c2[nb] = acc.cr[nb] = acc.ci[nb] = f32x4{};
-  };
 
-  // products of step S
+  // products of step S; the first step of a tile starts from a zero
+  // accumulator operand (no register clearing)
   auto products = [&](const Frag& F, auto s_c) {
     constexpr int S = decltype(s_c)::value;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      acc.c0[nb] = mma16(w0[nb][S], F.x0, acc.c0[nb]);
-      acc.cr[nb] = mma16(wr[nb][S], F.xr, acc.cr[nb]);
-      acc.c2[nb] = mma16(w2[nb][S], F.x2, acc.c2[nb]);
-      acc.ci[nb] = mma16(wi[nb][S], F.xr, acc.ci[nb]);
+      acc.c0[nb] = mma16(w0[nb][S], F.x0, S == 0 ? f32x4{} : acc.c0[nb]);
+      acc.cr[nb] = mma16(wr[nb][S], F.xr, S == 0 ? f32x4{} : acc.cr[nb]);
+      acc.c2[nb] = mma16(w2[nb][S], F.x2, S == 0 ? f32x4{} : acc.c2[nb]);
+      acc.ci[nb] = mma16(wi[nb][S], F.xr, S == 0 ? f32x4{} : acc.ci[nb]);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -998,7 +1045,6 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       q[2 * 64] = acc.cr[nb];
       q[3 * 64] = acc.ci[nb];
     }
-    zero_acc();
     __syncthreads();
     if (wave < NB) {
       const int nb = wave;
@@ -1015,21 +1061,29 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       const int px = t * 16 + i16;
       const int col = d0 + nb * 16 + 4 * g;
       if (px < src.P && col < n_out) {
+        float v[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float u = __builtin_fmaf(Y[0][r], 0.25f, bl[r]);
+          const float pp = __builtin_fmaf(Y[1][r], 0.25f, u);
+          const float mm = __builtin_fmaf(Y[1][r], -0.25f, u);
+          v[r][0] = __builtin_fmaf(Y[2][r], 0.5f, pp);
+          v[r][1] = __builtin_fmaf(Y[3][r], -0.5f, mm);
+          v[r][2] = __builtin_fmaf(Y[2][r], -0.5f, pp);
+          v[r][3] = __builtin_fmaf(Y[3][r], 0.5f, mm);
+        }
+        // one uniform branch for the activation, not one per value
+        if (act != ACT_NONE) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[r][q] = activate(v[r][q], act);
+        }
         uint32_t o[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float b = bl[r];
-          const float u = __builtin_fmaf(Y[0][r], 0.25f, b);
-          const float pp = __builtin_fmaf(Y[1][r], 0.25f, u);
-          const float mm = __builtin_fmaf(Y[1][r], -0.25f, u);
-          float v0 = __builtin_fmaf(Y[2][r], 0.5f, pp), v1 = __builtin_fmaf(Y[3][r], -0.5f, mm);
-          float v2 = __builtin_fmaf(Y[2][r], -0.5f, pp), v3 = __builtin_fmaf(Y[3][r], 0.5f, mm);
-          v0 = activate(v0, act);
-          v1 = activate(v1, act);
-          v2 = activate(v2, act);
-          v3 = activate(v3, act);
-          o[2 * r] = pack2h(v0, v1);
-          o[2 * r + 1] = pack2h(v2, v3);
+          o[2 * r] = pack2h(v[r][0], v[r][1]);
+          o[2 * r + 1] = pack2h(v[r][2], v[r][3]);
         }
         u32x4v* const dst = reinterpret_cast<u32x4v*>(y + ((int64_t)px * n_out + col) * 4);
         dst[0] = u32x4v{o[0], o[1], o[2], o[3]};
@@ -1051,7 +1105,6 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     typedef std::integral_constant<int, 0> s0_t;
     typedef std::integral_constant<int, 1 % CNT> s1_t;
     typedef std::integral_constant<int, 2 % CNT> s2_t;
-    zero_acc();
     u32x4v ring[2][4];
     gather(ring[0], 0, s0_t{});
     gather(ring[1], 1 / CNT, s1_t{});
@@ -1078,7 +1131,7 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
   });
 }
 
-template <int NB, int KSW>
+template <int NB, int KSW, bool UNI>
 static hipError_t launch_rd_t(const PatchSrc& src, const _Float16* spec, const float* bias,
                               _Float16* out, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
   const int KS = (src.K + 31) / 32;
@@ -1087,35 +1140,45 @@ static hipError_t launch_rd_t(const PatchSrc& src, const _Float16* spec, const f
   const int per = (n_tiles + 7) / 8;
   const int Qx = per < 32 ? per : 32;  // workers per XCD and channel range
   const int64_t grid = (int64_t)8 * Qx * n_ranges;
-  // Steps per wave.  With three channel blocks the fourth wave finishes no
-  // block at the end of a tile, so it takes up to KSW steps and the three
-  // that do share the rest; otherwise the steps are split evenly.
+  // Steps per wave: the contiguous ranges (1 to KSW steps each) that even
+  // out the estimated time per tile.  Measured at the stage shape, in units
+  // of 1/20 of an orbit step: a centre step costs 15, the end-of-tile work
+  // of a wave that finishes a channel block 23 (LDS exchange, inverse
+  // butterfly, stores) and 40 more with an activation, of a wave that only
+  // hands over its partial spectra 7.
+  const int n_centre = src.Cc / 32;
+  const int fin = act != ACT_NONE ? 63 : 23;
+  auto range_cost = [&](int a, int b, bool finishes) {
+    const int nc = (n_centre < b ? n_centre : b) - a;
+    const int centre = nc > 0 ? nc : 0;
+    return 15 * centre + 20 * (b - a - centre) + (finishes ? fin : 7);
+  };
   WaveSplit sp;
-  const int rest_waves = 4 - NB;
-  int tail = 0;
-  if (NB == 3) tail = KSW < KS - 3 ? KSW : KS - 3;
-  const int head = KS - rest_waves * tail;  // steps of the NB finishing waves
-  int k = 0;
-  for (int w = 0; w < 4; ++w) {
-    sp.start[w] = k;
-    if (NB == 3)
-      k += w < NB ? head * (w + 1) / NB - head * w / NB : tail;
-    else
-      k = KS * (w + 1) / 4;
-  }
-  sp.start[4] = k;
-  for (int w = 0; w < 4; ++w) {
-    const int c = sp.start[w + 1] - sp.start[w];
-    if (c < 1 || c > KSW) return hipErrorNotSupported;
-  }
-  hipLaunchKernelGGL((k_conv_rd_f16<NB, KSW>), dim3((unsigned)grid), dim3(256), 0, s, src, spec, bias,
+  int best = -1;
+  for (int a = 1; a <= KSW && a < KS; ++a)
+    for (int b = a + 1; b - a <= KSW && b < KS; ++b)
+      for (int c = b + 1; c - b <= KSW && c < KS; ++c) {
+        if (KS - c > KSW) continue;
+        const int bounds[5] = {0, a, b, c, KS};
+        int worst = 0;
+        for (int w = 0; w < 4; ++w) {
+          const int t = range_cost(bounds[w], bounds[w + 1], w < NB);
+          worst = t > worst ? t : worst;
+        }
+        if (best < 0 || worst < best) {
+          best = worst;
+          for (int w = 0; w < 5; ++w) sp.start[w] = bounds[w];
+        }
+      }
+  if (best < 0) return hipErrorNotSupported;
+  hipLaunchKernelGGL((k_conv_rd_f16<NB, KSW, UNI>), dim3((unsigned)grid), dim3(256), 0, s, src, spec, bias,
                      out, sp, k_pad, n_out, n_pad, n_ranges, n_tiles, Qx, act);
   return hipGetLastError();
 }
 
 // Register-direct kernel when the steps of a wave fit its weight registers
 // (at least four reduction steps, at most 24); hipErrorNotSupported
-// otherwise.  A wave takes ceil(KS/4) or floor(KS/4) steps.
+// otherwise.  A wave takes at most KSW steps, one more than an even share.
 static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const float* bias,
                             _Float16* out, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
   const char* env = getenv("EQL_CONV_RD");
@@ -1125,15 +1188,22 @@ static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const flo
   // Eight waves (two per SIMD, fewer weight registers each) measured 7x
   // slower at the 448-channel patch width: the compiler spills to scratch
   // within 256 registers.  Four waves, one per SIMD.
-  // three channel blocks up to 16 steps, with one step more for the wave
-  // that finishes no block; two blocks and an even split up to 24
+  // three channel blocks up to 16 steps (room for one step more than an even
+  // share per wave), two blocks up to 24
+  const bool uni = src.Cs % 8 == 0;
   switch ((KS + 3) / 4) {
-    case 1: return launch_rd_t<3, 2>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 2: return launch_rd_t<3, 3>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 3: return launch_rd_t<3, 4>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 4: return launch_rd_t<3, 5>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 5: return launch_rd_t<2, 5>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
-    case 6: return launch_rd_t<2, 6>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 1: return uni ? launch_rd_t<3, 2, true>(src, spec, bias, out, k_pad, n_out, n_pad, act, s)
+                   : launch_rd_t<3, 2, false>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 2: return uni ? launch_rd_t<3, 3, true>(src, spec, bias, out, k_pad, n_out, n_pad, act, s)
+                   : launch_rd_t<3, 3, false>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 3: return uni ? launch_rd_t<3, 4, true>(src, spec, bias, out, k_pad, n_out, n_pad, act, s)
+                   : launch_rd_t<3, 4, false>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 4: return uni ? launch_rd_t<3, 5, true>(src, spec, bias, out, k_pad, n_out, n_pad, act, s)
+                   : launch_rd_t<3, 5, false>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 5: return uni ? launch_rd_t<2, 5, true>(src, spec, bias, out, k_pad, n_out, n_pad, act, s)
+                   : launch_rd_t<2, 5, false>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
+    case 6: return uni ? launch_rd_t<2, 6, true>(src, spec, bias, out, k_pad, n_out, n_pad, act, s)
+                   : launch_rd_t<2, 6, false>(src, spec, bias, out, k_pad, n_out, n_pad, act, s);
     default: return hipErrorNotSupported;
   }
 }
