@@ -977,26 +977,29 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       // orbit step: patch channels (c, e = 0..3), (c + 1, e = 0..3); the
       // group vector of (ch, e) over the turns jj is neighbour jj's value
       // (jj + e) mod 4 of channel c + ch
-      const half8 L0 = __builtin_bit_cast(half8, raw[0]), L1 = __builtin_bit_cast(half8, raw[1]);
-      const half8 L2 = __builtin_bit_cast(half8, raw[2]), L3 = __builtin_bit_cast(half8, raw[3]);
+      // (ch, e) over the turns jj is neighbour jj's value (jj + e) mod 4 of
+      // channel c + ch.  Every sum and difference is one mixed-precision fma
+      // on the loaded binary16 halves (no repacking of the loads), rounded
+      // once to binary16.
+      const half8 L[4] = {__builtin_bit_cast(half8, raw[0]), __builtin_bit_cast(half8, raw[1]),
+                          __builtin_bit_cast(half8, raw[2]), __builtin_bit_cast(half8, raw[3])};
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int ch = e2 >> 1, ea = 2 * (e2 & 1), eb = ea + 1;
-        half8 wv;
-        wv[0] = L0[4 * ch + ((0 + ea) & 3)];
-        wv[1] = L1[4 * ch + ((1 + ea) & 3)];
-        wv[2] = L2[4 * ch + ((2 + ea) & 3)];
-        wv[3] = L3[4 * ch + ((3 + ea) & 3)];
-        wv[4] = L0[4 * ch + ((0 + eb) & 3)];
-        wv[5] = L1[4 * ch + ((1 + eb) & 3)];
-        wv[6] = L2[4 * ch + ((2 + eb) & 3)];
-        wv[7] = L3[4 * ch + ((3 + eb) & 3)];
-        uint32_t t0, t2, tr, tq;
-        bfly(wv, t0, t2, tr, tq);
-        v0[e2] = t0;
-        v2[e2] = t2;
-        vr[e2] = tr;
-        vi[e2] = tq;
+        float a[4], b[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          a[jj] = (float)L[jj][4 * ch + ((jj + ea) & 3)];
+          b[jj] = (float)L[jj][4 * ch + ((jj + eb) & 3)];
+        }
+        const float sa = __builtin_fmaf(a[0], one, a[2]), ta = __builtin_fmaf(a[1], one, a[3]);
+        const float sb = __builtin_fmaf(b[0], one, b[2]), tb = __builtin_fmaf(b[1], one, b[3]);
+        const float ra = __builtin_fmaf(a[2], -one, a[0]), qa = __builtin_fmaf(a[3], -one, a[1]);
+        const float rb = __builtin_fmaf(b[2], -one, b[0]), qb = __builtin_fmaf(b[3], -one, b[1]);
+        v0[e2] = pack2h(sa + ta, sb + tb);
+        v2[e2] = pack2h(sa - ta, sb - tb);
+        vr[e2] = pack2h(ra, rb);
+        vi[e2] = pack2h(qa, qb);
       }
     }
     Frag F;
