@@ -602,30 +602,46 @@ static hipError_t launch_conv32(const PatchSrc& src, const float* spec, const fl
   }
 }
 
-// Patches of a field written out, x'[P][K][4] (the weight-gradient operand).
-// One thread per (pixel, four patch channels).
+// Patches of a binary32 field written out, x'[P][K][4] (the weight-gradient
+// operand).  One thread per (pixel, four patch channels): 64 bytes of output,
+// consecutive for consecutive threads, staged through LDS so that each of a
+// wave's four stores writes 1 KB contiguously.
 template <typename T>
 __global__ __launch_bounds__(256) void k_conv_gather(const PatchSrc src, T* __restrict__ xp) {
-  typedef typename Elem<T>::quad Q;
-  const int blocks4 = (src.K + 3) / 4;
+  static_assert(sizeof(T) == 4, "four binary32 quads per thread");
+  __shared__ __attribute__((aligned(16))) floatx4 stage[4][256];
+  const int blocks4 = src.K / 4;
+  const int64_t total = (int64_t)src.P * blocks4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)src.P * blocks4) return;
-  const int pix = (int)(i / blocks4);
-  const int cp = (int)(i % blocks4) * 4;
-  int mode = 2, c = 0, ua = 0, ub = 0;
-  patch_mode<T>(src, cp, mode, c, ua, ub);
-  const int halo = src.h * src.W + src.h;
-  const int pix0 = pix - halo > 0 ? pix - halo : 0;
-  const int pix1 = pix + 1 + halo < src.P ? pix + 1 + halo : src.P;
-  const __amdgpu_buffer_rsrc_t rf =
-      conv_rsrc((const T*)src.f + (int64_t)pix0 * src.Cs * 4,
-                (uint32_t)((int64_t)(pix1 - pix0) * src.Cs * 4 * (int)sizeof(T)));
-  const PatchQuads<T> r =
-      patch_load<T>(src, rf, pix0, pix, (pix / src.W) % src.H, pix % src.W, mode, c, ua, ub);
-  T* out = xp + ((int64_t)pix * src.K + cp) * 4;
+  const int lane = threadIdx.x & 63, wbase = threadIdx.x & ~63;
+  floatx4 out[4] = {};
+  if (i < total) {
+    const int pix = (int)(i / blocks4);
+    const int cp = (int)(i % blocks4) * 4;
+    int mode = 2, c = 0, ua = 0, ub = 0;
+    patch_mode<T>(src, cp, mode, c, ua, ub);
+    const int halo = src.h * src.W + src.h;
+    const int pix0 = pix - halo > 0 ? pix - halo : 0;
+    const int pix1 = pix + 1 + halo < src.P ? pix + 1 + halo : src.P;
+    const __amdgpu_buffer_rsrc_t rf =
+        conv_rsrc((const T*)src.f + (int64_t)pix0 * src.Cs * 4,
+                  (uint32_t)((int64_t)(pix1 - pix0) * src.Cs * 4 * (int)sizeof(T)));
+    const PatchQuads<T> r =
+        patch_load<T>(src, rf, pix0, pix, (pix / src.W) % src.H, pix % src.W, mode, c, ua, ub);
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (cp + e < src.K) *reinterpret_cast<Q*>(out + 4 * e) = Elem<T>::pack(patch_vector<T>(r, mode, e));
+    for (int e = 0; e < 4; ++e) out[e] = patch_vector<T>(r, mode, e);
+  }
+  floatx4* const run = &stage[0][0] + wbase * 4;  // the wave's 4 KB in output order
+#pragma unroll
+  for (int e = 0; e < 4; ++e) run[4 * lane + e] = out[e];
+  __syncthreads();
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + wbase;
+  floatx4* const dst = reinterpret_cast<floatx4*>(xp) + i0 * 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int slot = 64 * e + lane;
+    if (i0 + slot / 4 < total) dst[slot] = run[slot];
+  }
 }
 
 // Orbit representative o (row-major over rows 1..h, columns 0..h).
@@ -1213,67 +1229,87 @@ static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const flo
 
 // Patches of a binary16 field written out, x'[P][K][4], one thread per
 // (pixel, 8 patch channels): the four 16-byte loads of the register-direct
-// kernel's gather and four 16-byte stores.
+// kernel's gather.  Consecutive threads own consecutive 64-byte pieces of
+// the output, so a wave's 64 pieces are 4 KB in one run; they go through
+// LDS so that each of the wave's four stores writes 1 KB contiguously
+// instead of 16 bytes every 64.
 __global__ __launch_bounds__(256) void k_conv_gather8_f16(const PatchSrc src,
                                                           _Float16* __restrict__ xp) {
+  __shared__ __attribute__((aligned(16))) u32x4v stage[4][256];  // [piece part][thread]
   const int units = src.K / 8;
+  const int64_t total = (int64_t)src.P * units;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)src.P * units) return;
-  const int p = (int)(i / units);
-  const int cp = (int)(i - (int64_t)p * units) * 8;
-  const int halo = src.h * src.W + src.h;
-  const int lo = p - halo > 0 ? p - halo : 0;
-  const int hi = p + 1 + halo < src.P ? p + 1 + halo : src.P;
-  const __amdgpu_buffer_rsrc_t r = conv_rsrc((const _Float16*)src.f + (int64_t)lo * src.Cs * 4,
-                                             (uint32_t)((int64_t)(hi - lo) * src.Cs * 8));
-  const bool centre = cp < src.Cc;
-  uint32_t off[4];
-  if (centre) {
+  const int lane = threadIdx.x & 63, wbase = threadIdx.x & ~63;
+  u32x4v out[4] = {};
+  if (i < total) {
+    const int p = (int)(i / units);
+    const int cp = (int)(i - (int64_t)p * units) * 8;
+    const int halo = src.h * src.W + src.h;
+    const int lo = p - halo > 0 ? p - halo : 0;
+    const int hi = p + 1 + halo < src.P ? p + 1 + halo : src.P;
+    const __amdgpu_buffer_rsrc_t r = conv_rsrc((const _Float16*)src.f + (int64_t)lo * src.Cs * 4,
+                                               (uint32_t)((int64_t)(hi - lo) * src.Cs * 8));
+    const bool centre = cp < src.Cc;
+    uint32_t off[4];
+    if (centre) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      off[e] = cp + 2 * e < src.Cs ? (uint32_t)(((p - lo) * src.Cs + cp + 2 * e) * 8) : OOB;
-  } else {
-    const int rem = cp - src.Cc;
-    const int o = rem / (4 * src.Cs);
-    const int c = (rem - o * 4 * src.Cs) >> 2;
-    int ua, ub;
-    orbit_rep(o, src.h, ua, ub);
-    const int pj = p % src.W, pi = (p / src.W) % src.H;
+      for (int e = 0; e < 4; ++e)
+        off[e] = cp + 2 * e < src.Cs ? (uint32_t)(((p - lo) * src.Cs + cp + 2 * e) * 8) : OOB;
+    } else {
+      const int rem = cp - src.Cc;
+      const int o = rem / (4 * src.Cs);
+      const int c = (rem - o * 4 * src.Cs) >> 2;
+      int ua, ub;
+      orbit_rep(o, src.h, ua, ub);
+      const int pj = p % src.W, pi = (p / src.W) % src.H;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      int va, vb;
-      turn(ua, ub, jj, va, vb);
-      const bool in = (unsigned)(pi + va) < (unsigned)src.H && (unsigned)(pj + vb) < (unsigned)src.W;
-      off[jj] = in ? (uint32_t)(((p + va * src.W + vb - lo) * src.Cs + c) * 8) : OOB;
+      for (int jj = 0; jj < 4; ++jj) {
+        int va, vb;
+        turn(ua, ub, jj, va, vb);
+        const bool in = (unsigned)(pi + va) < (unsigned)src.H && (unsigned)(pj + vb) < (unsigned)src.W;
+        off[jj] = in ? (uint32_t)(((p + va * src.W + vb - lo) * src.Cs + c) * 8) : OOB;
+      }
+    }
+    u32x4v raw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) raw[e] = __builtin_amdgcn_raw_buffer_load_b128(r, off[e], 0, 0);
+    if (centre) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = raw[e];
+    } else {
+      // patch channels (c, e = 0..3), (c + 1, e = 0..3): the group vector
+      // of (ch, e) over the turns jj is neighbour jj's value (jj + e) mod 4
+      // of channel c + ch
+      const half8 L0 = __builtin_bit_cast(half8, raw[0]), L1 = __builtin_bit_cast(half8, raw[1]);
+      const half8 L2 = __builtin_bit_cast(half8, raw[2]), L3 = __builtin_bit_cast(half8, raw[3]);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int ch = e2 >> 1, ea = 2 * (e2 & 1), eb = ea + 1;
+        half8 wv;
+        wv[0] = L0[4 * ch + ((0 + ea) & 3)];
+        wv[1] = L1[4 * ch + ((1 + ea) & 3)];
+        wv[2] = L2[4 * ch + ((2 + ea) & 3)];
+        wv[3] = L3[4 * ch + ((3 + ea) & 3)];
+        wv[4] = L0[4 * ch + ((0 + eb) & 3)];
+        wv[5] = L1[4 * ch + ((1 + eb) & 3)];
+        wv[6] = L2[4 * ch + ((2 + eb) & 3)];
+        wv[7] = L3[4 * ch + ((3 + eb) & 3)];
+        out[e2] = __builtin_bit_cast(u32x4v, wv);
+      }
     }
   }
-  u32x4v raw[4];
+  // the wave's output run in LDS in output order (piece part e of thread t
+  // at 16-byte slot 4t + e of the wave's 4 KB), read back as four 1 KB rows
+  u32x4v* const run = &stage[0][0] + wbase * 4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) raw[e] = __builtin_amdgcn_raw_buffer_load_b128(r, off[e], 0, 0);
-  u32x4v* const dst = reinterpret_cast<u32x4v*>(xp + ((int64_t)p * src.K + cp) * 4);
-  if (centre) {
+  for (int e = 0; e < 4; ++e) run[4 * lane + e] = out[e];
+  __syncthreads();
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + wbase;  // first piece of the wave
+  u32x4v* const dst = reinterpret_cast<u32x4v*>(xp) + i0 * 4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = raw[e];
-    return;
-  }
-  // patch channels (c, e = 0..3), (c + 1, e = 0..3): the group vector of
-  // (ch, e) over the turns jj is neighbour jj's value (jj + e) mod 4 of
-  // channel c + ch
-  const half8 L0 = __builtin_bit_cast(half8, raw[0]), L1 = __builtin_bit_cast(half8, raw[1]);
-  const half8 L2 = __builtin_bit_cast(half8, raw[2]), L3 = __builtin_bit_cast(half8, raw[3]);
-#pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2) {
-    const int ch = e2 >> 1, ea = 2 * (e2 & 1), eb = ea + 1;
-    half8 wv;
-    wv[0] = L0[4 * ch + ((0 + ea) & 3)];
-    wv[1] = L1[4 * ch + ((1 + ea) & 3)];
-    wv[2] = L2[4 * ch + ((2 + ea) & 3)];
-    wv[3] = L3[4 * ch + ((3 + ea) & 3)];
-    wv[4] = L0[4 * ch + ((0 + eb) & 3)];
-    wv[5] = L1[4 * ch + ((1 + eb) & 3)];
-    wv[6] = L2[4 * ch + ((2 + eb) & 3)];
-    wv[7] = L3[4 * ch + ((3 + eb) & 3)];
-    dst[e2] = __builtin_bit_cast(u32x4v, wv);
+  for (int e = 0; e < 4; ++e) {
+    const int slot = 64 * e + lane;  // 16-byte slot of the wave's run
+    if (i0 + slot / 4 < total) dst[slot] = run[slot];
   }
 }
 
