@@ -605,7 +605,7 @@ static hipError_t launch_conv32(const PatchSrc& src, const float* spec, const fl
 // Patches of a binary32 field written out, x'[P][K][4] (the weight-gradient
 // operand).  One thread per (pixel, four patch channels): 64 bytes of output,
 // consecutive for consecutive threads, staged through LDS so that each of a
-// wave's four stores writes 1 KB contiguously.
+// wave's four stores writes 1 KB contiguously (non-temporal: streamed).
 template <typename T>
 __global__ __launch_bounds__(256) void k_conv_gather(const PatchSrc src, T* __restrict__ xp) {
   static_assert(sizeof(T) == 4, "four binary32 quads per thread");
@@ -640,7 +640,7 @@ __global__ __launch_bounds__(256) void k_conv_gather(const PatchSrc src, T* __re
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int slot = 64 * e + lane;
-    if (i0 + slot / 4 < total) dst[slot] = run[slot];
+    if (i0 + slot / 4 < total) __builtin_nontemporal_store(run[slot], &dst[slot]);
   }
 }
 
@@ -1232,7 +1232,8 @@ static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const flo
 // kernel's gather.  Consecutive threads own consecutive 64-byte pieces of
 // the output, so a wave's 64 pieces are 4 KB in one run; they go through
 // LDS so that each of the wave's four stores writes 1 KB contiguously
-// instead of 16 bytes every 64.
+// instead of 16 bytes every 64.  The patches (k^2 times the field) are
+// streamed: non-temporal stores.
 __global__ __launch_bounds__(256) void k_conv_gather8_f16(const PatchSrc src,
                                                           _Float16* __restrict__ xp) {
   __shared__ __attribute__((aligned(16))) u32x4v stage[4][256];  // [piece part][thread]
@@ -1309,7 +1310,7 @@ __global__ __launch_bounds__(256) void k_conv_gather8_f16(const PatchSrc src,
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int slot = 64 * e + lane;  // 16-byte slot of the wave's run
-    if (i0 + slot / 4 < total) dst[slot] = run[slot];
+    if (i0 + slot / 4 < total) __builtin_nontemporal_store(run[slot], &dst[slot]);
   }
 }
 
