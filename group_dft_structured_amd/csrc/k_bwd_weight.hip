@@ -250,10 +250,17 @@ __global__ __launch_bounds__(256) void k_bwd_weight_reduce(const float* __restri
 // Work-group tile of the partial kernel.
 constexpr int BW_BD = 64, BW_BC = 64;
 
+// Rows per split: 512, or more when 512-row splits would give over about
+// four work-groups per CU (1024 in all): every split writes four fp32
+// partial planes that the reduce pass reads back, and the reduce runs one
+// thread per output over all splits (at the 448-channel patch layer of the
+// 3 x 3 convolution over 200704 pixels, 392 splits of 512 rows wrote 180 MB
+// of partials).
 int64_t bwd_weight_rows_per_split(const eqlinear_plan* p, int64_t N) {
-  (void)p;
-  (void)N;
-  return 512;
+  const int64_t tiles = (round_up(p->D, BW_BD) / BW_BD) * (round_up(p->C, BW_BC) / BW_BC);
+  const int64_t splits = 1024 / tiles > 1 ? 1024 / tiles : 1;
+  const int64_t R = round_up((N + splits - 1) / splits, 512);
+  return R > 512 ? R : 512;
 }
 
 static void bw_dims(const eqlinear_plan* p, int64_t N, int64_t* S, int64_t* d_pad, int64_t* c_pad) {
