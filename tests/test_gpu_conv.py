@@ -68,6 +68,21 @@ def test_forward_act(act, dtype):
     plan.close()
 
 
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+@pytest.mark.parametrize("shape", [(2, 7, 9, 48, 48, 3), (1, 10, 9, 64, 40, 3), (1, 9, 12, 20, 132, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_forward_act_register_direct(shape, act):
+    """The fused activation on the register-direct binary16 kernel, whose
+    host split of the reduction steps depends on the activation: 14, 18 and
+    6 steps, channel counts 48 and 64 (wave-uniform orbit addressing) and 20
+    (per-lane addressing)."""
+    inp, plan = _case(shape, "f16")
+    y = plan.forward(to_dev(inp["f"]), act=act)
+    ref = oracle.conv_forward_act(inp["f"], inp["psi"], inp["bias"], act)
+    assert rel_err(to_np64(y), ref) <= TOL["f16"]
+    plan.close()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_backward_input(shape, dtype):
