@@ -14,9 +14,9 @@ OUT = os.path.join(PKG, "libeqlinear.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["eqlinear_api.hip", "k_spectra.hip", "k_spectral_gemm.hip", "k_fwd_stream.hip", "k_fwd_coop.hip", "k_fwd_ws.hip", "k_fwd_ws32.hip",
-           "k_bwd_weight.hip", "k_bwd_weight_mfma.hip", "k_bwd_weight_ws.hip",
-           "k_gemm_kstream.hip", "k_cyclic.hip", "k_p4m_pairs.hip",
+SOURCES = ["eqlinear_api.hip", "k_spectra.hip", "k_spectral_gemm.hip", "k_fwd_ws.hip", "k_fwd_ws32.hip",
+           "k_bwd_weight.hip", "k_bwd_weight_ws.hip",
+           "k_cyclic.hip", "k_p4m_pairs.hip",
            "k_conv.hip", "eqconv_api.hip"]
 
 FLAGS = [
@@ -38,7 +38,7 @@ def _compile(src):
 
 def build_library(verbose=True):
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs

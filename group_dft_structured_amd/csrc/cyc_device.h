@@ -165,21 +165,22 @@ __host__ __device__ __forceinline__ void dft_fwd(const R (&x)[T], R (&X)[T]) {
 }
 
 // Inverse: the T kept planes back to T group values, with the 1/T and 2/T
-// scalings.  Outputs t and T - t share their cosine part and differ in the
+// scalings times MUL (a power of two that undoes the plane scalings of the
+// operands).  Outputs t and T - t share their cosine part and differ in the
 // sign of their sine part.
-template <int T, typename R>
+template <int T, typename R, int MUL = 1>
 __host__ __device__ __forceinline__ void dft_inv(const R (&Q)[T], R (&y)[T]) {
   constexpr int H = NCX<T>;
   static_for<0, T / 2 + 1>([&](auto tt) {
     constexpr int t = decltype(tt)::value;
-    R a = cmad<Scaled<T, 1, One>>((R)0, Q[0]);
-    if constexpr (HAS_NYQ<T> && (t % 2) == 1) a = cmad<Scaled<T, -1, One>>(a, Q[T - 1]);
-    if constexpr (HAS_NYQ<T> && (t % 2) == 0) a = cmad<Scaled<T, 1, One>>(a, Q[T - 1]);
+    R a = cmad<Scaled<T, MUL, One>>((R)0, Q[0]);
+    if constexpr (HAS_NYQ<T> && (t % 2) == 1) a = cmad<Scaled<T, -MUL, One>>(a, Q[T - 1]);
+    if constexpr (HAS_NYQ<T> && (t % 2) == 0) a = cmad<Scaled<T, MUL, One>>(a, Q[T - 1]);
     R b = (R)0;
     static_for<1, H + 1>([&](auto kk) {
       constexpr int k = decltype(kk)::value;
-      a = cmad<Scaled<T, 2, Cos<T, k * t>>>(a, Q[2 * k - 1]);
-      b = cmad<Scaled<T, -2, Sin<T, k * t>>>(b, Q[2 * k]);
+      a = cmad<Scaled<T, 2 * MUL, Cos<T, k * t>>>(a, Q[2 * k - 1]);
+      b = cmad<Scaled<T, -2 * MUL, Sin<T, k * t>>>(b, Q[2 * k]);
     });
     if constexpr (t == 0 || 2 * t == T) {
       y[t] = a;
@@ -190,11 +191,30 @@ __host__ __device__ __forceinline__ void dft_inv(const R (&Q)[T], R (&y)[T]) {
   });
 }
 
+// Plane scaling of a group of order n: 2^-ceil(log2 n).  Every transform
+// plane of a vector of n values is a signed sum of them with coefficients of
+// modulus at most 1, so the scaled planes are bounded by the largest input
+// magnitude and no binary16 plane overflows while its inputs are finite.
+// Both operands of every product carry the scaling (input planes and weight
+// spectra; upstream-gradient and input planes in the weight gradient), so
+// the inverse multiplies by 1/scale^2, a power of two (exact).
+constexpr double plane_scale(int n) {
+  double s = 1.0;
+  for (int m = 1; m < n; m *= 2) s *= 0.5;
+  return s;
+}
+constexpr int inverse_mul(int n) {
+  int v = 1;
+  for (int m = 1; m < n; m *= 2) v *= 4;
+  return v;
+}
+
 // ---- group descriptors ------------------------------------------------------
 // The kernels of k_cyclic.hip are written once over a descriptor G that
 // gives the group order T (values per group vector and spectral planes),
-// the forward transform of one group vector into its T planes, the inverse
-// (with the 1/|G| scalings), the plane map of the adjoint spectrum, and the
+// the forward transform of one group vector into its T planes, their
+// scaling (scale), the inverse of products of two scaled operands (with the
+// 1/|G| scalings), the plane map of the adjoint spectrum, and the
 // matrix-core products of the forward (input planes times weight planes)
 // and of the weight gradient (upstream-gradient planes against input
 // planes, summed over rows).  Each product step takes a functor
@@ -213,8 +233,12 @@ struct Cyclic {
     dft_fwd<T, R>(x, X);
   }
   template <typename R>
+  static __host__ __device__ __forceinline__ void scale(R (&X)[T]) {
+    static_for<0, T>([&](auto jj) { X[decltype(jj)::value] *= (R)plane_scale(T); });
+  }
+  template <typename R>
   static __host__ __device__ __forceinline__ void inv(const R (&Q)[T], R (&y)[T]) {
-    dft_inv<T, R>(Q, y);
+    dft_inv<T, R, inverse_mul(T)>(Q, y);
   }
   static constexpr __host__ __device__ int adj_src(int j) { return j; }
   static constexpr __host__ __device__ bool adj_neg(int j) {
@@ -305,8 +329,12 @@ struct Dihedral {
     });
   }
   template <typename R>
+  static __host__ __device__ __forceinline__ void scale(R (&X)[T]) {
+    static_for<0, T>([&](auto jj) { X[decltype(jj)::value] *= (R)plane_scale(T); });
+  }
+  template <typename R>
   static __host__ __device__ __forceinline__ void inv(const R (&Q)[T], R (&y)[T]) {
-    const R h = (R)0.5;
+    const R h = (R)(0.5 * inverse_mul(T));
     R V0[n], V1[n], y0[n], y1[n];
     V0[0] = (Q[0] + Q[1]) * h;
     V1[0] = (Q[0] - Q[1]) * h;

@@ -165,7 +165,7 @@ static eqlinear_status_t run_conv(const eqlinear_plan* inner, const eqconv_plan*
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != inner->device) return EQL_ERR_INVALID_ARG;
   return hip_status("convolution launch",
-                    eql::launch_conv(p->dtype, src, (int)H, (int)W, (int)Cs, (int)p->k, P,
+                    eql::launch_conv(inner->tune, p->dtype, src, (int)H, (int)W, (int)Cs, (int)p->k, P,
                                      inner->spec_fwd, inner->bias_f32, out, (int)inner->fwd.k_pad,
                                      (int)n_out, (int)inner->fwd.n_pad, act,
                                      (hipStream_t)stream));

@@ -10,6 +10,17 @@
 // symmetry of the real DFT, "Approccio Algoritmico"):
 //     y0 = (Y0 + Y2)/4 + Yr/2        y1 = (Y0 - Y2)/4 - Yi/2
 //     y2 = (Y0 + Y2)/4 - Yr/2        y3 = (Y0 - Y2)/4 + Yi/2
+//
+// Scaled planes.  Every spectral plane the kernels store is the coefficient
+// above times a power of two that bounds it by the largest input magnitude:
+// X0 and X2 by 1/4 (|X0|, |X2| <= 4 max|x|), Xr and Xi by 1/2 (|Xr|, |Xi| <=
+// 2 max|x|).  So no binary16 plane overflows while its inputs are finite, and
+// the layer keeps the input range of the dense fp16-in, fp32-accumulate layer
+// it replaces.  Both operands of every product carry the scaling (input planes
+// and weight spectra; upstream-gradient planes and input planes in the weight
+// gradient), so a product is 1/16 (frequencies 0 and 2) or 1/4 (frequency 1)
+// of the unscaled one, and the inverse takes the factors 4 and 2 in place of
+// 1/4 and 1/2.  All of these scalings are exact in fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,7 +34,12 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// Forward length-4 butterfly on one group vector (fp32 arithmetic).
+// Plane scalings of the forward transform and factors of the inverse.
+constexpr float SCALE02 = 0.25f, SCALE1 = 0.5f;
+constexpr float INV02 = 4.0f, INV1 = 2.0f;
+
+// Forward length-4 butterfly on one group vector (fp32 arithmetic), scaled
+// planes: f0 = X0/4, f2 = X2/4, fr = Xr/2, fi = Xi/2.
 struct Spec4 {
   float f0, f2, fr, fi;
 };
@@ -31,23 +47,54 @@ struct Spec4 {
 __device__ __forceinline__ Spec4 dft4(float x0, float x1, float x2, float x3) {
   const float s02 = x0 + x2, s13 = x1 + x3;
   Spec4 s;
-  s.f0 = s02 + s13;
-  s.f2 = s02 - s13;
-  s.fr = x0 - x2;
-  s.fi = x3 - x1;
+  s.f0 = (s02 + s13) * SCALE02;
+  s.f2 = (s02 - s13) * SCALE02;
+  s.fr = (x0 - x2) * SCALE1;
+  s.fi = (x3 - x1) * SCALE1;
   return s;
 }
 
-// Inverse length-4 butterfly, fp32, with the 1/4 and 1/2 scalings (exact).
-__device__ __forceinline__ floatx4 idft4(float Y0, float Y2, float Yr, float Yi) {
-  const float a = 0.25f * (Y0 + Y2), b = 0.25f * (Y0 - Y2);
-  const float r = 0.5f * Yr, i = 0.5f * Yi;
+// Inverse length-4 butterfly, fp32, of products of two scaled operands:
+// factors 4 and 2 (exact).
+__device__ __forceinline__ floatx4 idft4(float Q0, float Q2, float Qr, float Qi) {
+  const float a = INV02 * (Q0 + Q2), b = INV02 * (Q0 - Q2);
+  const float r = INV1 * Qr, i = INV1 * Qi;
   floatx4 o;
   o[0] = a + r;
   o[1] = b - i;
   o[2] = a - r;
   o[3] = b + i;
   return o;
+}
+
+// Inverse with the bias of the output channel (forward epilogues):
+// y = 4 (Q0 +- Q2) +- 2 Qr|Qi + b as fused multiply-adds.
+__device__ __forceinline__ floatx4 idft4_bias(float Q0, float Q2, float Qr, float Qi, float b) {
+  const float u = __builtin_fmaf(Q0, INV02, b);
+  const float p = __builtin_fmaf(Q2, INV02, u);   // 4 (Q0 + Q2) + b
+  const float m = __builtin_fmaf(Q2, -INV02, u);  // 4 (Q0 - Q2) + b
+  floatx4 o;
+  o[0] = __builtin_fmaf(Qr, INV1, p);
+  o[1] = __builtin_fmaf(Qi, -INV1, m);
+  o[2] = __builtin_fmaf(Qr, -INV1, p);
+  o[3] = __builtin_fmaf(Qi, INV1, m);
+  return o;
+}
+
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+
+// Packed binary16 (Xr/2, -Xi/2) of one group vector held as the pairs
+// a01 = (x0, x1), a23 = (x2, x3): (x0 - x2)/2 and (x1 - x3)/2 with one
+// rounding each (the halving of a23 is exact for normal values), and no
+// overflow for finite inputs.
+__device__ __forceinline__ f16x2v half_diff(f16x2v a01, f16x2v a23) {
+  const f16x2v h = {(_Float16)SCALE1, (_Float16)SCALE1};
+  return __builtin_elementwise_fma(a01, h, a23 * -h);
+}
+
+// Binary16 value of v/4 (v in fp32, one rounding)
+__device__ __forceinline__ _Float16 quarter_h(float v) {
+  return (_Float16)__builtin_fmaf(v, SCALE02, 0.0f);
 }
 
 // ---- pointwise activation of the forward epilogue ---------------------------

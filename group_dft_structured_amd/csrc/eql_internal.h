@@ -26,6 +26,43 @@ struct SpectraLayout {
 
 }  // namespace eql
 
+namespace eql {
+
+// Launch choices of a plan, read once from EQL_* environment variables when
+// the plan is created and range-checked there (-1: unset or out of range,
+// which keeps the shape-based default).  They let tests force one kernel path
+// and let tuning sweeps vary tile shapes; the workspace query and every
+// launch of a plan see the same values, also inside a captured HIP graph.
+struct Tuning {
+  // producer/consumer binary16 kernel (forward and backward_input)
+  int ws_off;       // EQL_NO_WS=1: the general tiled kernel instead
+  int ws_nc, ws_np, ws_nb, ws_wpc, ws_qx;  // consumer and producer waves, 16-channel
+                                           // blocks per consumer, work-groups per CU,
+                                           // workers per XCD
+  int ws_g8;        // 8-channel producer units (0/1)
+  int ws_pipe;      // software-pipelined activation epilogue (0/1)
+  int ws_out;       // 1: consumers store their fragments (streaming)
+  int ws_split;     // split producer/consumer stores beyond the cache (0/1)
+  int64_t ws_small_bytes;  // outputs up to this size take the write-through producer stores
+  // producer/consumer binary32 forward
+  int ws32_off, ws32_nc, ws32_np, ws32_qx, ws32_stream, ws32_pst;
+  // general tiled kernel: tile shape
+  int gemm_tile;
+  // backward_weight: producer/consumer kernel off, tiled kernel forced,
+  // tile configuration, split count
+  int bws_off, bw_tiled, bws_cfg, bws_s;
+  // generic group kernels: tile shape; p4 through them; weight-gradient
+  // tile edge and work-group target; p4m on the p4 kernels
+  int cyc_tile, cyclic_p4, cyc_bw_tile, cyc_bw_wgs, p4m_pairs;
+  // group convolution: register-direct kernel (0/1), tile shape, binary32 kernel
+  int conv_rd, conv_tile, conv_f32_16;
+};
+
+// Reads and range-checks every knob (host only, no HIP call).
+Tuning read_tuning();
+
+}  // namespace eql
+
 struct eqlinear_plan {
   int64_t C, D;
   int T;        // group order: values per group vector (2..16)
@@ -34,6 +71,7 @@ struct eqlinear_plan {
   // cyclic backward_weight: tile edge (64 or 32) and work-group target, fixed
   // at plan creation so that workspace size and launch always agree
   int cyc_bw_tile, cyc_bw_wgs;
+  eql::Tuning tune;  // launch choices, fixed at plan creation
   eqlinear_dtype_t dtype;
   size_t esize;  // bytes per element of the plan dtype
   int device;    // device of the spectra, -1 before the first set_weight
@@ -63,10 +101,6 @@ namespace eql {
 int64_t bwd_weight_rows_per_split(const eqlinear_plan* p, int64_t N);
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N);
 
-// Matrix-core backward-weight path (binary16, even channel counts).
-size_t bwd_weight_mfma_workspace(const eqlinear_plan* p, int64_t N);
-hipError_t launch_bwd_weight_mfma(const eqlinear_plan* p, const void* x, const void* dy, float* dW,
-                                  float* dbias, int64_t N, void* ws, hipStream_t s);
 
 // Fixed-order sum of S fp32 partial planes [S][4][c_pad][d_pad] (+ bias
 // partials [S][d_pad]) and the inverse butterfly into dW [D][C][4], dbias [D].
@@ -80,27 +114,17 @@ hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, flo
                       int64_t N, void* ws, hipStream_t s);
 
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
-// Streaming kernel for reduction widths that fit in LDS; hipErrorNotSupported
-// when the shape is outside its limits.
-hipError_t launch_stream(eqlinear_dtype_t dt, const void* a, const void* spec, const float* bias,
-                         void* out, int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
-// Weight-stationary pipelined kernel (binary16, reduction width <= 192).
-hipError_t launch_coop(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias,
-                       void* y, int64_t N, int K, int k_pad, int n_out, int n_pad, hipStream_t s);
 // Producer/consumer spectral kernel (binary16): the forward, or with the
 // conjugate-transposed spectra (adjoint = true) the backward-input pass.
 // act: pointwise activation of the forward epilogue (0 none, 1 GELU, 2 GELU
 // with the tanh approximation); 0 for backward_input.
-hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, int act,
-                     hipStream_t s);
+hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,
+                     const float* bias, void* y, int64_t N, int K, int k_pad, int n_out, int n_pad,
+                     bool adjoint, int act, hipStream_t s);
 // Producer/consumer forward kernel, binary32 (reduction width a multiple of 16, <= 192).
-hipError_t launch_ws32(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                       int64_t N, int K, int k_pad, int n_out, int n_pad, int act, hipStream_t s);
-// K-streaming kernel (binary16, weights of the output range in LDS).
-hipError_t launch_kstream(eqlinear_dtype_t dt, const void* a, const void* spec, const float* bias,
-                          void* out, int64_t N, int K, int k_pad, int n_out, int n_pad,
-                          hipStream_t s);
+hipError_t launch_ws32(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,
+                       const float* bias, void* y, int64_t N, int K, int k_pad, int n_out, int n_pad,
+                       int act, hipStream_t s);
 hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, int act,
                           hipStream_t s);
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
@@ -130,9 +154,9 @@ __host__ __device__ inline int conv_centre_width(int Cs) { return (Cs + 31) / 32
 __host__ __device__ inline int conv_patch_width(int Cs, int k) {
   return conv_centre_width(Cs) + (k * k - 1) * Cs;
 }
-hipError_t launch_conv(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs, int k, int64_t P,
-                       const void* spec, const float* bias, void* out, int k_pad, int n_out,
-                       int n_pad, int act, hipStream_t s);
+hipError_t launch_conv(const Tuning& tn, eqlinear_dtype_t dt, const void* f, int H, int W, int Cs,
+                       int k, int64_t P, const void* spec, const float* bias, void* out, int k_pad,
+                       int n_out, int n_pad, int act, hipStream_t s);
 hipError_t launch_conv_gather(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs, int k,
                               int64_t P, void* xp, hipStream_t s);
 hipError_t launch_conv_patch_weights(eqlinear_dtype_t dt, const void* psi, void* wf, void* wa,

@@ -47,13 +47,12 @@ eqlinear_status_t check_device(const eqlinear_plan* p) {
 // the group Fourier transform, on kernels that are bound by HBM bytes, not
 // by the matrix cores, at these widths (measured on MI355X at C = 48,
 // D = 192: forward 20.9 us on the generic kernels against the p4 kernel's
-// 11.7 us at the paired width).  EQL_P4M_PAIRS=0 selects the generic
-// kernels.
-bool use_p4m_pairs(eqlinear_group_t group, int64_t n, eqlinear_dtype_t dtype, int64_t C,
-                   int64_t D) {
+// 11.7 us at the paired width).  The knob EQL_P4M_PAIRS=0 selects the
+// generic kernels.
+bool use_p4m_pairs(const eql::Tuning& tn, eqlinear_group_t group, int64_t n,
+                   eqlinear_dtype_t dtype, int64_t C, int64_t D) {
   if (group != EQL_GROUP_DIHEDRAL || n != 4 || dtype != EQL_F16) return false;
-  const char* env = getenv("EQL_P4M_PAIRS");
-  if (env != nullptr && atoi(env) == 0) return false;
+  if (tn.p4m_pairs == 0) return false;
   const int64_t k = 2 * C;  // reduction width of the paired forward
   const bool ws_width = k % 32 == 0 && (k <= 192 || k == 256 || k == 384);
   return ws_width && (2 * D) % 4 == 0 && 2 * C <= MAX_CHANNELS && 2 * D <= MAX_CHANNELS;
@@ -68,7 +67,53 @@ size_t pair_ws_dw(const eqlinear_plan* p) {
   return eql::round_up(16 * p->C * p->D * (int64_t)sizeof(float), 256);
 }
 
+// One knob: -1 when unset, empty or outside [lo, hi].
+int knob(const char* name, int lo, int hi) {
+  const char* v = getenv(name);
+  if (v == nullptr || *v == 0) return -1;
+  char* end = nullptr;
+  const long x = strtol(v, &end, 10);
+  if (end == v || *end != 0 || x < lo || x > hi) return -1;
+  return (int)x;
+}
+
 }  // namespace
+
+eql::Tuning eql::read_tuning() {
+  Tuning t;
+  t.ws_off = knob("EQL_NO_WS", 0, 1);
+  t.ws_nc = knob("EQL_WS_NC", 1, 16);
+  t.ws_np = knob("EQL_WS_NP", 1, 16);
+  t.ws_nb = knob("EQL_WS_NB", 1, 4);
+  t.ws_wpc = knob("EQL_WS_WPC", 1, 8);
+  t.ws_qx = knob("EQL_WS_QX", 1, 1 << 20);
+  t.ws_g8 = knob("EQL_WS_G8", 0, 1);
+  t.ws_pipe = knob("EQL_WS_PIPE", 0, 1);
+  t.ws_out = knob("EQL_WS_OUT", 0, 1);
+  t.ws_split = knob("EQL_WS_SPLIT", 0, 1);
+  const int small_mb = knob("EQL_WS_SMALL_MB", 0, 1 << 20);
+  t.ws_small_bytes = small_mb >= 0 ? (int64_t)small_mb << 20 : (int64_t)128 << 20;
+  t.ws32_off = knob("EQL_NO_WS32", 0, 1);
+  t.ws32_nc = knob("EQL_WS32_NC", 1, 16);
+  t.ws32_np = knob("EQL_WS32_NP", 1, 16);
+  t.ws32_qx = knob("EQL_WS32_QX", 1, 1 << 20);
+  t.ws32_stream = knob("EQL_WS32_STREAM", 0, 1);
+  t.ws32_pst = knob("EQL_WS32_PST", 0, 1);
+  t.gemm_tile = knob("EQL_GEMM_TILE", 0, 4);
+  t.bws_off = knob("EQL_NO_BWS", 0, 1);
+  t.bw_tiled = knob("EQL_BW_TILED", 0, 1);
+  t.bws_cfg = knob("EQL_BWS_CFG", 0, 2);
+  t.bws_s = knob("EQL_BWS_S", 1, 1 << 20);
+  t.cyc_tile = knob("EQL_CYC_TILE", 0, 3);
+  t.cyclic_p4 = knob("EQL_CYCLIC_P4", 0, 1);
+  t.cyc_bw_tile = knob("EQL_CYC_BW_TILE", 32, 64);
+  t.cyc_bw_wgs = knob("EQL_CYC_BW_WGS", 1, 1 << 20);
+  t.p4m_pairs = knob("EQL_P4M_PAIRS", 0, 1);
+  t.conv_rd = knob("EQL_CONV_RD", 0, 1);
+  t.conv_tile = knob("EQL_CONV_TILE", 0, 4);
+  t.conv_f32_16 = knob("EQL_CONV_F32_16", 0, 1);
+  return t;
+}
 
 extern "C" {
 
@@ -117,16 +162,12 @@ eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_grou
   p->D = D;
   p->T = (int)T;
   p->group = group;
-  {
-    // the cyclic T = 4 (p4) runs the p4 kernels unless EQL_CYCLIC_P4 asks for
-    // the generic ones; every other group runs the generic ones
-    const char* env = getenv("EQL_CYCLIC_P4");
-    p->cyclic = group != EQL_GROUP_CYCLIC || T != 4 || (env != nullptr && atoi(env) != 0);
-    const char* tile = getenv("EQL_CYC_BW_TILE");
-    p->cyc_bw_tile = (tile != nullptr && atoi(tile) == 64 && T <= 8) ? 64 : 32;
-    const char* wgs = getenv("EQL_CYC_BW_WGS");
-    p->cyc_bw_wgs = (wgs != nullptr && atoi(wgs) > 0) ? atoi(wgs) : 512;
-  }
+  p->tune = eql::read_tuning();
+  // the cyclic T = 4 (p4) runs the p4 kernels unless EQL_CYCLIC_P4 asks for
+  // the generic ones; every other group runs the generic ones
+  p->cyclic = group != EQL_GROUP_CYCLIC || T != 4 || p->tune.cyclic_p4 == 1;
+  p->cyc_bw_tile = (p->tune.cyc_bw_tile == 64 && T <= 8) ? 64 : 32;
+  p->cyc_bw_wgs = p->tune.cyc_bw_wgs > 0 ? p->tune.cyc_bw_wgs : 512;
   p->dtype = dtype;
   p->esize = dtype == EQL_F16 ? 2 : 4;
   p->device = -1;
@@ -137,7 +178,7 @@ eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_grou
   p->adj.k_pad = eql::round_up(D, eql::KPAD);
   p->inner = nullptr;
   p->pair_w = nullptr;
-  if (use_p4m_pairs(group, n, dtype, C, D)) {
+  if (use_p4m_pairs(p->tune, group, n, dtype, C, D)) {
     eqlinear_status_t st = eqlinear_plan_create_group(2 * C, 2 * D, EQL_GROUP_CYCLIC, 4, dtype,
                                                       &p->inner);
     if (st != EQL_OK) {

@@ -58,10 +58,10 @@ __device__ __forceinline__ float step_frag2<float>(const LaneK2<float>& v, int s
 }
 
 // Stage rows [r, r+BR) x features [f0, f0+BF) of a [rows][F][4] tensor,
-// transposed, as four spectral planes dst[p][feature][row] (stride SK).
-// Unit = (feature j, block q of RB rows); consecutive threads take
-// consecutive features so that the quad loads coalesce.  The fp32 value of
-// plane 0 (before rounding) is summed into fsum[it] when SUM is set.
+// transposed, as four scaled spectral planes dst[p][feature][row] (stride
+// SK).  Unit = (feature j, block q of RB rows); consecutive threads take
+// consecutive features so that the quad loads coalesce.  The fp32 sum of the
+// four group values (X0, unscaled) is summed into fsum[it] when SUM is set.
 template <typename T, int BF, int NT, bool SUM>
 __device__ __forceinline__ void stage_cols_dft(const T* __restrict__ src, int F, int r, int r_end,
                                                int f0, T* __restrict__ dst, float* fsum) {
@@ -85,8 +85,8 @@ __device__ __forceinline__ void stage_cols_dft(const T* __restrict__ src, int F,
         typedef typename Elem<T>::quad Q;
         v = Elem<T>::unpack(*reinterpret_cast<const Q*>(src + ((int64_t)n * F + f) * 4));
       }
-      const Spec4 s = dft4(v[0], v[1], v[2], v[3]);
-      if (SUM) fsum[it] += s.f0;
+      const Spec4 s = dft4(v[0], v[1], v[2], v[3]);  // scaled planes
+      if (SUM) fsum[it] += (v[0] + v[2]) + (v[1] + v[3]);  // unscaled X0 for the bias
       o0[e] = Elem<T>::from_f(s.f0);
       o2[e] = Elem<T>::from_f(s.f2);
       orr[e] = Elem<T>::from_f(s.fr);
@@ -270,17 +270,14 @@ static void bw_dims(const eqlinear_plan* p, int64_t N, int64_t* S, int64_t* d_pa
   *c_pad = round_up(p->C, BW_BC);
 }
 
-// The matrix-core path handles binary16 with even channel counts (16-byte
-// loads of column pairs); everything else uses the tiled kernel below.
-static bool use_mfma_path(const eqlinear_plan* p) {
-  const char* v = getenv("EQL_BW_TILED");
-  if (v && *v && atoi(v)) return false;
-  return p->dtype == EQL_F16 && p->C % 2 == 0 && p->D % 2 == 0;
-}
+// The producer/consumer matrix-core kernel handles binary16 with even channel
+// counts (16-byte loads of column pairs); everything else, and plans whose
+// knobs turn it off, use the tiled kernel below.
+static bool use_bws(const eqlinear_plan* p) { return p->tune.bw_tiled != 1 && bws_supported(p); }
 
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N) {
   if (p->cyclic) return cyc::workspace_bytes(p, N);
-  if (use_mfma_path(p)) return bws_supported(p) ? bws_workspace(p, N) : bwd_weight_mfma_workspace(p, N);
+  if (use_bws(p)) return bws_workspace(p, N);
   int64_t S, dp, cp;
   bw_dims(p, N, &S, &dp, &cp);
   if (S == 0) return 0;
@@ -324,9 +321,7 @@ hipError_t launch_backward_weight(const eqlinear_plan* p, const void* x, const v
     return hipGetLastError();
   }
   if (p->cyclic) return cyc::launch_backward_weight(p, x, dy, dW, dbias, N, ws, s);
-  if (use_mfma_path(p))
-    return bws_supported(p) ? launch_bws(p, x, dy, dW, dbias, N, ws, s)
-                            : launch_bwd_weight_mfma(p, x, dy, dW, dbias, N, ws, s);
+  if (use_bws(p)) return launch_bws(p, x, dy, dW, dbias, N, ws, s);
   if (p->dtype == EQL_F16) return launch_bw_t<_Float16>(p, x, dy, dW, dbias, N, ws, s);
   return launch_bw_t<float>(p, x, dy, dW, dbias, N, ws, s);
 }

@@ -19,11 +19,12 @@
 // Roles inside a work-group, one barrier per 32-row step:
 //  * NP producer waves load each step's dy and x rows (range-checked 16-byte
 //    buffer loads, three steps ahead in a register ring), apply the length-4
-//    butterfly in packed binary16 (X0 = (x0 + x2) + (x1 + x3) and
-//    X2 = (x0 + x2) - (x1 + x3) from the rounded pair sums, Xr = x0 - x2,
-//    Xi = x3 - x1) and write the four planes to LDS in matrix-core fragment
-//    order, transposing rows into the operand's K dimension; dbias is summed
-//    from exact fp32 sums of dy over the group;
+//    butterfly in packed binary16 into the scaled planes (X0/4 and X2/4 as
+//    the sum and difference of the rounded quarter pair sums (x0 + x2)/4 and
+//    (x1 + x3)/4, Xr/2 = (x0 - x2)/2, Xi/2 = (x3 - x1)/2) and write the four
+//    planes to LDS in matrix-core fragment order, transposing rows into the
+//    operand's K dimension; dbias is summed from exact fp32 sums of dy over
+//    the group;
 //  * NWD x NWC consumer waves own DB x CB blocks of 16 x 16 outputs and run
 //    v_mfma_f32_16x16x32_f16 on fragments read from LDS (K = 32 rows).
 #include "eql_device.h"
@@ -140,18 +141,24 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
       for (int k = 0; k < UPT; ++k) {
         const bool is_dy = unit_is_dy(k);
         // per row e and column (a: halves 0-3, b: 4-7): pair sums and (Xr, Xi)
+        // scaled planes (eql_device.h): the pair sums carry 1/4, so that
+        // their sum and difference are X0/4 and X2/4, and the differences
+        // 1/2; one packed fused multiply-add each, no overflow for finite
+        // inputs
+        const f16x2 qq = {(_Float16)SCALE02, (_Float16)SCALE02};
+        const f16x2 hh = {(_Float16)SCALE1, (_Float16)SCALE1};
         f16x2 sa[4], sb[4], ra[4], rb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const half8 w = raw[k][e];
           const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};
           const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};
-          sa[e] = a01 + a23;                            // (x0 + x2, x1 + x3)
-          sb[e] = b01 + b23;
+          sa[e] = __builtin_elementwise_fma(a01, qq, a23 * qq);  // (x0 + x2, x1 + x3)/4
+          sb[e] = __builtin_elementwise_fma(b01, qq, b23 * qq);
           const f16x2 a0n1 = {w[0], -w[1]}, na2a3 = {-w[2], w[3]};
           const f16x2 b0n1 = {w[4], -w[5]}, nb2b3 = {-w[6], w[7]};
-          ra[e] = a0n1 + na2a3;                         // (x0 - x2, x3 - x1)
-          rb[e] = b0n1 + nb2b3;
+          ra[e] = __builtin_elementwise_fma(a0n1, hh, na2a3 * hh);  // (x0 - x2, x3 - x1)/2
+          rb[e] = __builtin_elementwise_fma(b0n1, hh, nb2b3 * hh);
           if (is_dy) {  // dbias: exact fp32 sum of the group values
             bsum[k][0] = __builtin_amdgcn_fdot2(a01, ones, __builtin_amdgcn_fdot2(a23, ones, bsum[k][0], false), false);
             bsum[k][1] = __builtin_amdgcn_fdot2(b01, ones, __builtin_amdgcn_fdot2(b23, ones, bsum[k][1], false), false);
@@ -318,12 +325,73 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
   }
 }
 
-// ---------------------------------------------------------------------------
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
+// Sum of the S partials, inverse butterfly, dW and dbias.  Work-group =
+// 64 consecutive d of one c (lanes) x 4 waves; wave w sums the splits
+// s = w, w+4, ... in increasing order, then wave 0 adds the four wave sums in
+// wave order: a fixed summation tree, so the result is deterministic.
+__global__ __launch_bounds__(256) void k_bwd_weight_finish(const float* __restrict__ part,
+                                                           const float* __restrict__ part_b,
+                                                           float* __restrict__ dW,
+                                                           float* __restrict__ dbias, int C, int D,
+                                                           int d_pad, int c_pad, int S) {
+  __shared__ float red[4][5][64];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_dchunk = (D + 63) / 64;
+  const int c = blockIdx.x / n_dchunk, d = (blockIdx.x % n_dchunk) * 64 + lane;
+  const bool bias_block = c == 0 && dbias != nullptr;
+  const int64_t plane = (int64_t)c_pad * d_pad;
+  float P[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  if (d < D) {
+    const int64_t o = (int64_t)c * d_pad + d;
+    // chunks of eight splits per wave: all their loads are in flight before
+    // the first add, and the adds keep the split order s = w, w + 4, ...
+    constexpr int IT = 8;
+    for (int s0 = w; s0 < S; s0 += 4 * IT) {
+      float v[IT][5];
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int s = s0 + 4 * i;
+        if (s < S) {
+          const float* ps = part + (int64_t)s * 4 * plane + o;
+          v[i][0] = ps[0];
+          v[i][1] = ps[plane];
+          v[i][2] = ps[2 * plane];
+          v[i][3] = ps[3 * plane];
+          v[i][4] = bias_block ? part_b[(int64_t)s * d_pad + d] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        if (s0 + 4 * i < S) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) P[p] += v[i][p];
+          if (bias_block) P[4] += v[i][4];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 5; ++p) red[w][p][lane] = P[p];
+  __syncthreads();
+  if (w == 0 && d < D) {
+    float q[5];
+#pragma unroll
+    for (int p = 0; p < 5; ++p) q[p] = ((red[0][p][lane] + red[1][p][lane]) + red[2][p][lane]) + red[3][p][lane];
+    *reinterpret_cast<floatx4*>(dW + ((int64_t)d * C + c) * 4) = idft4(q[0], q[1], q[2], q[3]);
+    if (bias_block) dbias[d] = q[4];
+  }
 }
 
+hipError_t launch_bwd_weight_finish(const float* part, const float* part_b, float* dW, float* dbias,
+                                    int64_t C, int64_t D, int64_t d_pad, int64_t c_pad, int64_t S,
+                                    hipStream_t s) {
+  const unsigned fblocks = (unsigned)(C * ((D + 63) / 64));
+  hipLaunchKernelGGL(k_bwd_weight_finish, dim3(fblocks), dim3(256), 0, s, part, part_b, dW, dbias,
+                     (int)C, (int)D, (int)d_pad, (int)c_pad, (int)S);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 struct BwsCfg {
   int nwd, nwc, db, cb, np;
   int bd() const { return nwd * db * 16; }
@@ -337,7 +405,7 @@ static const BwsCfg kBwsCfgs[] = {
 };
 
 bool bws_supported(const eqlinear_plan* p) {
-  if (env_int("EQL_NO_BWS", 0) || p->dtype != EQL_F16) return false;
+  if (p->tune.bws_off == 1 || p->dtype != EQL_F16) return false;
   // whole column pairs (16-byte units), column tiles of 96.  Wider layers
   // re-read dy once per column tile and still beat the symmetric
   // matrix-core kernel (measured on MI355X, binary16: 168 -> 45 us at
@@ -347,8 +415,8 @@ bool bws_supported(const eqlinear_plan* p) {
   return p->C % 2 == 0 && p->D % 2 == 0;
 }
 
-static int bws_sel() {
-  const int sel = env_int("EQL_BWS_CFG", 0);
+static int bws_sel(const eqlinear_plan* p) {
+  const int sel = p->tune.bws_cfg;
   return (sel < 0 || sel >= (int)(sizeof(kBwsCfgs) / sizeof(kBwsCfgs[0]))) ? 0 : sel;
 }
 
@@ -360,14 +428,14 @@ struct BwsDims {
 
 static BwsDims bws_dims(const eqlinear_plan* p, int64_t N) {
   BwsDims m;
-  m.cfg = kBwsCfgs[bws_sel()];
+  m.cfg = kBwsCfgs[bws_sel(p)];
   m.n_dt = (int)((p->D + m.cfg.bd() - 1) / m.cfg.bd());
   m.n_ct = (int)((p->C + m.cfg.bc() - 1) / m.cfg.bc());
   m.d_pad = (int64_t)m.n_dt * m.cfg.bd();
   m.c_pad = (int64_t)m.n_ct * m.cfg.bc();
   const int T = m.n_dt * m.n_ct;
   // about one work-group per CU (one fits per CU), splits of whole 32-row steps
-  int64_t S = env_int("EQL_BWS_S", (int)(256 / T > 0 ? 256 / T : 1));
+  int64_t S = p->tune.bws_s > 0 ? p->tune.bws_s : (256 / T > 0 ? 256 / T : 1);
   const int64_t steps = (N + 31) / 32;
   if (S > steps) S = steps;
   if (S < 1) S = 1;
@@ -401,7 +469,7 @@ hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, flo
   float* part = (float*)ws;
   float* part_b = part + m.S * 4 * m.c_pad * m.d_pad;
   hipError_t e = hipErrorNotSupported;
-  switch (bws_sel()) {
+  switch (bws_sel(p)) {
     case 1: e = launch_bws_t<1, 2, 1, 3, 7>(m, p, x, dy, part, part_b, N, s); break;
     case 2: e = launch_bws_t<2, 2, 1, 3, 4>(m, p, x, dy, part, part_b, N, s); break;
 

@@ -954,8 +954,9 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
   };
 
   // butterfly of two channels' group vectors (a0..a3, b0..b3) into packed
-  // binary16 pairs (X0, X2, Xr, -Xi): X0, X2 from fp32 pair sums rounded
-  // once; Xr and -Xi = x1 - x3 from one packed subtraction
+  // binary16 pairs of the scaled planes (X0/4, X2/4, Xr/2, -Xi/2): X0, X2
+  // from fp32 pair sums, scaled and rounded once; (Xr, -Xi)/2 =
+  // (x0 - x2, x1 - x3)/2 from one packed fused multiply-add
   float one = 1.0f;
   asm volatile("" : "+v"(one));
   auto bfly = [&](const half8& w, uint32_t& o0, uint32_t& o2, uint32_t& orr, uint32_t& oi) {
@@ -963,11 +964,11 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
     const float ta = __builtin_fmaf((float)w[1], one, (float)w[3]);
     const float sb = __builtin_fmaf((float)w[4], one, (float)w[6]);
     const float tb = __builtin_fmaf((float)w[5], one, (float)w[7]);
-    o0 = pack2h(sa + ta, sb + tb);
-    o2 = pack2h(sa - ta, sb - tb);
+    o0 = __builtin_bit_cast(uint32_t, f16x2{quarter_h(sa + ta), quarter_h(sb + tb)});
+    o2 = __builtin_bit_cast(uint32_t, f16x2{quarter_h(sa - ta), quarter_h(sb - tb)});
     const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};
     const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};
-    const f16x2 da = a01 - a23, db = b01 - b23;
+    const f16x2 da = half_diff(a01, a23), db = half_diff(b01, b23);
     orr = __builtin_bit_cast(uint32_t, f16x2{da[0], db[0]});
     oi = __builtin_bit_cast(uint32_t, f16x2{da[1], db[1]});
   };
@@ -995,8 +996,8 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
       // (jj + e) mod 4 of channel c + ch
       // (ch, e) over the turns jj is neighbour jj's value (jj + e) mod 4 of
       // channel c + ch.  Every sum and difference is one mixed-precision fma
-      // on the loaded binary16 halves (no repacking of the loads), rounded
-      // once to binary16.
+      // on the loaded binary16 halves (no repacking of the loads); the
+      // scaled planes X0/4, X2/4, Xr/2, -Xi/2 are rounded once to binary16.
       const half8 L[4] = {__builtin_bit_cast(half8, raw[0]), __builtin_bit_cast(half8, raw[1]),
                           __builtin_bit_cast(half8, raw[2]), __builtin_bit_cast(half8, raw[3])};
 #pragma unroll
@@ -1012,10 +1013,10 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
         const float sb = __builtin_fmaf(b[0], one, b[2]), tb = __builtin_fmaf(b[1], one, b[3]);
         const float ra = __builtin_fmaf(a[2], -one, a[0]), qa = __builtin_fmaf(a[3], -one, a[1]);
         const float rb = __builtin_fmaf(b[2], -one, b[0]), qb = __builtin_fmaf(b[3], -one, b[1]);
-        v0[e2] = pack2h(sa + ta, sb + tb);
-        v2[e2] = pack2h(sa - ta, sb - tb);
-        vr[e2] = pack2h(ra, rb);
-        vi[e2] = pack2h(qa, qb);
+        v0[e2] = __builtin_bit_cast(uint32_t, f16x2{quarter_h(sa + ta), quarter_h(sb + tb)});
+        v2[e2] = __builtin_bit_cast(uint32_t, f16x2{quarter_h(sa - ta), quarter_h(sb - tb)});
+        vr[e2] = pack2h(ra * SCALE1, rb * SCALE1);
+        vi[e2] = pack2h(qa * SCALE1, qb * SCALE1);
       }
     }
     Frag F;
@@ -1083,13 +1084,11 @@ __global__ __launch_bounds__(256, 1) void k_conv_rd_f16(
         float v[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float u = __builtin_fmaf(Y[0][r], 0.25f, bl[r]);
-          const float pp = __builtin_fmaf(Y[1][r], 0.25f, u);
-          const float mm = __builtin_fmaf(Y[1][r], -0.25f, u);
-          v[r][0] = __builtin_fmaf(Y[2][r], 0.5f, pp);
-          v[r][1] = __builtin_fmaf(Y[3][r], -0.5f, mm);
-          v[r][2] = __builtin_fmaf(Y[2][r], -0.5f, pp);
-          v[r][3] = __builtin_fmaf(Y[3][r], 0.5f, mm);
+          const floatx4 o = idft4_bias(Y[0][r], Y[1][r], Y[2][r], Y[3][r], bl[r]);
+          v[r][0] = o[0];
+          v[r][1] = o[1];
+          v[r][2] = o[2];
+          v[r][3] = o[3];
         }
         // one uniform branch for the activation, not one per value
         if (act != ACT_NONE) {
@@ -1198,10 +1197,10 @@ static hipError_t launch_rd_t(const PatchSrc& src, const _Float16* spec, const f
 // Register-direct kernel when the steps of a wave fit its weight registers
 // (at least four reduction steps, at most 24); hipErrorNotSupported
 // otherwise.  A wave takes at most KSW steps, one more than an even share.
-static hipError_t launch_rd(const PatchSrc& src, const _Float16* spec, const float* bias,
-                            _Float16* out, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
-  const char* env = getenv("EQL_CONV_RD");
-  if (env != nullptr && atoi(env) == 0) return hipErrorNotSupported;
+static hipError_t launch_rd(const Tuning& tn, const PatchSrc& src, const _Float16* spec,
+                            const float* bias, _Float16* out, int k_pad, int n_out, int n_pad,
+                            int act, hipStream_t s) {
+  if (tn.conv_rd == 0) return hipErrorNotSupported;
   const int KS = (src.K + 31) / 32;
   if (KS < 4) return hipErrorNotSupported;
   // Eight waves (two per SIMD, fewer weight registers each) measured 7x
@@ -1339,28 +1338,25 @@ static hipError_t launch_conv_cfg(int cfg, const PatchSrc& src, const T* spec, c
   }
 }
 
-hipError_t launch_conv(eqlinear_dtype_t dt, const void* f, int H, int W, int Cs, int k, int64_t P,
-                       const void* spec, const float* bias, void* out, int k_pad, int n_out,
-                       int n_pad, int act, hipStream_t s) {
+hipError_t launch_conv(const Tuning& tn, eqlinear_dtype_t dt, const void* f, int H, int W, int Cs,
+                       int k, int64_t P, const void* spec, const float* bias, void* out, int k_pad,
+                       int n_out, int n_pad, int act, hipStream_t s) {
   if (P <= 0) return hipSuccess;
   PatchSrc src{f, H, W, Cs, k / 2, centre_width(Cs), patch_width(Cs, k), (int)P};
-  int cfg = n_out <= 64 ? 0 : 1;
-  const char* env = getenv("EQL_CONV_TILE");
-  if (env != nullptr && *env) cfg = atoi(env);
+  // a tile shape set by its knob selects the LDS-tiled kernel
+  const bool tiled = tn.conv_tile >= 0;
+  const int cfg = tiled ? tn.conv_tile : (n_out <= 64 ? 0 : 1);
   if (dt == EQL_F16) {
-    if (env == nullptr || !*env) {
-      const hipError_t e =
-          launch_rd(src, (const _Float16*)spec, bias, (_Float16*)out, k_pad, n_out, n_pad, act, s);
+    if (!tiled) {
+      const hipError_t e = launch_rd(tn, src, (const _Float16*)spec, bias, (_Float16*)out, k_pad,
+                                     n_out, n_pad, act, s);
       if (e != hipErrorNotSupported) return e;
     }
     return launch_conv_cfg<_Float16>(cfg, src, (const _Float16*)spec, bias, (_Float16*)out, k_pad,
                                      n_out, n_pad, act, s);
   }
-  if (env == nullptr || !*env) {
-    const char* e32 = getenv("EQL_CONV_F32_16");
-    if (e32 == nullptr || atoi(e32) != 0)
-      return launch_conv32(src, (const float*)spec, bias, (float*)out, k_pad, n_out, n_pad, act, s);
-  }
+  if (!tiled && tn.conv_f32_16 != 0)
+    return launch_conv32(src, (const float*)spec, bias, (float*)out, k_pad, n_out, n_pad, act, s);
   return launch_conv_cfg<float>(cfg, src, (const float*)spec, bias, (float*)out, k_pad, n_out, n_pad,
                                 act, s);
 }

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(256) void k_cyc_spectra(
       const DT* src = W + ((int64_t)d * C + c) * T;
       for (int s = 0; s < T; ++s) w[s] = (double)to_f(src[s]);
       G::template fwd<double>(w, X);
+      G::template scale<double>(X);
     }
   };
   if (i < fwd_elems) {
@@ -293,6 +294,7 @@ __global__ __launch_bounds__(256) void k_cyc_gemm(const DT* __restrict__ a,
 #pragma unroll
       for (int s = 0; s < T; ++s) xf[s] = to_f(xv[i][s]);
       G::template fwd<float>(xf, X);
+      G::template scale<float>(X);
 #pragma unroll
       for (int j = 0; j < T; ++j)
         *reinterpret_cast<DT*>(lx + (j * BM + r) * 64 + c * (int)sizeof(DT)) = (DT)X[j];
@@ -461,8 +463,11 @@ __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
         for (int t = 0; t < T; ++t) v[t] = to_f(gv[i][h][t]);
         G::template fwd<float>(v, Gs[h]);
       }
+      // plane 0 before its scaling is the sum over the group
       bsum += Gs[0][0];
       bsum += Gs[1][0];
+      G::template scale<float>(Gs[0]);
+      G::template scale<float>(Gs[1]);
       const int rp = dgrp + GD * i;
 #pragma unroll
       for (int j = 0; j < T; ++j) {
@@ -479,6 +484,7 @@ __global__ __launch_bounds__(256) void k_cyc_bwp(const DT* __restrict__ x,
 #pragma unroll
         for (int t = 0; t < T; ++t) v[t] = to_f(xv[i][h][t]);
         G::template fwd<float>(v, X[h]);
+        G::template scale<float>(X[h]);
       }
       const int rp = cgrp + GC * i;
 #pragma unroll
@@ -622,16 +628,12 @@ hipError_t launch_gemm_tile(const void* a, const void* spec, const float* bias, 
   return hipGetLastError();
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v != nullptr && *v) ? atoi(v) : dflt;
-}
-
 // Tile shapes (rows x output channels): 0 = 64x64, 1 = 64x32, 2 = 32x64,
 // 3 = 32x32 (EQL_CYC_TILE overrides the default).
 template <typename G, typename DT>
-hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, void* out, int64_t N,
-                         int K, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
+hipError_t launch_gemm_t(const Tuning& tn, const void* a, const void* spec, const float* bias,
+                         void* out, int64_t N, int K, int k_pad, int n_out, int n_pad, int act,
+                         hipStream_t s) {
   constexpr int T = G::T;
   const bool wide = T <= 8 && sizeof(DT) == 2;
   if (act != ACT_NONE) {  // fused activation: the default tile only
@@ -641,7 +643,7 @@ hipError_t launch_gemm_t(const void* a, const void* spec, const float* bias, voi
     return launch_gemm_tile<G, DT, 32, 32, true>(a, spec, bias, out, N, K, k_pad, n_out, n_pad, act,
                                                  s);
   }
-  int cfg = env_int("EQL_CYC_TILE", wide ? 2 : 3);
+  int cfg = tn.cyc_tile >= 0 ? tn.cyc_tile : (wide ? 2 : 3);
   if (T > 8 && cfg == 0) cfg = 3;
   switch (cfg) {
     case 0:
@@ -750,7 +752,7 @@ hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bia
 hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_t N, int act,
                           hipStream_t s) {
 #define EQL_CALL(G_, DT_)                                                                    \
-  launch_gemm_t<G_, DT_>(x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, \
+  launch_gemm_t<G_, DT_>(p->tune, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, \
                          (int)p->D, (int)p->fwd.n_pad, act, s)
   EQL_GROUP_DISPATCH(EQL_CALL)
 #undef EQL_CALL
@@ -759,7 +761,7 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s) {
 #define EQL_CALL(G_, DT_)                                                                      \
-  launch_gemm_t<G_, DT_>(dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad, \
+  launch_gemm_t<G_, DT_>(p->tune, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad, \
                          (int)p->C, (int)p->adj.n_pad, ACT_NONE, s)
   EQL_GROUP_DISPATCH(EQL_CALL)
 #undef EQL_CALL

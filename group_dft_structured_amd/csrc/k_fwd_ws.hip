@@ -9,10 +9,11 @@
 // Organisation on CDNA4.  A persistent work-group owns BN = 16*NB*NC output
 // channels and walks 16-row tiles of x.  Its waves have one of two roles:
 //  * NP producer waves stream x: range-checked 16-byte buffer loads three
-//    tiles ahead in a register ring, the length-4 butterfly (X0, X2 from
-//    pair sums in fp32, rounded once to binary16; Xr and -Xi from one
-//    correctly rounded packed subtraction) and the write of the four planes
-//    to LDS in matrix-core fragment order (double buffered).  They also
+//    tiles ahead in a register ring, the length-4 butterfly into the scaled
+//    planes X0/4, X2/4 (pair sums in fp32, rounded once to binary16) and
+//    Xr/2, -Xi/2 (one packed fused multiply-add per channel), and the write
+//    of the four planes to LDS in matrix-core fragment order (double
+//    buffered).  They also
 //    write the previous tile's output, staged in LDS by the consumers, to
 //    memory as whole rows;
 //  * NC consumer waves keep the weight-spectrum fragments of their 16*NB
@@ -42,17 +43,10 @@ __device__ __forceinline__ f32x4 mma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// inverse butterfly of one (row, channel) with its bias, fp32
+// inverse butterfly of one (row, channel) with its bias, fp32 (products of
+// scaled planes: factors 4 and 2)
 __device__ __forceinline__ f32x4 epi4(float Y0, float Y2, float Yr, float Yi, float b) {
-  const float u = __builtin_fmaf(Y0, 0.25f, b);
-  const float p = __builtin_fmaf(Y2, 0.25f, u);   // (Y0 + Y2)/4 + b
-  const float m = __builtin_fmaf(Y2, -0.25f, u);  // (Y0 - Y2)/4 + b
-  f32x4 o;
-  o[0] = __builtin_fmaf(Yr, 0.5f, p);
-  o[1] = __builtin_fmaf(Yi, -0.5f, m);
-  o[2] = __builtin_fmaf(Yr, -0.5f, p);
-  o[3] = __builtin_fmaf(Yi, 0.5f, m);
-  return o;
+  return idft4_bias(Y0, Y2, Yr, Yi, b);
 }
 
 // Raw buffer resource over [base, base + bytes): out-of-range loads return
@@ -191,14 +185,15 @@ __device__ __forceinline__ void ws_body(
       }
     };
     // butterfly of one 16-byte word (channels c, c + 1, four group values
-    // each) into packed binary16 pairs (X0, X2, Xr, -Xi) of the two channels.
-    // X0 and X2 from the pair sums x0 + x2 and x1 + x3 in fp32, rounded once
-    // to binary16; Xr = x0 - x2 and -Xi = x1 - x3 from one correctly rounded
-    // packed subtraction.  The fourth plane holds -Xi so that no lane ever
-    // negates a fragment; the consumers fold the sign into their sums.
-    // The multiplier 1.0 is made opaque to the optimiser so that each pair
-    // sum stays one mixed-precision fma (binary16 operands, fp32 result)
-    // instead of two conversions and an add.
+    // each) into packed binary16 pairs (X0/4, X2/4, Xr/2, -Xi/2) of the two
+    // channels (scaled planes, eql_device.h).  X0 and X2 come from the pair
+    // sums x0 + x2 and x1 + x3 in fp32, scaled and rounded once to binary16;
+    // (Xr, -Xi)/2 = (x0 - x2, x1 - x3)/2 from one packed fused multiply-add
+    // per channel.  The fourth plane holds -Xi/2 so that no lane ever negates
+    // a fragment; the consumers fold the sign into their sums.  The
+    // multiplier 1.0 is made opaque to the optimiser so that each pair sum
+    // stays one mixed-precision fma (binary16 operands, fp32 result) instead
+    // of two conversions and an add.
     float one = 1.0f;
     asm volatile("" : "+v"(one));
     auto bfly = [&](const half8& w, uint32_t& o0, uint32_t& o2, uint32_t& orr, uint32_t& oi) {
@@ -206,11 +201,11 @@ __device__ __forceinline__ void ws_body(
       const float ta = __builtin_fmaf((float)w[1], one, (float)w[3]);
       const float sb = __builtin_fmaf((float)w[4], one, (float)w[6]);
       const float tb = __builtin_fmaf((float)w[5], one, (float)w[7]);
-      o0 = pack2(sa + ta, sb + tb);
-      o2 = pack2(sa - ta, sb - tb);
+      o0 = __builtin_bit_cast(uint32_t, f16x2{quarter_h(sa + ta), quarter_h(sb + tb)});
+      o2 = __builtin_bit_cast(uint32_t, f16x2{quarter_h(sa - ta), quarter_h(sb - tb)});
       const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};  // channel c
       const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};  // channel c + 1
-      const f16x2 da = a01 - a23, db = b01 - b23;           // (Xr, -Xi) of each channel
+      const f16x2 da = half_diff(a01, a23), db = half_diff(b01, b23);  // (Xr, -Xi)/2 of each channel
       orr = __builtin_bit_cast(uint32_t, f16x2{da[0], db[0]});
       oi = __builtin_bit_cast(uint32_t, f16x2{da[1], db[1]});
     };
@@ -497,15 +492,13 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
 }
 
 // ---------------------------------------------------------------------------
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
+// knob value, or the default when the knob is unset (-1)
+static int pick(int knob, int dflt) { return knob >= 0 ? knob : dflt; }
 
 template <int NC, int NP, int NB, int KS>
-static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias, void* y, int64_t N,
-                              int K, int n_out, int n_pad, int wpc, bool adjoint, int act,
-                              hipStream_t s) {
+static hipError_t launch_ws_t(const Tuning& tn, const void* x, const void* spec, const float* bias,
+                              void* y, int64_t N, int K, int n_out, int n_pad, int wpc, bool adjoint,
+                              int act, hipStream_t s) {
   constexpr int BN = NC * NB * 16;
   const int n_ct = (n_out + BN - 1) / BN;
   if ((int64_t)n_ct * BN > n_pad) return hipErrorNotSupported;  // weight reads stay in the planes
@@ -514,7 +507,7 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   if (qx < 1) qx = 1;
   const int64_t max_qx = (n_rt + 7) / 8;
   if (qx > max_qx) qx = (int)(max_qx < 1 ? 1 : max_qx);
-  qx = env_int("EQL_WS_QX", qx);
+  qx = pick(tn.ws_qx, qx);
   const unsigned blocks = (unsigned)(8 * n_ct * qx);
   // Output path (measured on MI355X, binary16): the producers store whole
   // rows, written through the L2 while the output fits well inside the
@@ -522,10 +515,10 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   // with streaming consumer stores) and streamed beyond it (C=192, D=768,
   // N=200704: 484 us against 507 written through).
   const int64_t y_bytes = N * (int64_t)n_out * 8;
-  const bool small = y_bytes <= (128LL << 20);
+  const bool small = y_bytes <= tn.ws_small_bytes;
   // 8-channel producer units for long reductions (fewer instructions per
   // tile)
-  const bool g8 = env_int("EQL_WS_G8", KS > 6 ? 1 : 0) != 0;
+  const bool g8 = pick(tn.ws_g8, KS > 6 ? 1 : 0) != 0;
   const dim3 grid(blocks), block((NC + NP) * 64);
 #define EQL_WS_LAUNCH4(YP_, G8_, PST_, SPLIT_)                                                      \
   do {                                                                                              \
@@ -549,7 +542,7 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   // GELU: 21.2 us against 22.8).  Elsewhere it measured no faster (plain
   // forward) or slower (C=192, D=768; backward_input at K=384, where the
   // second accumulator set costs occupancy).
-  const bool pipe = act != ACT_NONE && !adjoint && small && env_int("EQL_WS_PIPE", 1) != 0;
+  const bool pipe = act != ACT_NONE && !adjoint && small && pick(tn.ws_pipe, 1) != 0;
   if (pipe) {
 #define EQL_WS_PIPE_ACT(G8_)                                                                          \
   hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_THROUGH, G8_, true, true, false, true>), grid, \
@@ -562,13 +555,13 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
   }
   // output mode: 0 producer stores (written through small outputs,
   // streamed large ones); 1 consumer stores, streaming
-  const int mode = env_int("EQL_WS_OUT", 0);
+  const int mode = pick(tn.ws_out, 0);
   // Outputs beyond the memory-side cache: the stores of each tile split
   // between producers (rows 0-7) and consumers (rows 8-15).  There the
   // producers set the pace and the consumers wait at the barrier (measured
   // at C=192, D=768: consumers wait 31% of their time, producers 12%);
   // measured 518 -> 499 us.
-  const bool split = !small && env_int("EQL_WS_SPLIT", 1) != 0;
+  const bool split = !small && pick(tn.ws_split, 1) != 0;
   if (mode == 1) {
     if (g8) EQL_WS_LAUNCH(POLICY_STREAM, true, false);
     else EQL_WS_LAUNCH(POLICY_STREAM, false, false);
@@ -588,10 +581,10 @@ static hipError_t launch_ws_t(const void* x, const void* spec, const float* bias
 }
 
 // hipErrorNotSupported when outside this kernel's limits.
-hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                     int64_t N, int K, int k_pad, int n_out, int n_pad, bool adjoint, int act,
-                     hipStream_t s) {
-  if (env_int("EQL_NO_WS", 0) || dt != EQL_F16) return hipErrorNotSupported;
+hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,
+                     const float* bias, void* y, int64_t N, int K, int k_pad, int n_out, int n_pad,
+                     bool adjoint, int act, hipStream_t s) {
+  if (tn.ws_off == 1 || dt != EQL_F16) return hipErrorNotSupported;
   // exact 32-channel steps (x rows are read without a channel mask) and whole
   // 4-channel output groups (32-byte stores)
   if (K != k_pad || K % 32 != 0 || n_out % 4 != 0) return hipErrorNotSupported;
@@ -611,13 +604,13 @@ hipError_t launch_ws(eqlinear_dtype_t dt, const void* x, const void* spec, const
   // short reductions then take 8 consumer waves of 16 channels (measured at
   // C = 96, D = 384 with GELU: 26.6 us against 37.6 us with 4 waves of 32)
   const bool act_wide = wide && act != 0 && !adjoint;
-  const int nc = env_int("EQL_WS_NC", act_wide ? 8 : wide ? 4 : deep ? (pad3 < pad4 ? 3 : 4) : 8);
-  const int np = env_int("EQL_WS_NP", 4);
-  const int nb = env_int("EQL_WS_NB", wide && !act_wide ? 2 : 1);
-  const int wpc = env_int("EQL_WS_WPC", 1);
+  const int nc = pick(tn.ws_nc, act_wide ? 8 : wide ? 4 : deep ? (pad3 < pad4 ? 3 : 4) : 8);
+  const int np = pick(tn.ws_np, 4);
+  const int nb = pick(tn.ws_nb, wide && !act_wide ? 2 : 1);
+  const int wpc = pick(tn.ws_wpc, 1);
 #define EQL_WS_CASE(NC_, NP_, NB_, KS_) \
   if (nc == NC_ && np == NP_ && nb == NB_ && ks == KS_) \
-    return launch_ws_t<NC_, NP_, NB_, KS_>(x, spec, bias, y, N, K, n_out, n_pad, wpc, adjoint, act, s);
+    return launch_ws_t<NC_, NP_, NB_, KS_>(tn, x, spec, bias, y, N, K, n_out, n_pad, wpc, adjoint, act, s);
   EQL_WS_CASE(4, 4, 2, 1)
   EQL_WS_CASE(4, 4, 2, 2)
   EQL_WS_CASE(4, 4, 2, 3)

@@ -36,17 +36,10 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// inverse butterfly of one (row, channel) with its bias, fp32
+// inverse butterfly of one (row, channel) with its bias, fp32 (products of
+// scaled planes: factors 4 and 2)
 __device__ __forceinline__ f32x4 epi4_32(float Y0, float Y2, float Yr, float Yi, float b) {
-  const float u = __builtin_fmaf(Y0, 0.25f, b);
-  const float p = __builtin_fmaf(Y2, 0.25f, u);   // (Y0 + Y2)/4 + b
-  const float m = __builtin_fmaf(Y2, -0.25f, u);  // (Y0 - Y2)/4 + b
-  f32x4 o;
-  o[0] = __builtin_fmaf(Yr, 0.5f, p);
-  o[1] = __builtin_fmaf(Yi, -0.5f, m);
-  o[2] = __builtin_fmaf(Yr, -0.5f, p);
-  o[3] = __builtin_fmaf(Yi, 0.5f, m);
-  return o;
+  return idft4_bias(Y0, Y2, Yr, Yi, b);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc32(const void* base, uint32_t bytes) {
@@ -125,11 +118,11 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // channel 4*c4 + e: values t = 0..3
           const f32x4 v = raw[4 * k + e];
-          const float s02 = v[0] + v[2], s13 = v[1] + v[3];
-          p0[e] = s02 + s13;
-          p2[e] = s02 - s13;
-          pr[e] = v[0] - v[2];
-          pi[e] = v[3] - v[1];
+          const Spec4 sp = dft4(v[0], v[1], v[2], v[3]);  // scaled planes
+          p0[e] = sp.f0;
+          p2[e] = sp.f2;
+          pr[e] = sp.fr;
+          pi[e] = sp.fi;
         }
         float* const dummy = xs + 2 * BUF + ptid * 4;
         float* const dst = buf + jb * FRAG + (g * 16 + row) * 4;
@@ -307,14 +300,12 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
 }
 
 // ---------------------------------------------------------------------------
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
+// knob value, or the default when the knob is unset (-1)
+static int pick32(int knob, int dflt) { return knob >= 0 ? knob : dflt; }
 
 template <int NC, int NP, int KB>
-static hipError_t launch_ws32_t(const void* x, const void* spec, const float* bias, void* y, int64_t N,
-                                int K, int n_out, int n_pad, int act, hipStream_t s) {
+static hipError_t launch_ws32_t(const Tuning& tn, const void* x, const void* spec, const float* bias,
+                                void* y, int64_t N, int K, int n_out, int n_pad, int act, hipStream_t s) {
   constexpr int BN = NC * 16;
   const int n_ct = (n_out + BN - 1) / BN;
   const int64_t n_rt = (N + 15) / 16;
@@ -322,16 +313,16 @@ static hipError_t launch_ws32_t(const void* x, const void* spec, const float* bi
   if (qx < 1) qx = 1;
   const int64_t max_qx = (n_rt + 7) / 8;
   if (qx > max_qx) qx = (int)(max_qx < 1 ? 1 : max_qx);
-  qx = env_int("EQL_WS32_QX", qx);
+  qx = pick32(tn.ws32_qx, qx);
   const unsigned blocks = (unsigned)(8 * n_ct * qx);
   const int64_t y_bytes = N * (int64_t)n_out * 16;
-  const bool stream = env_int("EQL_WS32_STREAM", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
+  const bool stream = pick32(tn.ws32_stream, y_bytes <= (128LL << 20) ? 1 : 0) != 0;
   // Output path (measured on MI355X): outputs inside the memory-side cache
   // are stored by the producers from LDS (C=96, D=96, N=12608: 26.1 us
   // against 30.4 with the consumers storing; 30.8 against 36.0 with GELU);
   // larger ones by the consumers (C=192, D=768: producer stores measured
   // 4038 us against 3690).
-  const bool pst = env_int("EQL_WS32_PST", y_bytes <= (128LL << 20) ? 1 : 0) != 0;
+  const bool pst = pick32(tn.ws32_pst, y_bytes <= (128LL << 20) ? 1 : 0) != 0;
   const dim3 grid(blocks), block((NC + NP) * 64);
 #define EQL_WS32_LAUNCH(YP_, ACT_, PST_)                                                              \
   hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, YP_, ACT_, PST_>), grid, block, 0, s, (const float*)x,  \
@@ -351,9 +342,10 @@ static hipError_t launch_ws32_t(const void* x, const void* spec, const float* bi
 }
 
 // hipErrorNotSupported when outside this kernel's limits.
-hipError_t launch_ws32(eqlinear_dtype_t dt, const void* x, const void* spec, const float* bias, void* y,
-                       int64_t N, int K, int k_pad, int n_out, int n_pad, int act, hipStream_t s) {
-  if (env_int("EQL_NO_WS32", 0) || dt != EQL_F32) return hipErrorNotSupported;
+hipError_t launch_ws32(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,
+                       const float* bias, void* y, int64_t N, int K, int k_pad, int n_out, int n_pad,
+                       int act, hipStream_t s) {
+  if (tn.ws32_off == 1 || dt != EQL_F32) return hipErrorNotSupported;
   // whole 16-channel reduction blocks read without a channel mask, whole
   // 4-channel output groups (64-byte stores)
   if (K != k_pad || K % 16 != 0 || n_out % 4 != 0) return hipErrorNotSupported;
@@ -363,11 +355,11 @@ hipError_t launch_ws32(eqlinear_dtype_t dt, const void* x, const void* spec, con
   // consumers: one per output block of 16 (up to 8); their weight
   // fragments take 16*kb VGPRs, so long reductions use four
   const int nc_default = (kb > 6 || (kb == 6 && n_out > 96)) ? 4 : (n_out <= 96 ? 6 : 8);
-  const int nc = env_int("EQL_WS32_NC", nc_default);
-  const int np = env_int("EQL_WS32_NP", kb > 6 ? 4 : 2);
+  const int nc = pick32(tn.ws32_nc, nc_default);
+  const int np = pick32(tn.ws32_np, kb > 6 ? 4 : 2);
   if ((int64_t)((n_out + 16 * nc - 1) / (16 * nc)) * 16 * nc > n_pad) return hipErrorNotSupported;
 #define EQL_WS32_CASE(NC_, NP_, KB_) \
-  if (nc == NC_ && np == NP_ && kb == KB_) return launch_ws32_t<NC_, NP_, KB_>(x, spec, bias, y, N, K, n_out, n_pad, act, s);
+  if (nc == NC_ && np == NP_ && kb == KB_) return launch_ws32_t<NC_, NP_, KB_>(tn, x, spec, bias, y, N, K, n_out, n_pad, act, s);
   EQL_WS32_CASE(6, 2, 6)
   EQL_WS32_CASE(4, 2, 6)
   EQL_WS32_CASE(6, 2, 2)

@@ -217,9 +217,8 @@ static hipError_t launch_gemm(int cfg, const T* a, const T* spec, const float* b
   }
 }
 
-static int pick_cfg(int64_t n_out) {
-  const char* env = getenv("EQL_GEMM_TILE");
-  if (env && *env) return atoi(env);
+static int pick_cfg(const Tuning& tn, int64_t n_out) {
+  if (tn.gemm_tile >= 0) return tn.gemm_tile;
   return n_out <= 64 ? 1 : 0;
 }
 
@@ -230,15 +229,10 @@ __global__ __launch_bounds__(256) void k_activate(T* __restrict__ y, int64_t n, 
     y[i] = (T)activate((float)y[i], act);
 }
 
+// The general fallback: any channel counts, both dtypes.
 static hipError_t launch_forward_plain(const eqlinear_plan* p, const void* x, void* y, int64_t N,
                                        hipStream_t s) {
-  hipError_t e = launch_coop(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
-                             (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, s);
-  if (e != hipErrorNotSupported) return e;
-  e = launch_stream(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
-                    (int)p->D, (int)p->fwd.n_pad, s);
-  if (e != hipErrorNotSupported) return e;
-  const int cfg = pick_cfg(p->D);
+  const int cfg = pick_cfg(p->tune, p->D);
   if (p->dtype == EQL_F16)
     return launch_gemm<_Float16>(cfg, (const _Float16*)x, (const _Float16*)p->spec_fwd, p->bias_f32,
                                  (_Float16*)y, N, (int)p->C, (int)p->fwd.k_pad, (int)p->D,
@@ -251,11 +245,11 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
                           hipStream_t s) {
   if (p->cyclic) return cyc::launch_forward(p, x, y, N, act, s);
   // the producer/consumer kernels apply the activation in their epilogue
-  hipError_t e = launch_ws(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
-                           (int)p->D, (int)p->fwd.n_pad, false, act, s);
+  hipError_t e = launch_ws(p->tune, p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
+                           (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, false, act, s);
   if (e != hipErrorNotSupported) return e;
-  e = launch_ws32(p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad, (int)p->D,
-                  (int)p->fwd.n_pad, act, s);
+  e = launch_ws32(p->tune, p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
+                  (int)p->D, (int)p->fwd.n_pad, act, s);
   if (e != hipErrorNotSupported) return e;
   // the fallbacks store the linear output; a second pass applies the activation
   e = launch_forward_plain(p, x, y, N, s);
@@ -273,13 +267,10 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s) {
   if (p->cyclic) return cyc::launch_backward_input(p, dy, dx, N, s);
-  hipError_t e = launch_ws(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D, (int)p->adj.k_pad,
-                           (int)p->C, (int)p->adj.n_pad, true, ACT_NONE, s);
+  hipError_t e = launch_ws(p->tune, p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D,
+                           (int)p->adj.k_pad, (int)p->C, (int)p->adj.n_pad, true, ACT_NONE, s);
   if (e != hipErrorNotSupported) return e;
-  e = launch_kstream(p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D,
-                                (int)p->adj.k_pad, (int)p->C, (int)p->adj.n_pad, s);
-  if (e != hipErrorNotSupported) return e;
-  const int cfg = pick_cfg(p->C);
+  const int cfg = pick_cfg(p->tune, p->C);
   if (p->dtype == EQL_F16)
     return launch_gemm<_Float16>(cfg, (const _Float16*)dy, (const _Float16*)p->spec_adj,
                                  p->zeros_f32, (_Float16*)dx, N, (int)p->D, (int)p->adj.k_pad,

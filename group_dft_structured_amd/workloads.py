@@ -141,3 +141,17 @@ def conv_workload_inputs(name, dtype=None, seed=0, dy=False):
     w = CONV_WORKLOADS[name]
     dt = dtype or w.dtypes[0]
     return make_conv_inputs(w.N, w.H, w.W, w.C, w.D, w.k, dt, seed, bias=w.bias, dy=dy)
+
+
+def same_sign_groups(shape, lo, hi, dtype, seed):
+    """Seeded tensor of ``shape`` whose group vectors (the last axis) have one
+    random sign each and magnitudes uniform in [lo, hi): with lo above
+    65504 / T every group sums past the binary16 range while each value stays
+    inside it.  For range tests of binary16 paths (loss-scaled gradients and
+    large activations)."""
+    if dtype not in _NP_DTYPE:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    sign = np.where(rng.random(shape[:-1] + (1,)) < 0.5, -1.0, 1.0)
+    mag = lo + (hi - lo) * rng.random(shape)
+    return _cast(sign * mag, dtype)

@@ -298,6 +298,29 @@ def check_counts(impl):
     assert impl.conv_mac_counts(1, 2, 2, 1) == (24, 64)
 
 
+def check_param_counts(impl):
+    """Parameters counted on the unrolled filter ("Livello di Rete", Flash
+    EQ-Linear summary: the equivariant layer shares its weights over the
+    group, 1/T of the parameters of the unconstrained layer it equals).  The
+    unconstrained convolution on the same fields has one weight per (output
+    channel d, output element t, input channel c, input element s, offset);
+    brute_forward's rot90 loops say which filter entry fills each of those
+    slots.  With every filter entry a distinct label, the compact count is
+    the number of labels seen, the dense count the number of slots, and each
+    label fills exactly T = 4 slots."""
+    for C, D, k in ((1, 1, 1), (3, 5, 3), (2, 4, 5)):
+        h = k // 2
+        psi = np.arange(1, D * C * k * k * 4 + 1, dtype=np.float64).reshape(D, C, k, k, 4)
+        rot = [np.rot90(psi, t, axes=(2, 3)) for t in range(4)]
+        slots = [rot[t][d, c, h + a, h + b, (t - s) % 4]
+                 for d in range(D) for t in range(4) for c in range(C) for s in range(4)
+                 for a in range(-h, h + 1) for b in range(-h, h + 1)]
+        labels, uses = np.unique(np.array(slots), return_counts=True)
+        assert np.all(uses == 4)
+        assert impl.conv_param_counts(C, D, k) == (len(labels), len(slots))
+        assert len(slots) == 4 * len(labels)
+
+
 ALL_CHECKS = [
     check_golden,
     check_brute_force,
@@ -309,6 +332,7 @@ ALL_CHECKS = [
     check_backward_weight_exact_differences,
     check_backward_weight_brute,
     check_counts,
+    check_param_counts,
 ]
 
 

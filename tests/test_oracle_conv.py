@@ -26,14 +26,10 @@ def test_even_kernel_rejected():
         oracle.conv_forward(np.zeros((1, 2, 2, 1, 4)), np.zeros((1, 1, 2, 2, 4)))
 
 
-def test_param_counts():
-    assert oracle.conv_param_counts(3, 5, 3) == (5 * 3 * 9 * 4, 20 * 12 * 9)
-
-
 # ------------------------------------------------------------------- mutants
 
 def _impl(rot_sign=-1, group_sign=1, swap=False, pad="constant", with_bias=True,
-          bwd_sign=-1, fold_sign=1, count=6):
+          bwd_sign=-1, fold_sign=1, count=6, dense_params=16):
     """A copy of the oracle with one knob turned away from the definition:
     rot_sign     -- filter tap R^(rot_sign * t) v (definition: -1)
     group_sign   -- weight index (group_sign * (t - s)) mod 4 (definition: +1)
@@ -42,7 +38,8 @@ def _impl(rot_sign=-1, group_sign=1, swap=False, pad="constant", with_bias=True,
     with_bias    -- bias added
     bwd_sign     -- backward_input reads dy at q + bwd_sign * v (definition: -1)
     fold_sign    -- weight gradient replica at v = R^(fold_sign * t) w
-    count        -- real products per (patch channel, output channel)"""
+    count        -- real products per (patch channel, output channel)
+    dense_params -- unrolled weights per (filter tap, c, d) (definition: 16)"""
     def tap(psi, a, b):
         D, C, k, _, _ = psi.shape
         h = k // 2
@@ -108,10 +105,14 @@ def _impl(rot_sign=-1, group_sign=1, swap=False, pad="constant", with_bias=True,
     def conv_mac_counts(pixels, C, D, k):
         return count * k * k * C * D * pixels, 16 * k * k * C * D * pixels
 
+    def conv_param_counts(C, D, k):
+        return D * C * k * k * 4, dense_params * D * C * k * k
+
     return types.SimpleNamespace(conv_forward=conv_forward,
                                  conv_backward_input=conv_backward_input,
                                  conv_backward_weight=conv_backward_weight,
-                                 conv_mac_counts=conv_mac_counts)
+                                 conv_mac_counts=conv_mac_counts,
+                                 conv_param_counts=conv_param_counts)
 
 
 MUTANTS = {
@@ -124,6 +125,7 @@ MUTANTS = {
     "backward_input_shifted_forward": dict(bwd_sign=1),
     "weight_fold_turned_the_other_way": dict(fold_sign=-1),
     "dense_product_count": dict(count=16),
+    "dense_params_not_unrolled": dict(dense_params=4),
 }
 
 
