@@ -51,6 +51,7 @@ EXPORTED = (
     "eqlinear_backward_input",
     "eqlinear_backward_weight_workspace",
     "eqlinear_backward_weight",
+    "eqlinear_backward_weight_noalloc",
     "eqlinear_status_string",
     "eqlinear_last_error",
     "eqlinear_mac_counts",
@@ -111,6 +112,8 @@ def load_library(path=LIB_PATH):
     lib.eqlinear_backward_weight_workspace.restype = ctypes.c_size_t
     lib.eqlinear_backward_weight.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
     lib.eqlinear_backward_weight.restype = st
+    lib.eqlinear_backward_weight_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, vp]
+    lib.eqlinear_backward_weight_noalloc.restype = st
     lib.eqlinear_status_string.argtypes = [st]
     lib.eqlinear_status_string.restype = ctypes.c_char_p
     lib.eqlinear_last_error.argtypes = []
@@ -213,6 +216,12 @@ def eqlinear_backward_weight(plan, x, dy, dW, dbias, N, workspace, workspace_byt
     _check(load_library().eqlinear_backward_weight(
         plan, _ptr(x), _ptr(dy), _ptr(dW), _ptr(dbias), N, _ptr(workspace), workspace_bytes,
         _stream(stream)), "eqlinear_backward_weight")
+
+
+def eqlinear_backward_weight_noalloc(plan, x, dy, dW, dbias, N, stream=None):
+    _check(load_library().eqlinear_backward_weight_noalloc(
+        plan, _ptr(x), _ptr(dy), _ptr(dW), _ptr(dbias), N, _stream(stream)),
+        "eqlinear_backward_weight_noalloc")
 
 
 def eqlinear_status_string(status):

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "eql_internal.h"
@@ -114,6 +115,48 @@ eql::Tuning eql::read_tuning() {
   t.conv_f32_16 = knob("EQL_CONV_F32_16", 0, 1);
   return t;
 }
+
+// ---- scratch of the no-allocation weight gradient --------------------------
+// One array per GPU the library runs on, in the code object's device memory
+// (zero-initialised, held until the process ends).  Host code never uses the
+// array's name as an address: each device's address comes from
+// hipGetSymbolAddress, once, on that device's first call.
+static __device__ __align__(256) unsigned char scratch[EQL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array.
+eqlinear_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return EQL_ERR_HIP;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    snprintf(g_last_error, sizeof(g_last_error), "device %d beyond the scratch table (%d)", dev,
+             MAX_DEVICES);
+    return EQL_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      set_error("hipGetSymbolAddress(scratch)", e);
+      return EQL_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return EQL_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -366,6 +409,30 @@ eqlinear_status_t eqlinear_backward_weight(eqlinear_plan_t p, const void* x, con
     return EQL_ERR_HIP;
   }
   return EQL_OK;
+}
+
+eqlinear_status_t eqlinear_backward_weight_noalloc(eqlinear_plan_t p, const void* x,
+                                                   const void* dy, float* dW, float* dbias,
+                                                   int64_t N, void* stream) {
+  if (p == nullptr || dW == nullptr) return EQL_ERR_INVALID_ARG;
+  if (N < 0 || N > MAX_ROWS) return EQL_ERR_INVALID_ARG;
+  if (N > 0 && (x == nullptr || dy == nullptr)) return EQL_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dW) || !aligned16(dbias))
+    return EQL_ERR_MISALIGNED;
+  const size_t need = eqlinear_backward_weight_workspace(p, N);
+  if (need > EQL_NOALLOC_SCRATCH_BYTES) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "backward_weight of %lld rows needs %zu bytes of scratch; the no-allocation "
+             "entry point holds %zu",
+             (long long)N, need, (size_t)EQL_NOALLOC_SCRATCH_BYTES);
+    return EQL_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const eqlinear_status_t st = scratch_address(&ws);
+    if (st != EQL_OK) return st;
+  }
+  return eqlinear_backward_weight(p, x, dy, dW, dbias, N, ws, need, stream);
 }
 
 eqlinear_status_t eqlinear_mac_counts(eqlinear_plan_t p, int64_t N, int64_t* spectral_macs,

@@ -182,7 +182,11 @@ eqlinear_status_t eqlinear_backward_input(eqlinear_plan_t plan, const void* dy,
  * (0 for an invalid plan or N < 0). */
 size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t N);
 
-/* Backward with respect to the weight and bias:
+/* Backward with respect to the weight and bias ("Implementazione": forward
+ * and backward passes; "Intuizione Centrale": the dense matrix replicates one
+ * set of shared weights, so each weight's gradient is the sum over its
+ * replicas; computed per kept frequency with the transforms of
+ * "Specializzazione per il Gruppo di Rotazione p4"):
  *     dW[d,c,r] = sum_{n,t} dy[n,d,t] * x[n,c,(t-r) mod T]   (binary32)
  *     dbias[d]  = sum_{n,t} dy[n,d,t]                          (binary32)
  * (dihedral: dW[d,c,u] = sum_{n,h} dy[n,d,h u] * x[n,c,h])
@@ -196,6 +200,27 @@ eqlinear_status_t eqlinear_backward_weight(eqlinear_plan_t plan, const void* x,
                                            const void* dy, float* dW, float* dbias,
                                            int64_t N, void* workspace,
                                            size_t workspace_bytes, void* stream);
+
+/* Size of the device scratch array of eqlinear_backward_weight_noalloc:
+ * 32 MiB per GPU the library runs on, held until the process ends. */
+#define EQL_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* eqlinear_backward_weight without a workspace argument and without any
+ * device allocation, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a static device array of EQL_NOALLOC_SCRATCH_BYTES in the
+ * library (one per GPU); the first call on a device looks up its address
+ * (hipGetSymbolAddress, no stream work).  Shapes whose workspace
+ * (eqlinear_backward_weight_workspace) exceeds it return EQL_ERR_WORKSPACE
+ * with the sizes in eqlinear_last_error(); host validation runs first, as
+ * for eqlinear_backward_weight.  Results are those of
+ * eqlinear_backward_weight (same kernels, same order).  Every call on a GPU
+ * uses that GPU's one array, and each call writes the parts it reads before
+ * reading them: calls that overlap on one GPU (different streams or
+ * threads) race and must be ordered by the caller. */
+eqlinear_status_t eqlinear_backward_weight_noalloc(eqlinear_plan_t plan, const void* x,
+                                                   const void* dy, float* dW, float* dbias,
+                                                   int64_t N, void* stream);
 
 /* Static description of a status code. */
 const char* eqlinear_status_string(eqlinear_status_t st);

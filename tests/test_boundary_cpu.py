@@ -253,3 +253,24 @@ def test_dihedral_workspace_and_python_plan():
     pl = eq.Plan(8, 8, "f16", T=8, group="dihedral")
     assert pl.T == 8 and pl.group == "dihedral"
     pl.close()
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """The no-allocation weight gradient checks its workspace need against
+    its fixed scratch size on the host, before any HIP call."""
+    lib = _lib()
+    scratch = 32 << 20
+    p = eq.eqlinear_plan_create(2048, 2048, 4, eq.EQL_F16)
+    try:
+        N = 1 << 16
+        assert eq.eqlinear_backward_weight_workspace(p, N) > scratch
+        # any aligned non-null addresses: the call returns before using them
+        fake = 1 << 20
+        st = lib.eqlinear_backward_weight_noalloc(p, fake, fake, fake, fake, N, None)
+        assert st == 5                                    # EQL_ERR_WORKSPACE
+        assert "scratch" in eq.eqlinear_last_error()
+        assert lib.eqlinear_backward_weight_noalloc(p, fake, fake, None, None, 16, None) == 1
+        assert lib.eqlinear_backward_weight_noalloc(p, fake + 8, fake, fake, fake, 16, None) == 4
+        assert lib.eqlinear_backward_weight_noalloc(None, fake, fake, fake, fake, 16, None) == 1
+    finally:
+        eq.eqlinear_plan_destroy(p)
