@@ -126,6 +126,20 @@ __device__ __forceinline__ float erf_as(float z) {
   return __builtin_copysignf(r, z);
 }
 
+// The activation with its kind fixed at compile time (no branch).
+template <int AK>
+__device__ __forceinline__ float activate_k(float v) {
+  if constexpr (AK == ACT_GELU) {
+    return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
+  } else if constexpr (AK == ACT_GELU_TANH) {
+    const float k1 = -2.3022082f, k2 = -0.10294324f;
+    const float e = __builtin_amdgcn_exp2f(v * __builtin_fmaf(k2, v * v, k1));
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+  } else {
+    return v;
+  }
+}
+
 __device__ __forceinline__ float activate(float v, int act) {
   if (act == ACT_GELU) return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
   if (act == ACT_GELU_TANH) {

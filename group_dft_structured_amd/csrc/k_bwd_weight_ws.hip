@@ -326,46 +326,44 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
 }
 
 // Sum of the S partials, inverse butterfly, dW and dbias.  Work-group =
-// 64 consecutive d of one c (lanes) x 4 waves; wave w sums the splits
-// s = w, w+4, ... in increasing order, then wave 0 adds the four wave sums in
+// 8 waves over one input channel c and 256 consecutive d (64 lanes x 4 d,
+// one 16-byte load per plane and split); wave w sums the splits s = w,
+// w + 8, ... in increasing order, then wave 0 adds the eight wave sums in
 // wave order: a fixed summation tree, so the result is deterministic.
-__global__ __launch_bounds__(256) void k_bwd_weight_finish(const float* __restrict__ part,
-                                                           const float* __restrict__ part_b,
-                                                           float* __restrict__ dW,
-                                                           float* __restrict__ dbias, int C, int D,
-                                                           int d_pad, int c_pad, int S) {
-  __shared__ float red[4][5][64];
+constexpr int FIN_WAVES = 8;
+__global__ __launch_bounds__(64 * FIN_WAVES) void k_bwd_weight_finish(
+    const float* __restrict__ part, const float* __restrict__ part_b, float* __restrict__ dW,
+    float* __restrict__ dbias, int C, int D, int d_pad, int c_pad, int S) {
+  __shared__ f32x4 red[FIN_WAVES][5][64];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_dchunk = (D + 63) / 64;
-  const int c = blockIdx.x / n_dchunk, d = (blockIdx.x % n_dchunk) * 64 + lane;
+  const int n_dchunk = (D + 255) / 256;
+  const int c = blockIdx.x / n_dchunk, d = (blockIdx.x % n_dchunk) * 256 + 4 * lane;
   const bool bias_block = c == 0 && dbias != nullptr;
   const int64_t plane = (int64_t)c_pad * d_pad;
-  float P[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  if (d < D) {
+  f32x4 P[5] = {};
+  if (d < D) {  // d_pad is a multiple of 16: d .. d + 3 lie inside the padded planes
     const int64_t o = (int64_t)c * d_pad + d;
-    // chunks of eight splits per wave: all their loads are in flight before
-    // the first add, and the adds keep the split order s = w, w + 4, ...
-    constexpr int IT = 8;
-    for (int s0 = w; s0 < S; s0 += 4 * IT) {
-      float v[IT][5];
+    // chunks of four splits per wave: all their loads are in flight before
+    // the first add, and the adds keep the split order s = w, w + 8, ...
+    constexpr int IT = 4;
+    for (int s0 = w; s0 < S; s0 += FIN_WAVES * IT) {
+      f32x4 v[IT][5];
 #pragma unroll
-      for (int i = 0; i < IT; ++i) {
-        const int s = s0 + 4 * i;
-        if (s < S) {
-          const float* ps = part + (int64_t)s * 4 * plane + o;
-          v[i][0] = ps[0];
-          v[i][1] = ps[plane];
-          v[i][2] = ps[2 * plane];
-          v[i][3] = ps[3 * plane];
-          v[i][4] = bias_block ? part_b[(int64_t)s * d_pad + d] : 0.f;
+      for (int it = 0; it < IT; ++it) {
+        const int sp = s0 + FIN_WAVES * it;
+        if (sp < S) {
+          const float* ps = part + (int64_t)sp * 4 * plane + o;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) v[it][p] = *reinterpret_cast<const f32x4*>(ps + p * plane);
+          v[it][4] = bias_block ? *reinterpret_cast<const f32x4*>(part_b + (int64_t)sp * d_pad + d)
+                                : f32x4{};
         }
       }
 #pragma unroll
-      for (int i = 0; i < IT; ++i) {
-        if (s0 + 4 * i < S) {
+      for (int it = 0; it < IT; ++it) {
+        if (s0 + FIN_WAVES * it < S) {
 #pragma unroll
-          for (int p = 0; p < 4; ++p) P[p] += v[i][p];
-          if (bias_block) P[4] += v[i][4];
+          for (int p = 0; p < 5; ++p) P[p] += v[it][p];
         }
       }
     }
@@ -374,20 +372,30 @@ __global__ __launch_bounds__(256) void k_bwd_weight_finish(const float* __restri
   for (int p = 0; p < 5; ++p) red[w][p][lane] = P[p];
   __syncthreads();
   if (w == 0 && d < D) {
-    float q[5];
+    f32x4 q[5];
 #pragma unroll
-    for (int p = 0; p < 5; ++p) q[p] = ((red[0][p][lane] + red[1][p][lane]) + red[2][p][lane]) + red[3][p][lane];
-    *reinterpret_cast<floatx4*>(dW + ((int64_t)d * C + c) * 4) = idft4(q[0], q[1], q[2], q[3]);
-    if (bias_block) dbias[d] = q[4];
+    for (int p = 0; p < 5; ++p) {
+      q[p] = red[0][p][lane];
+#pragma unroll
+      for (int ww = 1; ww < FIN_WAVES; ++ww) q[p] += red[ww][p][lane];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (d + j < D) {
+        *reinterpret_cast<floatx4*>(dW + ((int64_t)(d + j) * C + c) * 4) =
+            idft4(q[0][j], q[1][j], q[2][j], q[3][j]);
+        if (bias_block) dbias[d + j] = q[4][j];
+      }
+    }
   }
 }
 
 hipError_t launch_bwd_weight_finish(const float* part, const float* part_b, float* dW, float* dbias,
                                     int64_t C, int64_t D, int64_t d_pad, int64_t c_pad, int64_t S,
                                     hipStream_t s) {
-  const unsigned fblocks = (unsigned)(C * ((D + 63) / 64));
-  hipLaunchKernelGGL(k_bwd_weight_finish, dim3(fblocks), dim3(256), 0, s, part, part_b, dW, dbias,
-                     (int)C, (int)D, (int)d_pad, (int)c_pad, (int)S);
+  const unsigned fblocks = (unsigned)(C * ((D + 255) / 256));
+  hipLaunchKernelGGL(k_bwd_weight_finish, dim3(fblocks), dim3(64 * FIN_WAVES), 0, s, part, part_b,
+                     dW, dbias, (int)C, (int)D, (int)d_pad, (int)c_pad, (int)S);
   return hipGetLastError();
 }
 
@@ -399,9 +407,12 @@ struct BwsCfg {
 };
 
 static const BwsCfg kBwsCfgs[] = {
-    {2, 2, 1, 3, 8},  // 0: 32 x 96 tiles, 4 consumers + 8 producers
-    {1, 2, 1, 3, 7},  // 1: 16 x 96 tiles, 2 consumers + 7 producers
-    {2, 2, 1, 3, 4},  // 2: 32 x 96 tiles, 4 consumers + 4 producers
+    {2, 2, 1, 3, 8},   // 0: 32 x 96 tiles, 4 consumers + 8 producers
+    {1, 2, 1, 3, 7},   // 1: 16 x 96 tiles, 2 consumers + 7 producers
+    {2, 2, 1, 3, 4},   // 2: 32 x 96 tiles, 4 consumers + 4 producers
+    {2, 2, 2, 3, 8},   // 3: 64 x 96 tiles, 4 consumers of 32 x 48 + 8 producers
+    {2, 2, 2, 3, 4},   // 4: 64 x 96 tiles, 4 consumers of 32 x 48 + 4 producers
+    {2, 2, 2, 3, 6},   // 5: 64 x 96 tiles, 4 consumers of 32 x 48 + 6 producers
 };
 
 bool bws_supported(const eqlinear_plan* p) {
@@ -472,6 +483,9 @@ hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, flo
   switch (bws_sel(p)) {
     case 1: e = launch_bws_t<1, 2, 1, 3, 7>(m, p, x, dy, part, part_b, N, s); break;
     case 2: e = launch_bws_t<2, 2, 1, 3, 4>(m, p, x, dy, part, part_b, N, s); break;
+    case 3: e = launch_bws_t<2, 2, 2, 3, 8>(m, p, x, dy, part, part_b, N, s); break;
+    case 4: e = launch_bws_t<2, 2, 2, 3, 4>(m, p, x, dy, part, part_b, N, s); break;
+    case 5: e = launch_bws_t<2, 2, 2, 3, 6>(m, p, x, dy, part, part_b, N, s); break;
 
     default: e = launch_bws_t<2, 2, 1, 3, 8>(m, p, x, dy, part, part_b, N, s); break;
   }

@@ -361,15 +361,23 @@ __device__ __forceinline__ void ws_body(
               float, __builtin_amdgcn_raw_buffer_load_b32(rb, (d0 + nb * 16 + 4 * g + r) * 4, 0, 0));
       }
     }
-    // Yr = Wr Xr - Wi Xi and Yi = Wi Xr + Wr Xi with the plane xn = -Xi:
-    // cr + cq and ci - cn, six independent accumulators
+    // Yr = Wr Xr - Wi Xi and Yi = Wi Xr + Wr Xi with the plane xn = -Xi.
+    // Six independent accumulators (Yr = cr + cq, Yi = ci - cn), so no
+    // fragment is negated; the pipelined consumers, which hold two sets,
+    // use four (Yr in cr, Yi in ci, with Xi = -xn by a sign flip of the
+    // fragment) to stay within the register budget.
+    constexpr bool ACC4 = PIPE;
+    constexpr int NA = ACC4 ? 1 : NB;  // extent of the unused cq, cn in ACC4
     struct Acc {
-      f32x4 c0[NB], c2[NB], cr[NB], cq[NB], ci[NB], cn[NB];
+      f32x4 c0[NB], c2[NB], cr[NB], ci[NB], cq[NA], cn[NA];
     };
     // products of one tile from buffer `buf`
     auto products = [&](Acc& a, const _Float16* buf) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) a.c0[nb] = a.c2[nb] = a.cr[nb] = a.cq[nb] = a.ci[nb] = a.cn[nb] = f32x4{};
+      for (int nb = 0; nb < NB; ++nb) {
+        a.c0[nb] = a.c2[nb] = a.cr[nb] = a.ci[nb] = f32x4{};
+        if constexpr (!ACC4) a.cq[nb] = a.cn[nb] = f32x4{};
+      }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const _Float16* f = buf + s * FRAG + lane * 8;
@@ -377,20 +385,35 @@ __device__ __forceinline__ void ws_body(
         const half8 x2 = *reinterpret_cast<const half8*>(f + 1 * PS);
         const half8 xr = *reinterpret_cast<const half8*>(f + 2 * PS);
         const half8 xn = *reinterpret_cast<const half8*>(f + 3 * PS);
+        if constexpr (ACC4) {
+          const half8 xi = __builtin_bit_cast(half8, __builtin_bit_cast(u32x4, xn) ^ 0x80008000u);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          a.c0[nb] = mma16(w0[nb][s], x0, a.c0[nb]);
-          a.cr[nb] = mma16(wr[nb][s], xr, a.cr[nb]);
-          a.c2[nb] = mma16(w2[nb][s], x2, a.c2[nb]);
-          a.ci[nb] = mma16(wi[nb][s], xr, a.ci[nb]);
-          a.cq[nb] = mma16(wi[nb][s], xn, a.cq[nb]);
-          a.cn[nb] = mma16(wr[nb][s], xn, a.cn[nb]);
+          for (int nb = 0; nb < NB; ++nb) {
+            a.c0[nb] = mma16(w0[nb][s], x0, a.c0[nb]);
+            a.cr[nb] = mma16(wr[nb][s], xr, a.cr[nb]);
+            a.ci[nb] = mma16(wi[nb][s], xr, a.ci[nb]);
+            a.c2[nb] = mma16(w2[nb][s], x2, a.c2[nb]);
+            a.cr[nb] = mma16(wi[nb][s], xn, a.cr[nb]);
+            a.ci[nb] = mma16(wr[nb][s], xi, a.ci[nb]);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            a.c0[nb] = mma16(w0[nb][s], x0, a.c0[nb]);
+            a.cr[nb] = mma16(wr[nb][s], xr, a.cr[nb]);
+            a.c2[nb] = mma16(w2[nb][s], x2, a.c2[nb]);
+            a.ci[nb] = mma16(wi[nb][s], xr, a.ci[nb]);
+            a.cq[nb] = mma16(wi[nb][s], xn, a.cq[nb]);
+            a.cn[nb] = mma16(wr[nb][s], xn, a.cn[nb]);
+          }
         }
       }
     };
     // epilogue of this worker's i-th tile: inverse butterfly, bias and
-    // activation in fp32, one rounding, then the staged (PST) or direct store
-    auto epilogue = [&](int i, const Acc& a) {
+    // activation (kind ak, a compile-time constant) in fp32, one rounding,
+    // then the staged (PST) or direct store
+    auto epilogue = [&](auto ak, int i, const Acc& a) {
+      constexpr int AK = decltype(ak)::value;
       const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
       const int64_t rows = N - r0 < 16 ? N - r0 : 16;
       const __amdgpu_buffer_rsrc_t ry = rsrc(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 8));
@@ -401,11 +424,12 @@ __device__ __forceinline__ void ws_body(
         uint32_t o[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          f32x4 v = epi4(a.c0[nb][r], a.c2[nb][r], a.cr[nb][r] + a.cq[nb][r], a.ci[nb][r] - a.cn[nb][r],
-                         bc[nb][r]);
-          if constexpr (ACT) {
+          const float yr = ACC4 ? a.cr[nb][r] : a.cr[nb][r] + a.cq[nb % NA][r];
+          const float yi = ACC4 ? a.ci[nb][r] : a.ci[nb][r] - a.cn[nb % NA][r];
+          f32x4 v = epi4(a.c0[nb][r], a.c2[nb][r], yr, yi, bc[nb][r]);
+          if constexpr (AK != ACT_NONE) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = activate(v[t], act);
+            for (int t = 0; t < 4; ++t) v[t] = activate_k<AK>(v[t]);
           }
           o[2 * r] = pack2(v[0], v[1]);
           o[2 * r + 1] = pack2(v[2], v[3]);
@@ -426,26 +450,72 @@ __device__ __forceinline__ void ws_body(
         }
       }
     };
+    typedef std::integral_constant<int, ACT_NONE> ak_none;
+    typedef std::integral_constant<int, ACT_GELU> ak_gelu;
+    typedef std::integral_constant<int, ACT_GELU_TANH> ak_tanh;
+    // epilogue with the activation chosen once per tile (one uniform branch)
+    auto epilogue_any = [&](int i, const Acc& a) {
+      if constexpr (!ACT) {
+        epilogue(ak_none{}, i, a);
+      } else if (act == ACT_GELU) {
+        epilogue(ak_gelu{}, i, a);
+      } else {
+        epilogue(ak_tanh{}, i, a);
+      }
+    };
+    // Software pipeline step: the products of the next tile (into `nx`, from
+    // buffer `buf`) and the epilogue of tile i (from `cu`) in one basic
+    // block, with the scheduler told to alternate them: every fragment read
+    // first, then one matrix-core product and VALU instructions of the
+    // epilogue in turn.  A wave issues a VALU instruction only every 8-9
+    // cycles but a 16x16x32 product every 16, so the epilogue runs in the
+    // shadow of the products instead of after them.
+    auto pipe_step = [&](Acc& nx, const _Float16* buf, int i, const Acc& cu) {
+      auto one = [&](auto ak) {
+        products(nx, buf);
+        epilogue(ak, i, cu);
+        constexpr int NM = 6 * NB * KS;
+        constexpr int VPM = (decltype(ak)::value != ACT_NONE ? 80 : 20) * NB / NM + 1;
+        // the fragments of step s + 1 are read before the products of step s
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          if (st + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int k = 0; k < 6 * NB; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          }
+        }
+      };
+      if constexpr (!ACT) {
+        one(ak_none{});
+      } else if (act == ACT_GELU) {
+        one(ak_gelu{});
+      } else {
+        one(ak_tanh{});
+      }
+    };
     __syncthreads();  // barrier 0
     if (PIPE) {
       // Software pipeline: between barriers i+1 and i+2 the products of tile
       // i+1 (buffer (i+1) % 2) are issued before the epilogue of tile i, so
       // the matrix cores work while the same wave runs the epilogue's VALU
       // instructions.  Two accumulator sets alternate (loop unrolled twice).
+      // The last iteration of an even tile count multiplies a buffer that
+      // holds no further tile into A; A is not used again.
       Acc A, B;
       products(A, xs);
       int i = 0;
       for (; i + 1 < n_my; i += 2) {
         __syncthreads();  // barrier i+1
-        products(B, xs + BUF);
-        epilogue(i, A);
+        pipe_step(B, xs + BUF, i, A);
         __syncthreads();  // barrier i+2
-        if (i + 2 < n_my) products(A, xs);
-        epilogue(i + 1, B);
+        pipe_step(A, xs, i + 1, B);
       }
       if (i < n_my) {
         __syncthreads();  // barrier n_my
-        epilogue(i, A);
+        epilogue_any(i, A);
       }
       if (PST) __syncthreads();  // barrier n_my + 1: the last tile is staged
     } else {
@@ -454,7 +524,7 @@ __device__ __forceinline__ void ws_body(
       typedef std::integral_constant<int, NC * 64> ctpr_t;
       for (int i = 0; i < n_my; ++i) {
         products(A, xs + cur * BUF);
-        epilogue(i, A);
+        epilogue_any(i, A);
         // SPLIT: the consumers' rows of the tile staged in the previous
         // phase, after this tile's products (the wait at the barrier would
         // otherwise be idle)
@@ -536,22 +606,27 @@ static hipError_t launch_ws_t(const Tuning& tn, const void* x, const void* spec,
                          n_out, n_pad, n_ct, qx, act);                                              \
   } while (0)
 #define EQL_WS_LAUNCH(YP_, G8_, PST_) EQL_WS_LAUNCH4(YP_, G8_, PST_, false)
-  // A fused activation with an output inside the memory-side cache runs the
-  // consumers' epilogue overlapped with the next tile's products (software
-  // pipeline, two accumulator sets; measured on MI355X at C=96, D=384 with
-  // GELU: 21.2 us against 22.8).  Elsewhere it measured no faster (plain
-  // forward) or slower (C=192, D=768; backward_input at K=384, where the
-  // second accumulator set costs occupancy).
-  const bool pipe = act != ACT_NONE && !adjoint && small && pick(tn.ws_pipe, 1) != 0;
-  if (pipe) {
-#define EQL_WS_PIPE_ACT(G8_)                                                                          \
-  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_THROUGH, G8_, true, true, false, true>), grid, \
+  // Software-pipelined consumers (products of tile i+1 interleaved with the
+  // epilogue of tile i, two accumulator sets) for forward outputs inside the
+  // memory-side cache and reductions of up to six steps (the second
+  // accumulator set fits the register budget there).
+  if constexpr (KS <= 6) {
+    const bool pipe = !adjoint && small && pick(tn.ws_pipe, 1) != 0;
+    if (pipe) {
+#define EQL_WS_PIPE_LAUNCH(G8_, ACT_)                                                                  \
+  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_THROUGH, G8_, true, true, false, ACT_>), grid, \
                      block, 0, s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, \
                      n_out, n_pad, n_ct, qx, act)
-    if (g8) EQL_WS_PIPE_ACT(true);
-    else EQL_WS_PIPE_ACT(false);
-#undef EQL_WS_PIPE_ACT
-    return hipGetLastError();
+      if (act != ACT_NONE) {
+        if (g8) EQL_WS_PIPE_LAUNCH(true, true);
+        else EQL_WS_PIPE_LAUNCH(false, true);
+      } else {
+        if (g8) EQL_WS_PIPE_LAUNCH(true, false);
+        else EQL_WS_PIPE_LAUNCH(false, false);
+      }
+#undef EQL_WS_PIPE_LAUNCH
+      return hipGetLastError();
+    }
   }
   // output mode: 0 producer stores (written through small outputs,
   // streamed large ones); 1 consumer stores, streaming
