@@ -652,15 +652,20 @@ def summarize_counters(root, workload):
 
 
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F16",
-                 "SQ_INSTS_VALU_MFMA_MOPS_F32")
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_F16", "SQ_INSTS_VALU_MFMA_F32",
+                 "SQ_BUSY_CYCLES")
 
 
 def summarize_mfma(root):
     """Matrix-core utilisation per kernel from one rocprofv3 --pmc run of
-    MFMA_COUNTERS, averaged over the kernel's dispatches:
-    util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs), with
-    GRBM_GUI_ACTIVE summed over the 8 XCDs and 1024 SIMDs (256 CUs x 4), the
-    ratio rocprofv3's own MfmaUtil metric takes; MFMA flops = MOPS * 512."""
+    MFMA_COUNTERS, averaged over the kernel's dispatches.  Both figures are
+    taken against the dispatch's own duration (End - Start timestamps) at the
+    nominal 2.4 GHz clock of 256 CUs x 4 SIMDs:
+      busy_util = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x 2.4 GHz x duration)
+      flop_util = MOPS x 512 flops / (duration x dense peak of the dtype)
+    They agree when the busy cycles count one SIMD-cycle per 1024 binary16
+    flops (busy_per_inst = 16 for v_mfma_f32_16x16x32_f16).  GRBM_GUI_ACTIVE
+    is listed for reference only: its window is wider than the dispatch."""
     import collections
     import csv
     import glob
@@ -670,21 +675,33 @@ def summarize_mfma(root):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] in MFMA_COUNTERS:
                 per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
-                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                if r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
                     dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    print("# MFMA utilisation per kernel from rocprofv3 counters (MI355X)")
+    clock = 2.4e9
+    simds = 1024.0
+    print("# MFMA utilisation per kernel from rocprofv3 counters (MI355X, 1024 SIMDs, 2.4 GHz)")
     print(f"sources_sha256 all {kernel_sources_hash()}")
-    print(f"{'mfma_util':>9} {'mfma_gflop':>10} {'dispatch_us':>11} {'calls':>5}  kernel")
+    print("# busy_util: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x 2.4 GHz x dispatch duration)")
+    print("# flop_util: MOPS x 512 flops / (dispatch duration x dense peak: 2.5 PFLOP/s binary16,")
+    print("#            157.3 TFLOP/s binary32); busy/inst: busy SIMD-cycles per MFMA instruction")
+    print("# durations are those of the counter run (the profiler slows a dispatch a little)")
+    print(f"{'busy_util':>9} {'flop_util':>9} {'busy/inst':>9} {'mfma_insts':>10} {'gflop':>7} "
+          f"{'disp_us':>8} {'calls':>5}  kernel")
     for k, c in sorted(per.items()):
-        if not c["GRBM_GUI_ACTIVE"] or "eql" not in k:
+        if not dur[k] or "eql" not in k:
             continue
         avg = {n: sum(v) / len(v) for n, v in c.items()}
         busy = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
-        gui = avg["GRBM_GUI_ACTIVE"] / 8.0
-        util = busy / (gui * 1024.0) if gui > 0 else 0.0
-        mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
-        d = sorted(dur[k])[len(dur[k]) // 2]
-        print(f"{util:9.4f} {mops * 512 / 1e9:10.3f} {d:11.2f} {len(c['GRBM_GUI_ACTIVE']):5d}  {k[:100]}")
+        m16 = avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        m32 = avg.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+        insts = avg.get("SQ_INSTS_VALU_MFMA_F16", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_F32", 0.0)
+        d = sum(dur[k]) / len(dur[k])
+        util = busy / (simds * clock * d * 1e-6) if d > 0 else 0.0
+        peak = 2.5e15 if m16 >= m32 else 157.3e12
+        futil = (m16 + m32) * 512 / (d * 1e-6 * peak) if d > 0 else 0.0
+        bpi = busy / insts if insts > 0 else 0.0
+        print(f"{util:9.4f} {futil:9.4f} {bpi:9.2f} {insts:10.0f} {(m16 + m32) * 512 / 1e9:7.3f} "
+              f"{d:8.2f} {len(dur[k]):5d}  {k[:90]}")
 
 
 def summarize_trace(root):

@@ -78,12 +78,14 @@ eqlinear_status_t hip_status(const char* what, hipError_t e) {
 
 extern "C" {
 
-eqlinear_status_t eqconv_plan_create(int64_t C, int64_t D, int64_t k, eqlinear_dtype_t dtype,
+eqlinear_status_t eqconv_plan_create(int64_t C, int64_t D, int64_t k, eqlinear_dtype_t dtype_arg,
                                      eqconv_plan_t* out) {
   if (out == nullptr) return EQL_ERR_INVALID_ARG;
   *out = nullptr;
   if (C <= 0 || D <= 0) return EQL_ERR_INVALID_ARG;
-  if (dtype != EQL_F32 && dtype != EQL_F16) return EQL_ERR_UNSUPPORTED;
+  const int dv = eql::enum_value(dtype_arg);
+  if (dv != EQL_F32 && dv != EQL_F16) return EQL_ERR_UNSUPPORTED;
+  const eqlinear_dtype_t dtype = (eqlinear_dtype_t)dv;
   if (k < 1 || k > MAX_K || k % 2 == 0) return EQL_ERR_UNSUPPORTED;
   if (C % 4 != 0 || D % 4 != 0) return EQL_ERR_UNSUPPORTED;
   if (C > MAX_PATCH_CHANNELS || D > MAX_PATCH_CHANNELS) return EQL_ERR_UNSUPPORTED;
@@ -172,11 +174,11 @@ static eqlinear_status_t run_conv(const eqlinear_plan* inner, const eqconv_plan*
 }
 
 eqlinear_status_t eqconv_forward(eqconv_plan_t p, const void* f, void* y, int64_t N, int64_t H,
-                                 int64_t W, eqlinear_act_t act, void* stream) {
+                                 int64_t W, eqlinear_act_t act_arg, void* stream) {
   if (p == nullptr) return EQL_ERR_INVALID_ARG;
-  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU && act != EQL_ACT_GELU_TANH)
-    return EQL_ERR_INVALID_ARG;
-  return run_conv(p->fwd, p, f, p->C, y, p->D, N, H, W, (int)act, stream);
+  const int av = eql::enum_value(act_arg);
+  if (av != EQL_ACT_NONE && av != EQL_ACT_GELU && av != EQL_ACT_GELU_TANH) return EQL_ERR_INVALID_ARG;
+  return run_conv(p->fwd, p, f, p->C, y, p->D, N, H, W, av, stream);
 }
 
 eqlinear_status_t eqconv_backward_input(eqconv_plan_t p, const void* dy, void* df, int64_t N,

@@ -18,6 +18,18 @@ constexpr int NPAD = 128;
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// The integer a C caller passed for an enumeration parameter.  A C caller may
+// pass any int; reading such a value through the C++ enumeration type is
+// undefined when it lies outside the enumeration's range, so the C ABI
+// validates its enumeration arguments through their bytes.
+template <typename E>
+inline int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enumerations of the C ABI are int-sized");
+  int v;
+  __builtin_memcpy(&v, &e, sizeof(v));
+  return v;
+}
+
 struct SpectraLayout {
   int64_t n_pad;  // padded output-channel count (rows of a plane)
   int64_t k_pad;  // padded reduction-channel count (contiguous)
@@ -43,6 +55,7 @@ struct Tuning {
   int ws_pipe;      // software-pipelined activation epilogue (0/1)
   int ws_out;       // 1: consumers store their fragments (streaming)
   int ws_split;     // split producer/consumer stores beyond the cache (0/1)
+  int ws_wfirst;    // consumers' weight fragments before the second and third tiles (0/1)
   int64_t ws_small_bytes;  // outputs up to this size take the write-through producer stores
   // producer/consumer binary32 forward
   int ws32_off, ws32_nc, ws32_np, ws32_qx, ws32_stream, ws32_pst;

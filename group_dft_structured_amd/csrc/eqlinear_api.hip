@@ -92,6 +92,7 @@ eql::Tuning eql::read_tuning() {
   t.ws_pipe = knob("EQL_WS_PIPE", 0, 1);
   t.ws_out = knob("EQL_WS_OUT", 0, 1);
   t.ws_split = knob("EQL_WS_SPLIT", 0, 1);
+  t.ws_wfirst = knob("EQL_WS_WFIRST", 0, 1);
   const int small_mb = knob("EQL_WS_SMALL_MB", 0, 1 << 20);
   t.ws_small_bytes = small_mb >= 0 ? (int64_t)small_mb << 20 : (int64_t)128 << 20;
   t.ws32_off = knob("EQL_NO_WS32", 0, 1);
@@ -160,8 +161,8 @@ eqlinear_status_t scratch_address(void** out) {
 
 extern "C" {
 
-const char* eqlinear_status_string(eqlinear_status_t st) {
-  switch (st) {
+const char* eqlinear_status_string(eqlinear_status_t status) {
+  switch (eql::enum_value(status)) {
     case EQL_OK: return "ok";
     case EQL_ERR_INVALID_ARG: return "invalid argument";
     case EQL_ERR_UNSUPPORTED: return "unsupported group, group order or dtype";
@@ -178,14 +179,23 @@ const char* eqlinear_last_error(void) { return g_last_error; }
 
 eqlinear_status_t eqlinear_plan_create(int64_t C, int64_t D, int64_t T, eqlinear_dtype_t dtype,
                                        eqlinear_plan_t* out) {
-  return eqlinear_plan_create_group(C, D, EQL_GROUP_CYCLIC, T, dtype, out);
+  if (out == nullptr) return EQL_ERR_INVALID_ARG;
+  *out = nullptr;
+  const int dv = eql::enum_value(dtype);
+  if (dv != EQL_F32 && dv != EQL_F16) return EQL_ERR_UNSUPPORTED;
+  return eqlinear_plan_create_group(C, D, EQL_GROUP_CYCLIC, T, (eqlinear_dtype_t)dv, out);
 }
 
-eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_group_t group,
-                                             int64_t n, eqlinear_dtype_t dtype,
+eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_group_t group_arg,
+                                             int64_t n, eqlinear_dtype_t dtype_arg,
                                              eqlinear_plan_t* out) {
   if (out == nullptr) return EQL_ERR_INVALID_ARG;
   *out = nullptr;
+  const int gv = eql::enum_value(group_arg), dv = eql::enum_value(dtype_arg);
+  if ((gv != EQL_GROUP_CYCLIC && gv != EQL_GROUP_DIHEDRAL) || (dv != EQL_F32 && dv != EQL_F16))
+    return EQL_ERR_UNSUPPORTED;
+  const eqlinear_group_t group = (eqlinear_group_t)gv;
+  const eqlinear_dtype_t dtype = (eqlinear_dtype_t)dv;
   int64_t T = 0;
   if (group == EQL_GROUP_CYCLIC) {
     if (n < MIN_T || n > MAX_T) return EQL_ERR_UNSUPPORTED;
@@ -196,7 +206,6 @@ eqlinear_status_t eqlinear_plan_create_group(int64_t C, int64_t D, eqlinear_grou
   } else {
     return EQL_ERR_UNSUPPORTED;
   }
-  if (dtype != EQL_F32 && dtype != EQL_F16) return EQL_ERR_UNSUPPORTED;
   if (C <= 0 || D <= 0 || C > MAX_CHANNELS || D > MAX_CHANNELS) return EQL_ERR_INVALID_ARG;
   eqlinear_plan* p = new (std::nothrow) eqlinear_plan;
   if (p == nullptr) return EQL_ERR_ALLOC;
@@ -336,9 +345,10 @@ eqlinear_status_t eqlinear_forward(eqlinear_plan_t p, const void* x, void* y, in
 }
 
 eqlinear_status_t eqlinear_forward_act(eqlinear_plan_t p, const void* x, void* y, int64_t N,
-                                       eqlinear_act_t act, void* stream) {
-  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU && act != EQL_ACT_GELU_TANH)
-    return EQL_ERR_INVALID_ARG;
+                                       eqlinear_act_t act_arg, void* stream) {
+  const int av = eql::enum_value(act_arg);
+  if (av != EQL_ACT_NONE && av != EQL_ACT_GELU && av != EQL_ACT_GELU_TANH) return EQL_ERR_INVALID_ARG;
+  const eqlinear_act_t act = (eqlinear_act_t)av;
   eqlinear_status_t st = check_gemm_args(p, x, y, N);
   if (st != EQL_OK || N == 0) return st;
   if (p->inner != nullptr) return eqlinear_forward_act(p->inner, x, y, N, act, stream);

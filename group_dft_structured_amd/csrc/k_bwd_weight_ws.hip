@@ -51,7 +51,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_bws(const void* base, uin
 // LDS per buffer: plane p, operand block b (dy blocks first, then x blocks):
 // one 1 KB fragment at (p*NBLK + b)*520 halves; lane (i16, g) of the operand
 // reads the 16 bytes at (g*16 + i16)*16 = rows 8g..8g+7 of column i16.
-template <int NWD, int NWC, int DB, int CB, int NP>
+template <int NWD, int NWC, int DB, int CB, int NP, int KSUB>
 __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
     const _Float16* __restrict__ x, const _Float16* __restrict__ dy, float* __restrict__ part,
     float* __restrict__ part_b, int N, int C, int D, int d_pad, int c_pad, int rows_per_split,
@@ -64,16 +64,19 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
   // blocks and two row groups hits every bank once.
   constexpr int FRAG = 520;                 // halves between consecutive blocks
   constexpr int PSTR = NBLK * FRAG;         // plane stride (halves)
-  constexpr int BUF = 4 * PSTR;             // halves per buffer
-  constexpr int DUNITS = (BD / 2) * 8;      // (column pair, row quartet) units of dy per step
-  constexpr int UNITS = (BD / 2 + BC / 2) * 8;
+  constexpr int SUB = 4 * PSTR;             // halves per 32-row sub-step
+  constexpr int BUF = KSUB * SUB;           // halves per buffer
+  constexpr int SROWS = 32 * KSUB;          // rows per step (one barrier each)
+  constexpr int QUARTS = SROWS / 4;         // row quartets per step
+  constexpr int DUNITS = (BD / 2) * QUARTS; // (column pair, row quartet) units of dy per step
+  constexpr int UNITS = (BD / 2 + BC / 2) * QUARTS;
   constexpr int PT = NP * 64;
   constexpr int UPT = (UNITS + PT - 1) / PT;
   constexpr bool EXACT = UNITS % PT == 0;
   constexpr int DUMMY = EXACT ? 0 : PT * 4;  // halves: one 8-byte slot per producer thread
   static_assert(DUNITS % 64 == 0, "dy and x units split at a wave boundary");
   __shared__ __attribute__((aligned(16))) _Float16 lds[2 * BUF + DUMMY];
-  __shared__ float bred[8][BD];
+  __shared__ float bred[QUARTS][BD];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -87,7 +90,7 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
   const int d0 = dt * BD, c0 = ct * BC;
   const int r_begin = split * rows_per_split;
   const int r_end = min(N, r_begin + rows_per_split);
-  const int nsteps = (r_end - r_begin + 31) / 32;
+  const int nsteps = (r_end - r_begin + SROWS - 1) / SROWS;
 
   if (wave >= NC) {
     // =========================== producer waves ===========================
@@ -114,12 +117,12 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
       goff[k] = ok ? (uint32_t)((quart * 4 * width + col) * 8) : 0x7FFFFFF0u;
       const int lc = 2 * cp;
       const int blk = (is_dy ? 0 : DBLK) + (lc >> 4);
-      const int gq = quart >> 1, hf = quart & 1;
-      loff[k] = (EXACT || u < UNITS) ? blk * FRAG + (gq * 16 + (lc & 15)) * 8 + hf * 4 : -1;
+      const int sub = quart >> 3, gq = (quart & 7) >> 1, hf = quart & 1;
+      loff[k] = (EXACT || u < UNITS) ? sub * SUB + blk * FRAG + (gq * 16 + (lc & 15)) * 8 + hf * 4 : -1;
     }
     auto load_step = [&](half8 (&raw)[UPT][4], int st) {
-      const int r0 = r_begin + st * 32;
-      const int rows = r0 < r_end ? min(32, r_end - r0) : 0;
+      const int r0 = r_begin + st * SROWS;
+      const int rows = r0 < r_end ? min(SROWS, r_end - r0) : 0;
       const int rb = rows > 0 ? r0 : 0;
       const __amdgpu_buffer_rsrc_t rdy = rsrc_bws(dy + (int64_t)rb * D * 4, (uint32_t)rows * D * 8);
       const __amdgpu_buffer_rsrc_t rx = rsrc_bws(x + (int64_t)rb * C * 4, (uint32_t)rows * C * 8);
@@ -263,7 +266,7 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
         for (int p = 0; p < 4; ++p) acc[a][b][p] = f32x4{};
         accn[a][b] = f32x4{};
       }
-    auto compute_step = [&](const _Float16* buf) {
+    auto compute_sub = [&](const _Float16* buf) {
       half8 gf[DB][4];
 #pragma unroll
       for (int a = 0; a < DB; ++a)
@@ -287,6 +290,10 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
           accn[a][b] = mma16(gf[a][2], xi, accn[a][b]);
         }
       }
+    };
+    auto compute_step = [&](const _Float16* buf) {
+#pragma unroll
+      for (int sb = 0; sb < KSUB; ++sb) compute_sub(buf + sb * SUB);
     };
     __syncthreads();  // barrier 0
     int cur = 0;
@@ -313,13 +320,13 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
       }
   }
 
-  // ---- bias partial: fixed-order sum over the eight row quartets ----------
+  // ---- bias partial: fixed-order sum over the row quartets of a step ------
   if (ct == 0) {
     __syncthreads();
     for (int j = tid; j < BD; j += (NC + NP) * 64) {
       float s = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) s += bred[q][j];
+      for (int q = 0; q < QUARTS; ++q) s += bred[q][j];
       part_b[(int64_t)split * d_pad + d0 + j] = s;
     }
   }
@@ -401,18 +408,18 @@ hipError_t launch_bwd_weight_finish(const float* part, const float* part_b, floa
 
 // ---------------------------------------------------------------------------
 struct BwsCfg {
-  int nwd, nwc, db, cb, np;
+  int nwd, nwc, db, cb, np, ksub;
   int bd() const { return nwd * db * 16; }
   int bc() const { return nwc * cb * 16; }
 };
 
 static const BwsCfg kBwsCfgs[] = {
-    {2, 2, 1, 3, 8},   // 0: 32 x 96 tiles, 4 consumers + 8 producers
-    {1, 2, 1, 3, 7},   // 1: 16 x 96 tiles, 2 consumers + 7 producers
-    {2, 2, 1, 3, 4},   // 2: 32 x 96 tiles, 4 consumers + 4 producers
-    {2, 2, 2, 3, 8},   // 3: 64 x 96 tiles, 4 consumers of 32 x 48 + 8 producers
-    {2, 2, 2, 3, 4},   // 4: 64 x 96 tiles, 4 consumers of 32 x 48 + 4 producers
-    {2, 2, 2, 3, 6},   // 5: 64 x 96 tiles, 4 consumers of 32 x 48 + 6 producers
+    {2, 2, 1, 3, 8, 1},   // 0: 32 x 96 tiles, 4 consumers + 8 producers, 32-row steps
+    {1, 2, 1, 3, 7, 1},   // 1: 16 x 96 tiles, 2 consumers + 7 producers
+    {2, 2, 1, 3, 4, 1},   // 2: 32 x 96 tiles, 4 consumers + 4 producers
+    {2, 2, 2, 3, 8, 1},   // 3: 64 x 96 tiles, 4 consumers of 32 x 48 + 8 producers
+    {2, 2, 1, 3, 8, 2},   // 4: as 0 with 64-row steps
+    {1, 2, 1, 3, 7, 2},   // 5: as 1 with 64-row steps
 };
 
 bool bws_supported(const eqlinear_plan* p) {
@@ -447,11 +454,12 @@ static BwsDims bws_dims(const eqlinear_plan* p, int64_t N) {
   const int T = m.n_dt * m.n_ct;
   // about one work-group per CU (one fits per CU), splits of whole 32-row steps
   int64_t S = p->tune.bws_s > 0 ? p->tune.bws_s : (256 / T > 0 ? 256 / T : 1);
-  const int64_t steps = (N + 31) / 32;
+  const int64_t srows = 32 * m.cfg.ksub;
+  const int64_t steps = (N + srows - 1) / srows;
   if (S > steps) S = steps;
   if (S < 1) S = 1;
   const int64_t steps_per = (steps + S - 1) / S;
-  m.R = steps_per * 32;
+  m.R = steps_per * srows;
   m.S = (N + m.R - 1) / m.R;
   if (m.S < 1) m.S = 1;
   m.per_xcd = (int)((m.S * T + 7) / 8);
@@ -464,11 +472,11 @@ size_t bws_workspace(const eqlinear_plan* p, int64_t N) {
   return (size_t)m.S * (size_t)(4 * m.c_pad * m.d_pad + m.d_pad) * sizeof(float);
 }
 
-template <int NWD, int NWC, int DB, int CB, int NP>
+template <int NWD, int NWC, int DB, int CB, int NP, int KSUB>
 static hipError_t launch_bws_t(const BwsDims& m, const eqlinear_plan* p, const void* x, const void* dy,
                                float* part, float* part_b, int64_t N, hipStream_t s) {
   const unsigned blocks = (unsigned)(8 * m.per_xcd);
-  hipLaunchKernelGGL((k_bwd_weight_ws<NWD, NWC, DB, CB, NP>), dim3(blocks), dim3((NWD * NWC + NP) * 64), 0,
+  hipLaunchKernelGGL((k_bwd_weight_ws<NWD, NWC, DB, CB, NP, KSUB>), dim3(blocks), dim3((NWD * NWC + NP) * 64), 0,
                      s, (const _Float16*)x, (const _Float16*)dy, part, part_b, (int)N, (int)p->C, (int)p->D,
                      (int)m.d_pad, (int)m.c_pad, (int)m.R, m.n_dt, m.n_ct, (int)m.S, m.per_xcd);
   return hipGetLastError();
@@ -481,13 +489,12 @@ hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, flo
   float* part_b = part + m.S * 4 * m.c_pad * m.d_pad;
   hipError_t e = hipErrorNotSupported;
   switch (bws_sel(p)) {
-    case 1: e = launch_bws_t<1, 2, 1, 3, 7>(m, p, x, dy, part, part_b, N, s); break;
-    case 2: e = launch_bws_t<2, 2, 1, 3, 4>(m, p, x, dy, part, part_b, N, s); break;
-    case 3: e = launch_bws_t<2, 2, 2, 3, 8>(m, p, x, dy, part, part_b, N, s); break;
-    case 4: e = launch_bws_t<2, 2, 2, 3, 4>(m, p, x, dy, part, part_b, N, s); break;
-    case 5: e = launch_bws_t<2, 2, 2, 3, 6>(m, p, x, dy, part, part_b, N, s); break;
-
-    default: e = launch_bws_t<2, 2, 1, 3, 8>(m, p, x, dy, part, part_b, N, s); break;
+    case 1: e = launch_bws_t<1, 2, 1, 3, 7, 1>(m, p, x, dy, part, part_b, N, s); break;
+    case 2: e = launch_bws_t<2, 2, 1, 3, 4, 1>(m, p, x, dy, part, part_b, N, s); break;
+    case 3: e = launch_bws_t<2, 2, 2, 3, 8, 1>(m, p, x, dy, part, part_b, N, s); break;
+    case 4: e = launch_bws_t<2, 2, 1, 3, 8, 2>(m, p, x, dy, part, part_b, N, s); break;
+    case 5: e = launch_bws_t<1, 2, 1, 3, 7, 2>(m, p, x, dy, part, part_b, N, s); break;
+    default: e = launch_bws_t<2, 2, 1, 3, 8, 1>(m, p, x, dy, part, part_b, N, s); break;
   }
   if (e != hipSuccess) return e;
   return launch_bwd_weight_finish(part, part_b, dW, dbias, p->C, p->D, m.d_pad, m.c_pad, m.S, s);

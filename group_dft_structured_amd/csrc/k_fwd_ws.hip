@@ -78,7 +78,8 @@ template <int NC, int NP, int NB, int KS, int YP, bool G8, bool STAGGER, bool PS
           bool SPLIT, bool ACT = false>
 __device__ __forceinline__ void ws_body(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
-    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
+    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act,
+    int wfirst) {
   constexpr int BN = NC * NB * 16;
   constexpr int KP = KS * 32;
   constexpr int FRAG = 512;                   // halves per fragment
@@ -272,9 +273,18 @@ __device__ __forceinline__ void ws_body(
       // prefetch burst of the grid
       __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): expcnt, lgkmcnt not waited
     }
-    load_tile(rb, 1);
-    load_tile(rc, 2);
-    store_tile(ra, xs);
+    if (wfirst) {
+      // weights first: tile 0 is transformed, then the producers wait for
+      // the consumers' weight fragments to arrive before requesting more
+      store_tile(ra, xs);
+      __syncthreads();  // barrier W
+      load_tile(rb, 1);
+      load_tile(rc, 2);
+    } else {
+      load_tile(rb, 1);
+      load_tile(rc, 2);
+      store_tile(ra, xs);
+    }
     load_tile(ra, 3);
     __syncthreads();  // barrier 0: tile 0 is in buffer 0
     int cur = 1;      // buffer of the next tile
@@ -496,6 +506,10 @@ __device__ __forceinline__ void ws_body(
         one(ak_tanh{});
       }
     };
+    if (wfirst) {
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): the weights are in
+      __syncthreads();  // barrier W
+    }
     __syncthreads();  // barrier 0
     if (PIPE) {
       // Software pipeline: between barriers i+1 and i+2 the products of tile
@@ -548,17 +562,18 @@ template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE, 
           bool ACT = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
-    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
+    _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act,
+    int wfirst) {
   ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE, SPLIT, ACT>(x, spec, bias, y, N, K, n_out, n_pad,
-                                                               n_ct, Qx, act);
+                                                               n_ct, Qx, act, wfirst);
 }
 
 template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE, bool SPLIT>
 __global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
     const _Float16* __restrict__ dy, const _Float16* __restrict__ spec, const float* __restrict__ bias,
-    _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx) {
+    _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int wfirst) {
   ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE, SPLIT>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct,
-                                                          Qx, ACT_NONE);
+                                                          Qx, ACT_NONE, wfirst);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,6 +594,7 @@ static hipError_t launch_ws_t(const Tuning& tn, const void* x, const void* spec,
   if (qx > max_qx) qx = (int)(max_qx < 1 ? 1 : max_qx);
   qx = pick(tn.ws_qx, qx);
   const unsigned blocks = (unsigned)(8 * n_ct * qx);
+  const int wfirst = pick(tn.ws_wfirst, 0);
   // Output path (measured on MI355X, binary16): the producers store whole
   // rows, written through the L2 while the output fits well inside the
   // 256 MB memory-side cache (C=96, D=384, N=12608: 11.2 us against 13.3
@@ -595,15 +611,15 @@ static hipError_t launch_ws_t(const Tuning& tn, const void* x, const void* spec,
     if (adjoint)                                                                                    \
       hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, false, SPLIT_>), grid, block, 0, \
                          s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K,   \
-                         n_out, n_pad, n_ct, qx);                                                   \
+                         n_out, n_pad, n_ct, qx, wfirst);                                           \
     else if (act != ACT_NONE)                                                                       \
       hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, false, SPLIT_, true>), grid, block, \
                          0, s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, \
-                         n_out, n_pad, n_ct, qx, act);                                              \
+                         n_out, n_pad, n_ct, qx, act, wfirst);                                      \
     else                                                                                            \
       hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, false, SPLIT_>), grid, block, 0, \
                          s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K,   \
-                         n_out, n_pad, n_ct, qx, act);                                              \
+                         n_out, n_pad, n_ct, qx, act, wfirst);                                      \
   } while (0)
 #define EQL_WS_LAUNCH(YP_, G8_, PST_) EQL_WS_LAUNCH4(YP_, G8_, PST_, false)
   // Software-pipelined consumers (products of tile i+1 interleaved with the
@@ -613,16 +629,21 @@ static hipError_t launch_ws_t(const Tuning& tn, const void* x, const void* spec,
   if constexpr (KS <= 6) {
     const bool pipe = !adjoint && small && pick(tn.ws_pipe, 1) != 0;
     if (pipe) {
-#define EQL_WS_PIPE_LAUNCH(G8_, ACT_)                                                                  \
-  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, POLICY_THROUGH, G8_, true, true, false, ACT_>), grid, \
-                     block, 0, s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, \
-                     n_out, n_pad, n_ct, qx, act)
+#define EQL_WS_PIPE_LAUNCH(YP_, G8_, PST_, ACT_)                                                       \
+  hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, true, false, ACT_>), grid, block, 0, s, \
+                     (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out,     \
+                     n_pad, n_ct, qx, act, wfirst)
+      // consumer stores (EQL_WS_OUT=1) or the producers' whole-row stores
+      const bool cst = pick(tn.ws_out, 0) == 1;
       if (act != ACT_NONE) {
-        if (g8) EQL_WS_PIPE_LAUNCH(true, true);
-        else EQL_WS_PIPE_LAUNCH(false, true);
+        if (g8) EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, true, true, true);
+        else EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, false, true, true);
+      } else if (cst) {
+        if (g8) EQL_WS_PIPE_LAUNCH(POLICY_STREAM, true, false, false);
+        else EQL_WS_PIPE_LAUNCH(POLICY_STREAM, false, false, false);
       } else {
-        if (g8) EQL_WS_PIPE_LAUNCH(true, false);
-        else EQL_WS_PIPE_LAUNCH(false, false);
+        if (g8) EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, true, true, false);
+        else EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, false, true, false);
       }
 #undef EQL_WS_PIPE_LAUNCH
       return hipGetLastError();

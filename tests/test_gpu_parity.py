@@ -255,8 +255,8 @@ BW_PATHS = {
     "ws_32x96_np4": {"EQL_BWS_CFG": "2"},
 
     "ws_64x96_np8": {"EQL_BWS_CFG": "3"},
-    "ws_64x96_np4": {"EQL_BWS_CFG": "4"},
-    "ws_64x96_np6": {"EQL_BWS_CFG": "5"},
+    "ws_32x96_64rows": {"EQL_BWS_CFG": "4"},
+    "ws_16x96_64rows": {"EQL_BWS_CFG": "5"},
     "ws_few_splits": {"EQL_BWS_S": "3"},
     "tiled": {"EQL_BW_TILED": "1"},
 }
