@@ -62,8 +62,8 @@ struct Tuning {
   // general tiled kernel: tile shape
   int gemm_tile;
   // backward_weight: producer/consumer kernel off, tiled kernel forced,
-  // tile configuration, split count
-  int bws_off, bw_tiled, bws_cfg, bws_s;
+  // split count
+  int bws_off, bw_tiled, bws_s;
   // generic group kernels: tile shape; p4 through them; weight-gradient
   // tile edge and work-group target; p4m on the p4 kernels
   int cyc_tile, cyclic_p4, cyc_bw_tile, cyc_bw_wgs, p4m_pairs;
@@ -115,12 +115,7 @@ int64_t bwd_weight_rows_per_split(const eqlinear_plan* p, int64_t N);
 size_t bwd_weight_workspace_bytes(const eqlinear_plan* p, int64_t N);
 
 
-// Fixed-order sum of S fp32 partial planes [S][4][c_pad][d_pad] (+ bias
-// partials [S][d_pad]) and the inverse butterfly into dW [D][C][4], dbias [D].
-hipError_t launch_bwd_weight_finish(const float* part, const float* part_b, float* dW, float* dbias,
-                                    int64_t C, int64_t D, int64_t d_pad, int64_t c_pad, int64_t S,
-                                    hipStream_t s);
-// Producer/consumer backward-weight path (binary16, even channel counts, C <= 96).
+// Producer/consumer backward-weight path (binary16, even channel counts).
 bool bws_supported(const eqlinear_plan* p);
 size_t bws_workspace(const eqlinear_plan* p, int64_t N);
 hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, float* dW, float* dbias,

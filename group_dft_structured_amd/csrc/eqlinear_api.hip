@@ -104,7 +104,6 @@ eql::Tuning eql::read_tuning() {
   t.gemm_tile = knob("EQL_GEMM_TILE", 0, 4);
   t.bws_off = knob("EQL_NO_BWS", 0, 1);
   t.bw_tiled = knob("EQL_BW_TILED", 0, 1);
-  t.bws_cfg = knob("EQL_BWS_CFG", 0, 5);
   t.bws_s = knob("EQL_BWS_S", 1, 1 << 20);
   t.cyc_tile = knob("EQL_CYC_TILE", 0, 3);
   t.cyclic_p4 = knob("EQL_CYCLIC_P4", 0, 1);

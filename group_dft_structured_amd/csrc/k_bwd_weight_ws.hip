@@ -11,22 +11,22 @@
 // Work decomposition: the output (D x C, four planes) is cut into tiles of
 // BD x BC channels and the rows into S splits; work-group (split, tile)
 // reduces its rows for its tile with fp32 matrix-core accumulators and
-// writes one fp32 partial per plane; the second pass (the finish kernel of
-// the matrix-core path) sums the S partials in split order and applies the
-// inverse butterfly.  Consecutive (split, tile) pairs run on one XCD, so the
-// x rows that the tiles of a split all read come from that XCD's L2.
+// writes one fp32 partial per plane; the finish kernel sums the S partials in
+// split order and applies the inverse butterfly.  Consecutive (split, tile)
+// pairs run on one XCD, so the x rows that the tiles of a split all read come
+// from that XCD's L2.
 //
 // Roles inside a work-group, one barrier per 32-row step:
 //  * NP producer waves load each step's dy and x rows (range-checked 16-byte
 //    buffer loads, three steps ahead in a register ring), apply the length-4
-//    butterfly in packed binary16 into the scaled planes (X0/4 and X2/4 as
-//    the sum and difference of the rounded quarter pair sums (x0 + x2)/4 and
-//    (x1 + x3)/4, Xr/2 = (x0 - x2)/2, Xi/2 = (x3 - x1)/2) and write the four
-//    planes to LDS in matrix-core fragment order, transposing rows into the
-//    operand's K dimension; dbias is summed from exact fp32 sums of dy over
-//    the group;
+//    butterfly on the matrix cores (below) into the scaled planes X0/4, X2/4,
+//    Xr/2, Xi/2 (eql_device.h) and write them to LDS in matrix-core fragment
+//    order with the rows along the fragments' k; dbias is summed in fp32 from
+//    the X0 plane before its rounding;
 //  * NWD x NWC consumer waves own DB x CB blocks of 16 x 16 outputs and run
-//    v_mfma_f32_16x16x32_f16 on fragments read from LDS (K = 32 rows).
+//    v_mfma_f32_16x16x32_f16 on fragments read from LDS (k = 32 rows).
+#include <type_traits>
+
 #include "eql_device.h"
 #include "eql_internal.h"
 
@@ -35,8 +35,6 @@ namespace eql {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -48,10 +46,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_bws(const void* base, uin
 
 }  // namespace
 
-// LDS per buffer: plane p, operand block b (dy blocks first, then x blocks):
-// one 1 KB fragment at (p*NBLK + b)*520 halves; lane (i16, g) of the operand
-// reads the 16 bytes at (g*16 + i16)*16 = rows 8g..8g+7 of column i16.
-template <int NWD, int NWC, int DB, int CB, int NP, int KSUB>
+// Producer unit: one 16-byte load per lane covering four rows x 32 channels,
+// lane (j, g) reading row g, channels 2j and 2j + 1 (so four consecutive
+// lanes read 64 contiguous bytes; a layout with consecutive lanes on
+// different rows costs the address unit four times as many cycles).  These
+// loads are the B operand of v_mfma_f32_16x16x32_f16 (column j, k = 8g .. 8g+7
+// = two channels x four group values of row g); the A operand holds the
+// butterfly, A[(p, r)][(g, e', s)] = F[p][s] when g = r and e' = e, for the
+// channel e of the pair (two instructions, e = 0, 1), with F the scaled rows
+// (1, 1, 1, 1)/4, (1, -1, 1, -1)/4, (1, 0, -1, 0)/2, (0, -1, 0, 1)/2 giving
+// X0/4, X2/4, Xr/2, Xi/2.  The result in lane (j, p) is plane p of channel
+// 2j + e for the four rows: four consecutive reduction indices of one operand
+// column, the layout of the matrix-core operand whose k runs over rows.  Two
+// such blocks fill one 16-byte fragment slot (eight rows), written with one
+// LDS store.  The products are exact in fp32 and each plane value is rounded
+// once to binary16.
+template <int NWD, int NWC, int DB, int CB, int NP>
 __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
     const _Float16* __restrict__ x, const _Float16* __restrict__ dy, float* __restrict__ part,
     float* __restrict__ part_b, int N, int C, int D, int d_pad, int c_pad, int rows_per_split,
@@ -59,28 +69,23 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
   constexpr int NC = NWD * NWC;
   constexpr int BD = NWD * DB * 16, BC = NWC * CB * 16;
   constexpr int DBLK = BD / 16, CBLK = BC / 16, NBLK = DBLK + CBLK;
-  // Fragments are 1 KB; consecutive blocks sit 1040 bytes apart, which moves
-  // each block by four LDS banks, so one producer instruction writing two
-  // blocks and two row groups hits every bank once.
-  constexpr int FRAG = 520;                 // halves between consecutive blocks
+  // 16-column fragments (1 KB) 1040 bytes apart: the 16 lanes of one store
+  // (channels 2j + e, j = 0..15, of two blocks) then cover the 64 banks once
+  constexpr int FRAG = 520;
   constexpr int PSTR = NBLK * FRAG;         // plane stride (halves)
-  constexpr int SUB = 4 * PSTR;             // halves per 32-row sub-step
-  constexpr int BUF = KSUB * SUB;           // halves per buffer
-  constexpr int SROWS = 32 * KSUB;          // rows per step (one barrier each)
-  constexpr int QUARTS = SROWS / 4;         // row quartets per step
-  constexpr int DUNITS = (BD / 2) * QUARTS; // (column pair, row quartet) units of dy per step
-  constexpr int UNITS = (BD / 2 + BC / 2) * QUARTS;
-  constexpr int PT = NP * 64;
-  constexpr int UPT = (UNITS + PT - 1) / PT;
-  constexpr bool EXACT = UNITS % PT == 0;
-  constexpr int DUMMY = EXACT ? 0 : PT * 4;  // halves: one 8-byte slot per producer thread
-  static_assert(DUNITS % 64 == 0, "dy and x units split at a wave boundary");
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * BUF + DUMMY];
-  __shared__ float bred[QUARTS][BD];
+  constexpr int BUF = 4 * PSTR;             // halves per 32-row step
+  static_assert(BD % 32 == 0 && BC % 32 == 0, "32-channel producer units");
+  constexpr int DCH = BD / 32, XCH = BC / 32;  // 32-channel units of dy and x per step
+  // HALVES producer waves share one 32-channel unit, each taking 8 / HALVES
+  // of the four-row blocks of a step
+  constexpr int HALVES = NP / (DCH + XCH);
+  static_assert(HALVES * (DCH + XCH) == NP && (HALVES == 1 || HALVES == 2), "producer waves per unit");
+  constexpr int NBK = 8 / HALVES;  // four-row blocks per producer wave and step
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * BUF];
+  __shared__ float bred[HALVES][BD];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  // work-group -> (split, tile): XCD x runs pairs [x*per_xcd, (x+1)*per_xcd)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wgid = blockIdx.x, xcd = wgid & 7, slot = wgid >> 3;
   const int T = n_dt * n_ct;
   const int L = xcd * per_xcd + slot;
@@ -90,173 +95,138 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
   const int d0 = dt * BD, c0 = ct * BC;
   const int r_begin = split * rows_per_split;
   const int r_end = min(N, r_begin + rows_per_split);
-  const int nsteps = (r_end - r_begin + SROWS - 1) / SROWS;
+  const int nsteps = (r_end - r_begin + 31) / 32;
+  const int j = lane & 15, g = lane >> 4;
 
   if (wave >= NC) {
     // =========================== producer waves ===========================
-    const int pw = wave - NC, ptid = tid - NC * 64;
-    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
-    // unit u = k*PT + ptid -> operand (dy for u < DUNITS), column pair, row
-    // quartet; the operand is the same for a whole wave
-    auto unit_is_dy = [&](int k) { return k * PT + pw * 64 < DUNITS; };
-    // per-unit constants (the same every step): global byte offset of the
-    // unit's first row within a step (or an out-of-range offset), and the
-    // LDS offset of its first fragment word (or the dummy slot)
-    uint32_t goff[UPT];
-    int loff[UPT];
+    const int pw = wave - NC;
+    auto produce = [&](auto dy_c) {
+      constexpr bool IS_DY = decltype(dy_c)::value;
+      const int width = IS_DY ? D : C;
+      const int pu = pw / HALVES, hp = pw % HALVES;  // unit and part of it
+      const int o = IS_DY ? pu : pu - DCH;           // unit within the operand's tile columns
+      // butterfly operand (A) of lane (i16 = j, g) for channel e = 0, 1 of each pair
+      half8 bf[2];
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-      const int u = k * PT + ptid;
-      const bool is_dy = unit_is_dy(k);
-      const int v = is_dy ? u : u - DUNITS;
-      const int cp = is_dy ? v % (BD / 2) : v % (BC / 2);
-      const int quart = is_dy ? v / (BD / 2) : v / (BC / 2);
-      const int col = (is_dy ? d0 : c0) + 2 * cp;
-      const int width = is_dy ? D : C;
-      const bool ok = (EXACT || u < UNITS) && col < width;
-      goff[k] = ok ? (uint32_t)((quart * 4 * width + col) * 8) : 0x7FFFFFF0u;
-      const int lc = 2 * cp;
-      const int blk = (is_dy ? 0 : DBLK) + (lc >> 4);
-      const int sub = quart >> 3, gq = (quart & 7) >> 1, hf = quart & 1;
-      loff[k] = (EXACT || u < UNITS) ? sub * SUB + blk * FRAG + (gq * 16 + (lc & 15)) * 8 + hf * 4 : -1;
-    }
-    auto load_step = [&](half8 (&raw)[UPT][4], int st) {
-      const int r0 = r_begin + st * SROWS;
-      const int rows = r0 < r_end ? min(SROWS, r_end - r0) : 0;
-      const int rb = rows > 0 ? r0 : 0;
-      const __amdgpu_buffer_rsrc_t rdy = rsrc_bws(dy + (int64_t)rb * D * 4, (uint32_t)rows * D * 8);
-      const __amdgpu_buffer_rsrc_t rx = rsrc_bws(x + (int64_t)rb * C * 4, (uint32_t)rows * C * 8);
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int k = 0; k < UPT; ++k) {
-        const bool is_dy = unit_is_dy(k);
-        const uint32_t rstride = (uint32_t)(is_dy ? D : C) * 8;  // bytes per row
+        for (int t = 0; t < 8; ++t) {
+          const int pl = j >> 2, rr = j & 3, sv = t & 3;
+          float v = 0.f;
+          if (g == rr && (t >> 2) == e) {
+            if (pl == 0) v = 0.25f;
+            else if (pl == 1) v = (sv & 1) ? -0.25f : 0.25f;
+            else if (pl == 2) v = sv == 0 ? 0.5f : sv == 2 ? -0.5f : 0.f;
+            else v = sv == 3 ? 0.5f : sv == 1 ? -0.5f : 0.f;
+          }
+          bf[e][t] = (_Float16)v;
+        }
+      // the lane's load: row g of each four-row block, channels 2j, 2j + 1 of
+      // the unit (an out-of-range offset past the channels)
+      const int col = (IS_DY ? d0 : c0) + 32 * o + 2 * j;
+      const uint32_t blk_off = 4u * (uint32_t)width * 8u;  // next four-row block
+      const uint32_t goff =
+          col < width ? (uint32_t)(g * width + col) * 8u + (uint32_t)(hp * NBK) * blk_off : 0x7FFFFFF0u;
+      // LDS slot of lane (j, p = g), channel 2j + e, slot 0 (slot q adds q * 16 * 8)
+      int lslot[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          raw[k][e] = __builtin_bit_cast(
-              half8, __builtin_amdgcn_raw_buffer_load_b128(is_dy ? rdy : rx, goff[k] + e * rstride, 0, 0));
+      for (int e = 0; e < 2; ++e) {
+        const int cc = 32 * o + 2 * j + e;
+        const int blk = (IS_DY ? 0 : DBLK) + (cc >> 4);
+        lslot[e] = g * PSTR + blk * FRAG + (hp * (NBK / 2) * 16 + (cc & 15)) * 8;
       }
-    };
-    float bsum[UPT][2];
+      const _Float16* const src = IS_DY ? dy : x;
+      auto load_step = [&](half8 (&raw)[NBK], int st) {
+        const int r0 = r_begin + st * 32;
+        const int rows = r0 < r_end ? min(32, r_end - r0) : 0;
+        const int64_t rb0 = rows > 0 ? r0 : 0;
+        const __amdgpu_buffer_rsrc_t rs =
+            rsrc_bws(src + rb0 * width * 4, (uint32_t)rows * (uint32_t)width * 8u);
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) bsum[k][0] = bsum[k][1] = 0.f;
-    auto store_step = [&](const half8 (&raw)[UPT][4], _Float16* buf) {
+        for (int bk = 0; bk < NBK; ++bk)
+          raw[bk] = __builtin_bit_cast(
+              half8, __builtin_amdgcn_raw_buffer_load_b128(rs, goff + (uint32_t)bk * blk_off, 0, 0));
+      };
+      float bsum[2] = {0.f, 0.f};
+      auto store_step = [&](const half8 (&raw)[NBK], _Float16* buf) {
 #pragma unroll
-      for (int k = 0; k < UPT; ++k) {
-        const bool is_dy = unit_is_dy(k);
-        // per row e and column (a: halves 0-3, b: 4-7): pair sums and (Xr, Xi)
-        // scaled planes (eql_device.h): the pair sums carry 1/4, so that
-        // their sum and difference are X0/4 and X2/4, and the differences
-        // 1/2; one packed fused multiply-add each, no overflow for finite
-        // inputs
-        const f16x2 qq = {(_Float16)SCALE02, (_Float16)SCALE02};
-        const f16x2 hh = {(_Float16)SCALE1, (_Float16)SCALE1};
-        f16x2 sa[4], sb[4], ra[4], rb[4];
+        for (int q = 0; q < NBK / 2; ++q) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const half8 w = raw[k][e];
-          const f16x2 a01 = {w[0], w[1]}, a23 = {w[2], w[3]};
-          const f16x2 b01 = {w[4], w[5]}, b23 = {w[6], w[7]};
-          sa[e] = __builtin_elementwise_fma(a01, qq, a23 * qq);  // (x0 + x2, x1 + x3)/4
-          sb[e] = __builtin_elementwise_fma(b01, qq, b23 * qq);
-          const f16x2 a0n1 = {w[0], -w[1]}, na2a3 = {-w[2], w[3]};
-          const f16x2 b0n1 = {w[4], -w[5]}, nb2b3 = {-w[6], w[7]};
-          ra[e] = __builtin_elementwise_fma(a0n1, hh, na2a3 * hh);  // (x0 - x2, x3 - x1)/2
-          rb[e] = __builtin_elementwise_fma(b0n1, hh, nb2b3 * hh);
-          if (is_dy) {  // dbias: exact fp32 sum of the group values
-            bsum[k][0] = __builtin_amdgcn_fdot2(a01, ones, __builtin_amdgcn_fdot2(a23, ones, bsum[k][0], false), false);
-            bsum[k][1] = __builtin_amdgcn_fdot2(b01, ones, __builtin_amdgcn_fdot2(b23, ones, bsum[k][1], false), false);
+          for (int e = 0; e < 2; ++e) {
+            const f32x4 t0 = mma16(bf[e], raw[2 * q], f32x4{});
+            const f32x4 t1 = mma16(bf[e], raw[2 * q + 1], f32x4{});
+            if constexpr (IS_DY)  // plane 0 (lanes g = 0): G0/4 of the eight rows, fp32
+              bsum[e] += ((t0[0] + t0[1]) + (t0[2] + t0[3])) + ((t1[0] + t1[1]) + (t1[2] + t1[3]));
+            half8 v;
+            v[0] = (_Float16)t0[0]; v[1] = (_Float16)t0[1]; v[2] = (_Float16)t0[2]; v[3] = (_Float16)t0[3];
+            v[4] = (_Float16)t1[0]; v[5] = (_Float16)t1[1]; v[6] = (_Float16)t1[2]; v[7] = (_Float16)t1[3];
+            *reinterpret_cast<half8*>(buf + lslot[e] + q * 128) = v;
           }
         }
-        f16x4 p0[2], p2[2], pr[2], pi[2];               // [column][row]
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {                   // row pairs (0,1), (2,3)
-          const f16x2 pa = {sa[2 * h][0], sa[2 * h + 1][0]}, qa = {sa[2 * h][1], sa[2 * h + 1][1]};
-          const f16x2 pb = {sb[2 * h][0], sb[2 * h + 1][0]}, qb = {sb[2 * h][1], sb[2 * h + 1][1]};
-          const f16x2 x0a = pa + qa, x2a = pa - qa, x0b = pb + qb, x2b = pb - qb;
-          p0[0][2 * h] = x0a[0]; p0[0][2 * h + 1] = x0a[1];
-          p2[0][2 * h] = x2a[0]; p2[0][2 * h + 1] = x2a[1];
-          p0[1][2 * h] = x0b[0]; p0[1][2 * h + 1] = x0b[1];
-          p2[1][2 * h] = x2b[0]; p2[1][2 * h + 1] = x2b[1];
-          pr[0][2 * h] = ra[2 * h][0]; pr[0][2 * h + 1] = ra[2 * h + 1][0];
-          pi[0][2 * h] = ra[2 * h][1]; pi[0][2 * h + 1] = ra[2 * h + 1][1];
-          pr[1][2 * h] = rb[2 * h][0]; pr[1][2 * h + 1] = rb[2 * h + 1][0];
-          pi[1][2 * h] = rb[2 * h][1]; pi[1][2 * h + 1] = rb[2 * h + 1][1];
+      };
+      // Ring of four steps in registers.  Between barriers i and i+1 the
+      // producers first request step i+4 into the slot that step i left
+      // (so the vector-memory queue works while they transform), then
+      // transform step i+1 into buffer (i+1) % 2; the loads have three
+      // intervals to arrive.  Steps past the split load as zeros.
+      half8 ra[NBK], rb[NBK], rc[NBK], rd[NBK];
+      load_step(ra, 0);
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+      load_step(rb, 1);
+      load_step(rc, 2);
+      load_step(rd, 3);
+      store_step(ra, lds);
+      __syncthreads();  // barrier 0: step 0 is in buffer 0
+      __builtin_amdgcn_sched_barrier(0);
+      int i = 0;
+      for (; i + 4 <= nsteps - 1; i += 4) {
+        load_step(ra, i + 4);
+        store_step(rb, lds + BUF);
+        __syncthreads();  // barrier i+1
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(rb, i + 5);
+        store_step(rc, lds);
+        __syncthreads();  // barrier i+2
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(rc, i + 6);
+        store_step(rd, lds + BUF);
+        __syncthreads();  // barrier i+3
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(rd, i + 7);
+        store_step(ra, lds);
+        __syncthreads();  // barrier i+4
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // at most three steps left, already in rb, rc, rd; step i+1 goes to buffer 1
+      const int rest = nsteps - 1 - i;
+      if (rest > 0) {
+        store_step(rb, lds + BUF);
+        __syncthreads();
+        if (rest > 1) {
+          store_step(rc, lds);
+          __syncthreads();
+          if (rest > 2) {
+            store_step(rd, lds + BUF);
+            __syncthreads();
+          }
         }
-        const bool real = EXACT || loff[k] >= 0;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          // the pair's second column is the next operand column: 8 halves on
-          _Float16* dst = buf + loff[k] + cc * 8;
-          _Float16* const dmy = lds + 2 * BUF + ptid * 4;  // units past the step (not EXACT only)
-          *reinterpret_cast<f16x4*>(real ? dst + 0 * PSTR : dmy) = p0[cc];
-          *reinterpret_cast<f16x4*>(real ? dst + 1 * PSTR : dmy) = p2[cc];
-          *reinterpret_cast<f16x4*>(real ? dst + 2 * PSTR : dmy) = pr[cc];
-          *reinterpret_cast<f16x4*>(real ? dst + 3 * PSTR : dmy) = pi[cc];
+      }
+      if constexpr (IS_DY) {
+        // bias partial of this split: lane (j, 0) holds channels 2j, 2j + 1
+        // for the wave's rows
+        if (ct == 0 && g == 0) {
+          const int cc = 32 * o + 2 * j;
+          bred[hp][cc] = bsum[0];
+          bred[hp][cc + 1] = bsum[1];
         }
       }
     };
-    // Ring: step i sits in slot i % 3 from its load until its transform;
-    // between barriers i and i+1 the producers transform step i+1 and load
-    // step i+4 into the slot it frees (steps past the split load as zeros).
-    half8 ra[UPT][4], rb[UPT][4], rc[UPT][4];
-    load_step(ra, 0);
-    // every work-group's first step is requested before any later one
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
-    load_step(rb, 1);
-    load_step(rc, 2);
-    store_step(ra, lds);
-    load_step(ra, 3);
-    __syncthreads();  // barrier 0: step 0 is in buffer 0
-    __builtin_amdgcn_sched_barrier(0);
-    int cur = 1;
-    int i = 0;
-    for (; i + 3 <= nsteps - 1; i += 3) {
-      store_step(rb, lds + cur * BUF);
-      __builtin_amdgcn_sched_barrier(0);
-      load_step(rb, i + 4);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      cur ^= 1;
-      store_step(rc, lds + cur * BUF);
-      __builtin_amdgcn_sched_barrier(0);
-      load_step(rc, i + 5);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      cur ^= 1;
-      store_step(ra, lds + cur * BUF);
-      __builtin_amdgcn_sched_barrier(0);
-      load_step(ra, i + 6);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      cur ^= 1;
-    }
-    const int rest = nsteps - 1 - i;
-    if (rest > 0) {
-      store_step(rb, lds + cur * BUF);
-      __syncthreads();
-      cur ^= 1;
-      if (rest > 1) {
-        store_step(rc, lds + cur * BUF);
-        __syncthreads();
-      }
-    }
-    // bias partial of this split: per (column, row quartet) sums
-    if (ct == 0) {
-#pragma unroll
-      for (int k = 0; k < UPT; ++k) {
-        const int u = k * PT + ptid;
-        if (unit_is_dy(k)) {
-          const int cp = u % (BD / 2), quart = u / (BD / 2);
-          bred[quart][2 * cp] = bsum[k][0];
-          bred[quart][2 * cp + 1] = bsum[k][1];
-        }
-      }
-    }
+    if (pw / HALVES < DCH) produce(std::true_type{});
+    else produce(std::false_type{});
   } else {
     // =========================== consumer waves ===========================
     const int wd = wave / NWC, wc = wave % NWC;
-    // acc[..][3] collects Gi^T Xr and accn the Gr^T Xi it loses (Pi is their
-    // difference, taken once at the end): no fragment is ever negated
     f32x4 acc[DB][CB][4], accn[DB][CB];
 #pragma unroll
     for (int a = 0; a < DB; ++a)
@@ -266,200 +236,179 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
         for (int p = 0; p < 4; ++p) acc[a][b][p] = f32x4{};
         accn[a][b] = f32x4{};
       }
-    auto compute_sub = [&](const _Float16* buf) {
-      half8 gf[DB][4];
+    half8 ga[DB][4], xb[CB][4];
+    auto read_step = [&](half8 (&ga)[DB][4], half8 (&xb)[CB][4], const _Float16* buf) {
 #pragma unroll
       for (int a = 0; a < DB; ++a)
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-          gf[a][p] = *reinterpret_cast<const half8*>(buf + p * PSTR + (wd * DB + a) * FRAG + lane * 8);
+          ga[a][p] = *reinterpret_cast<const half8*>(buf + p * PSTR + (wd * DB + a) * FRAG + lane * 8);
 #pragma unroll
-      for (int b = 0; b < CB; ++b) {
-        const _Float16* xb = buf + (DBLK + wc * CB + b) * FRAG + lane * 8;
-        const half8 x0 = *reinterpret_cast<const half8*>(xb + 0 * PSTR);
-        const half8 x2 = *reinterpret_cast<const half8*>(xb + 1 * PSTR);
-        const half8 xr = *reinterpret_cast<const half8*>(xb + 2 * PSTR);
-        const half8 xi = *reinterpret_cast<const half8*>(xb + 3 * PSTR);
+      for (int b = 0; b < CB; ++b)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          xb[b][p] = *reinterpret_cast<const half8*>(buf + p * PSTR + (DBLK + wc * CB + b) * FRAG + lane * 8);
+    };
+    auto mma_step = [&](const half8 (&ga)[DB][4], const half8 (&xb)[CB][4]) {
+#pragma unroll
+      for (int b = 0; b < CB; ++b)
 #pragma unroll
         for (int a = 0; a < DB; ++a) {
-          acc[a][b][0] = mma16(gf[a][0], x0, acc[a][b][0]);
-          acc[a][b][2] = mma16(gf[a][2], xr, acc[a][b][2]);
-          acc[a][b][1] = mma16(gf[a][1], x2, acc[a][b][1]);
-          acc[a][b][3] = mma16(gf[a][3], xr, acc[a][b][3]);
-          acc[a][b][2] = mma16(gf[a][3], xi, acc[a][b][2]);
-          accn[a][b] = mma16(gf[a][2], xi, accn[a][b]);
+          acc[a][b][0] = mma16(ga[a][0], xb[b][0], acc[a][b][0]);
+          acc[a][b][2] = mma16(ga[a][2], xb[b][2], acc[a][b][2]);
+          acc[a][b][1] = mma16(ga[a][1], xb[b][1], acc[a][b][1]);
+          acc[a][b][3] = mma16(ga[a][3], xb[b][2], acc[a][b][3]);
+          acc[a][b][2] = mma16(ga[a][3], xb[b][3], acc[a][b][2]);
+          accn[a][b] = mma16(ga[a][2], xb[b][3], accn[a][b]);
         }
-      }
     };
-    auto compute_step = [&](const _Float16* buf) {
-#pragma unroll
-      for (int sb = 0; sb < KSUB; ++sb) compute_sub(buf + sb * SUB);
-    };
-    __syncthreads();  // barrier 0
-    int cur = 0;
     for (int st = 0; st < nsteps; ++st) {
-      compute_step(lds + cur * BUF);
-      cur ^= 1;
-      if (st + 1 < nsteps) __syncthreads();  // barrier st+1
+      __syncthreads();  // barrier st: step st is in buffer st % 2
+      read_step(ga, xb, lds + (st & 1) * BUF);
+      mma_step(ga, xb);
     }
-    // partial planes: part[split][p][c][d] (d contiguous); lane (i16, g)
-    // holds rows d 4g..4g+3 of column c i16 of each 16 x 16 block
+    // partial planes part[split][p][d][c] (c contiguous): lane (j, g) holds
+    // rows d 4g..4g+3 of column c j of each 16 x 16 block; sixteen lanes store
+    // 64 contiguous bytes per row
     const int64_t plane = (int64_t)c_pad * d_pad;
     float* pout = part + (int64_t)split * 4 * plane;
-    const int i16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int a = 0; a < DB; ++a)
 #pragma unroll
       for (int b = 0; b < CB; ++b) {
         const int d = d0 + (wd * DB + a) * 16 + 4 * g;
-        const int c = c0 + (wc * CB + b) * 16 + i16;
+        const int c = c0 + (wc * CB + b) * 16 + j;
         acc[a][b][3] -= accn[a][b];
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-          *reinterpret_cast<f32x4*>(pout + p * plane + (int64_t)c * d_pad + d) = acc[a][b][p];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pout[p * plane + (int64_t)(d + r) * c_pad + c] = acc[a][b][p][r];
       }
   }
 
-  // ---- bias partial: fixed-order sum over the row quartets of a step ------
+  // ---- bias partial: the producer parts summed in a fixed order ------------
   if (ct == 0) {
     __syncthreads();
-    for (int j = tid; j < BD; j += (NC + NP) * 64) {
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < QUARTS; ++q) s += bred[q][j];
-      part_b[(int64_t)split * d_pad + d0 + j] = s;
+    for (int jj = tid; jj < BD; jj += (NC + NP) * 64) {
+      float sb = bred[0][jj];
+      if constexpr (HALVES == 2) sb += bred[1][jj];
+      part_b[(int64_t)split * d_pad + d0 + jj] = 4.0f * sb;
     }
   }
 }
 
-// Sum of the S partials, inverse butterfly, dW and dbias.  Work-group =
-// 8 waves over one input channel c and 256 consecutive d (64 lanes x 4 d,
-// one 16-byte load per plane and split); wave w sums the splits s = w,
-// w + 8, ... in increasing order, then wave 0 adds the eight wave sums in
-// wave order: a fixed summation tree, so the result is deterministic.
+// Sum of the S partials [S][4][d_pad][c_pad] (c contiguous) and [S][d_pad],
+// inverse butterfly, dW and dbias.  Work-group = 8 waves over 256
+// consecutive (d, c) elements of a plane (64 lanes x 4 c); wave w sums the
+// splits s = w, w + 8, ... in increasing order and wave 0 adds the eight wave
+// sums in wave order: a fixed summation tree, so the result is
+// deterministic.  Loads and the stores of dW [D][C][4] are contiguous across
+// lanes.  The last ceil(d_pad / 256) work-groups sum the bias partials.
 constexpr int FIN_WAVES = 8;
 __global__ __launch_bounds__(64 * FIN_WAVES) void k_bwd_weight_finish(
     const float* __restrict__ part, const float* __restrict__ part_b, float* __restrict__ dW,
-    float* __restrict__ dbias, int C, int D, int d_pad, int c_pad, int S) {
-  __shared__ f32x4 red[FIN_WAVES][5][64];
+    float* __restrict__ dbias, int C, int D, int d_pad, int c_pad, int S, int n_main) {
+  __shared__ f32x4 red[FIN_WAVES][4][64];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_dchunk = (D + 255) / 256;
-  const int c = blockIdx.x / n_dchunk, d = (blockIdx.x % n_dchunk) * 256 + 4 * lane;
-  const bool bias_block = c == 0 && dbias != nullptr;
   const int64_t plane = (int64_t)c_pad * d_pad;
-  f32x4 P[5] = {};
-  if (d < D) {  // d_pad is a multiple of 16: d .. d + 3 lie inside the padded planes
-    const int64_t o = (int64_t)c * d_pad + d;
-    // chunks of four splits per wave: all their loads are in flight before
-    // the first add, and the adds keep the split order s = w, w + 8, ...
+  if ((int)blockIdx.x >= n_main) {  // bias: 256 consecutive d per work-group
+    if (dbias == nullptr) return;    // whole work-group
+    const int d = ((int)blockIdx.x - n_main) * 256 + 4 * lane;
+    f32x4 b = {};
+    if (d < d_pad)  // d_pad is a multiple of 32
+      for (int s = w; s < S; s += FIN_WAVES) b += *reinterpret_cast<const f32x4*>(part_b + (int64_t)s * d_pad + d);
+    red[w][0][lane] = b;
+    __syncthreads();
+    if (w == 0) {
+      f32x4 q = red[0][0][lane];
+#pragma unroll
+      for (int ww = 1; ww < FIN_WAVES; ++ww) q += red[ww][0][lane];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (d + k < D) dbias[d + k] = q[k];
+    }
+    return;
+  }
+  const int64_t e0 = (int64_t)blockIdx.x * 256 + 4 * lane;  // c_pad is a multiple of 32
+  f32x4 P[4] = {};
+  if (e0 < plane) {
     constexpr int IT = 4;
     for (int s0 = w; s0 < S; s0 += FIN_WAVES * IT) {
-      f32x4 v[IT][5];
+      f32x4 v[IT][4];
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int sp = s0 + FIN_WAVES * it;
         if (sp < S) {
-          const float* ps = part + (int64_t)sp * 4 * plane + o;
+          const float* ps = part + (int64_t)sp * 4 * plane + e0;
 #pragma unroll
           for (int p = 0; p < 4; ++p) v[it][p] = *reinterpret_cast<const f32x4*>(ps + p * plane);
-          v[it][4] = bias_block ? *reinterpret_cast<const f32x4*>(part_b + (int64_t)sp * d_pad + d)
-                                : f32x4{};
         }
       }
 #pragma unroll
-      for (int it = 0; it < IT; ++it) {
+      for (int it = 0; it < IT; ++it)
         if (s0 + FIN_WAVES * it < S) {
 #pragma unroll
-          for (int p = 0; p < 5; ++p) P[p] += v[it][p];
+          for (int p = 0; p < 4; ++p) P[p] += v[it][p];
         }
-      }
     }
   }
 #pragma unroll
-  for (int p = 0; p < 5; ++p) red[w][p][lane] = P[p];
+  for (int p = 0; p < 4; ++p) red[w][p][lane] = P[p];
   __syncthreads();
-  if (w == 0 && d < D) {
-    f32x4 q[5];
+  if (w == 0 && e0 < plane) {
+    f32x4 q[4];
 #pragma unroll
-    for (int p = 0; p < 5; ++p) {
+    for (int p = 0; p < 4; ++p) {
       q[p] = red[0][p][lane];
 #pragma unroll
       for (int ww = 1; ww < FIN_WAVES; ++ww) q[p] += red[ww][p][lane];
     }
+    const int d = (int)(e0 / c_pad), c = (int)(e0 % c_pad);
+    if (d < D) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (d + j < D) {
-        *reinterpret_cast<floatx4*>(dW + ((int64_t)(d + j) * C + c) * 4) =
-            idft4(q[0][j], q[1][j], q[2][j], q[3][j]);
-        if (bias_block) dbias[d + j] = q[4][j];
-      }
+      for (int k = 0; k < 4; ++k)
+        if (c + k < C)
+          *reinterpret_cast<floatx4*>(dW + ((int64_t)d * C + c + k) * 4) = idft4(q[0][k], q[1][k], q[2][k], q[3][k]);
     }
   }
 }
 
-hipError_t launch_bwd_weight_finish(const float* part, const float* part_b, float* dW, float* dbias,
-                                    int64_t C, int64_t D, int64_t d_pad, int64_t c_pad, int64_t S,
-                                    hipStream_t s) {
-  const unsigned fblocks = (unsigned)(C * ((D + 255) / 256));
-  hipLaunchKernelGGL(k_bwd_weight_finish, dim3(fblocks), dim3(64 * FIN_WAVES), 0, s, part, part_b,
-                     dW, dbias, (int)C, (int)D, (int)d_pad, (int)c_pad, (int)S);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
-struct BwsCfg {
-  int nwd, nwc, db, cb, np, ksub;
-  int bd() const { return nwd * db * 16; }
-  int bc() const { return nwc * cb * 16; }
-};
-
-static const BwsCfg kBwsCfgs[] = {
-    {2, 2, 1, 3, 8, 1},   // 0: 32 x 96 tiles, 4 consumers + 8 producers, 32-row steps
-    {1, 2, 1, 3, 7, 1},   // 1: 16 x 96 tiles, 2 consumers + 7 producers
-    {2, 2, 1, 3, 4, 1},   // 2: 32 x 96 tiles, 4 consumers + 4 producers
-    {2, 2, 2, 3, 8, 1},   // 3: 64 x 96 tiles, 4 consumers of 32 x 48 + 8 producers
-    {2, 2, 1, 3, 8, 2},   // 4: as 0 with 64-row steps
-    {1, 2, 1, 3, 7, 2},   // 5: as 1 with 64-row steps
-};
+// Tiles of 32 (d) x 96 (c) outputs: 4 consumer waves of 16 x 48, 8 producer
+// waves (dy: one 32-column unit, x: three, each split over two waves by rows).
+// Measured on MI355X at N = 12608, C = 96, D = 384 (binary16, warm): 22.1 us
+// for this kernel and the finish against 26.9 us for the vector-unit
+// butterfly with 16-byte loads whose lanes walk rows (four times the address
+// cycles of lanes along a row) it replaces.
+constexpr int BWS_NWD = 2, BWS_NWC = 2, BWS_DB = 1, BWS_CB = 3, BWS_NP = 8;
+constexpr int BWS_BD = BWS_NWD * BWS_DB * 16, BWS_BC = BWS_NWC * BWS_CB * 16;
 
 bool bws_supported(const eqlinear_plan* p) {
   if (p->tune.bws_off == 1 || p->dtype != EQL_F16) return false;
-  // whole column pairs (16-byte units), column tiles of 96.  Wider layers
-  // re-read dy once per column tile and still beat the symmetric
-  // matrix-core kernel (measured on MI355X, binary16: 168 -> 45 us at
-  // N = 12608, C = 192, D = 384; 5252 -> 911 us at N = 200704, C = 192,
-  // D = 768; 1527 -> 496 us for the 448-channel patch layer of the 3 x 3
-  // group convolution at 64 x 56 x 56, C = D = 48)
+  // whole column pairs (16-byte units).  Wider layers re-read dy once per
+  // column tile and still beat the tiled kernel of k_bwd_weight.hip.
   return p->C % 2 == 0 && p->D % 2 == 0;
 }
 
-static int bws_sel(const eqlinear_plan* p) {
-  const int sel = p->tune.bws_cfg;
-  return (sel < 0 || sel >= (int)(sizeof(kBwsCfgs) / sizeof(kBwsCfgs[0]))) ? 0 : sel;
-}
-
 struct BwsDims {
-  BwsCfg cfg;
   int64_t S, R, d_pad, c_pad;
   int n_dt, n_ct, per_xcd;
 };
 
 static BwsDims bws_dims(const eqlinear_plan* p, int64_t N) {
   BwsDims m;
-  m.cfg = kBwsCfgs[bws_sel(p)];
-  m.n_dt = (int)((p->D + m.cfg.bd() - 1) / m.cfg.bd());
-  m.n_ct = (int)((p->C + m.cfg.bc() - 1) / m.cfg.bc());
-  m.d_pad = (int64_t)m.n_dt * m.cfg.bd();
-  m.c_pad = (int64_t)m.n_ct * m.cfg.bc();
+  m.n_dt = (int)((p->D + BWS_BD - 1) / BWS_BD);
+  m.n_ct = (int)((p->C + BWS_BC - 1) / BWS_BC);
+  m.d_pad = (int64_t)m.n_dt * BWS_BD;
+  m.c_pad = (int64_t)m.n_ct * BWS_BC;
   const int T = m.n_dt * m.n_ct;
   // about one work-group per CU (one fits per CU), splits of whole 32-row steps
   int64_t S = p->tune.bws_s > 0 ? p->tune.bws_s : (256 / T > 0 ? 256 / T : 1);
-  const int64_t srows = 32 * m.cfg.ksub;
-  const int64_t steps = (N + srows - 1) / srows;
+  const int64_t steps = (N + 31) / 32;
   if (S > steps) S = steps;
   if (S < 1) S = 1;
   const int64_t steps_per = (steps + S - 1) / S;
-  m.R = steps_per * srows;
+  m.R = steps_per * 32;
   m.S = (N + m.R - 1) / m.R;
   if (m.S < 1) m.S = 1;
   m.per_xcd = (int)((m.S * T + 7) / 8);
@@ -472,32 +421,23 @@ size_t bws_workspace(const eqlinear_plan* p, int64_t N) {
   return (size_t)m.S * (size_t)(4 * m.c_pad * m.d_pad + m.d_pad) * sizeof(float);
 }
 
-template <int NWD, int NWC, int DB, int CB, int NP, int KSUB>
-static hipError_t launch_bws_t(const BwsDims& m, const eqlinear_plan* p, const void* x, const void* dy,
-                               float* part, float* part_b, int64_t N, hipStream_t s) {
-  const unsigned blocks = (unsigned)(8 * m.per_xcd);
-  hipLaunchKernelGGL((k_bwd_weight_ws<NWD, NWC, DB, CB, NP, KSUB>), dim3(blocks), dim3((NWD * NWC + NP) * 64), 0,
-                     s, (const _Float16*)x, (const _Float16*)dy, part, part_b, (int)N, (int)p->C, (int)p->D,
-                     (int)m.d_pad, (int)m.c_pad, (int)m.R, m.n_dt, m.n_ct, (int)m.S, m.per_xcd);
-  return hipGetLastError();
-}
-
 hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, float* dW, float* dbias,
                       int64_t N, void* ws, hipStream_t s) {
   const BwsDims m = bws_dims(p, N);
   float* part = (float*)ws;
   float* part_b = part + m.S * 4 * m.c_pad * m.d_pad;
-  hipError_t e = hipErrorNotSupported;
-  switch (bws_sel(p)) {
-    case 1: e = launch_bws_t<1, 2, 1, 3, 7, 1>(m, p, x, dy, part, part_b, N, s); break;
-    case 2: e = launch_bws_t<2, 2, 1, 3, 4, 1>(m, p, x, dy, part, part_b, N, s); break;
-    case 3: e = launch_bws_t<2, 2, 2, 3, 8, 1>(m, p, x, dy, part, part_b, N, s); break;
-    case 4: e = launch_bws_t<2, 2, 1, 3, 8, 2>(m, p, x, dy, part, part_b, N, s); break;
-    case 5: e = launch_bws_t<1, 2, 1, 3, 7, 2>(m, p, x, dy, part, part_b, N, s); break;
-    default: e = launch_bws_t<2, 2, 1, 3, 8, 1>(m, p, x, dy, part, part_b, N, s); break;
-  }
+  const unsigned blocks = (unsigned)(8 * m.per_xcd);
+  hipLaunchKernelGGL((k_bwd_weight_ws<BWS_NWD, BWS_NWC, BWS_DB, BWS_CB, BWS_NP>), dim3(blocks),
+                     dim3((BWS_NWD * BWS_NWC + BWS_NP) * 64), 0, s, (const _Float16*)x, (const _Float16*)dy,
+                     part, part_b, (int)N, (int)p->C, (int)p->D, (int)m.d_pad, (int)m.c_pad, (int)m.R, m.n_dt,
+                     m.n_ct, (int)m.S, m.per_xcd);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_bwd_weight_finish(part, part_b, dW, dbias, p->C, p->D, m.d_pad, m.c_pad, m.S, s);
+  const int n_main = (int)((m.d_pad * m.c_pad + 255) / 256);
+  const int n_bias = (int)((m.d_pad + 255) / 256);
+  hipLaunchKernelGGL(k_bwd_weight_finish, dim3((unsigned)(n_main + n_bias)), dim3(64 * FIN_WAVES), 0, s, part,
+                     part_b, dW, dbias, (int)p->C, (int)p->D, (int)m.d_pad, (int)m.c_pad, (int)m.S, n_main);
+  return hipGetLastError();
 }
 
 }  // namespace eql

@@ -250,13 +250,7 @@ def test_backward_input_paths(C, D, N, path, monkeypatch):
 
 # backward-weight paths forced one at a time (binary16)
 BW_PATHS = {
-    "ws_32x96": {"EQL_BWS_CFG": "0"},
-    "ws_16x96": {"EQL_BWS_CFG": "1"},
-    "ws_32x96_np4": {"EQL_BWS_CFG": "2"},
-
-    "ws_64x96_np8": {"EQL_BWS_CFG": "3"},
-    "ws_32x96_64rows": {"EQL_BWS_CFG": "4"},
-    "ws_16x96_64rows": {"EQL_BWS_CFG": "5"},
+    "ws": {},
     "ws_few_splits": {"EQL_BWS_S": "3"},
     "tiled": {"EQL_BW_TILED": "1"},
 }
@@ -264,7 +258,7 @@ BW_PATHS = {
 
 @pytest.mark.parametrize("path", sorted(BW_PATHS))
 @pytest.mark.parametrize("C,D,N", [(2, 2, 1), (32, 34, 95), (96, 384, 3001), (96, 100, 12608),
-                                   (64, 256, 777)])
+                                   (64, 256, 777), (192, 66, 530)])
 def test_backward_weight_paths(C, D, N, path, monkeypatch):
     for k, v in BW_PATHS[path].items():
         monkeypatch.setenv(k, v)
