@@ -98,6 +98,10 @@ struct eqlinear_plan {
   eql::SpectraLayout adj;
   void* spec_fwd;     // device, plan dtype
   void* spec_adj;     // device, plan dtype
+  // Binary16 p4 plans: the same two operands in matrix-core fragment order
+  // (k_spectra.hip), read by the producer/consumer kernels; nullptr otherwise.
+  void* frag_fwd;
+  void* frag_adj;
   float* bias_f32;    // device, [fwd.n_pad], zeros where no bias
   float* zeros_f32;   // device, [adj.n_pad] zeros (bias of backward_input)
   // p4m (D_4) in binary16 at widths the p4 producer/consumer kernels take:
@@ -124,6 +128,7 @@ hipError_t launch_bws(const eqlinear_plan* p, const void* x, const void* dy, flo
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s);
 // Producer/consumer spectral kernel (binary16): the forward, or with the
 // conjugate-transposed spectra (adjoint = true) the backward-input pass.
+// `spec` is an operand in fragment order (frag_fwd or frag_adj).
 // act: pointwise activation of the forward epilogue (0 none, 1 GELU, 2 GELU
 // with the tanh approximation); 0 for backward_input.
 hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,

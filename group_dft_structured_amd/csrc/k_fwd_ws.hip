@@ -345,7 +345,8 @@ __device__ __forceinline__ void ws_body(
     const int i16 = lane & 15, g = lane >> 4;
     const int d0 = j * BN + wave * NB * 16;  // this wave's first output channel
     // weight fragments (A operand): channel d0 + 16nb + i16, reduction
-    // channels 32s + 8g .. 32s + 8g + 7
+    // channels 32s + 8g .. 32s + 8g + 7, from the operand in fragment order
+    // (1 KB per fragment, lane l at 16 l bytes: one contiguous wave load)
     half8 w0[NB][KS], w2[NB][KS], wr[NB][KS], wi[NB][KS];
     float bc[NB][4];
     {
@@ -357,13 +358,13 @@ __device__ __forceinline__ void ws_body(
       const __amdgpu_buffer_rsrc_t rb = rsrc(bias, (uint32_t)n_pad * 4);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const uint32_t off = (uint32_t)((d0 + nb * 16 + i16) * KP + 8 * g) * 2;
+        const uint32_t off = (uint32_t)(((d0 / 16 + nb) * KS) * 1024 + lane * 16);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          w0[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r0, off + s * 64, 0, 0));
-          w2[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r2, off + s * 64, 0, 0));
-          wr[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rr, off + s * 64, 0, 0));
-          wi[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ri, off + s * 64, 0, 0));
+          w0[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r0, off + s * 1024, 0, 0));
+          w2[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r2, off + s * 1024, 0, 0));
+          wr[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rr, off + s * 1024, 0, 0));
+          wi[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ri, off + s * 1024, 0, 0));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)

@@ -245,7 +245,7 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
                           hipStream_t s) {
   if (p->cyclic) return cyc::launch_forward(p, x, y, N, act, s);
   // the producer/consumer kernels apply the activation in their epilogue
-  hipError_t e = launch_ws(p->tune, p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C,
+  hipError_t e = launch_ws(p->tune, p->dtype, x, p->frag_fwd, p->bias_f32, y, N, (int)p->C,
                            (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, false, act, s);
   if (e != hipErrorNotSupported) return e;
   e = launch_ws32(p->tune, p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
@@ -267,7 +267,7 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
 hipError_t launch_backward_input(const eqlinear_plan* p, const void* dy, void* dx, int64_t N,
                                  hipStream_t s) {
   if (p->cyclic) return cyc::launch_backward_input(p, dy, dx, N, s);
-  hipError_t e = launch_ws(p->tune, p->dtype, dy, p->spec_adj, p->zeros_f32, dx, N, (int)p->D,
+  hipError_t e = launch_ws(p->tune, p->dtype, dy, p->frag_adj, p->zeros_f32, dx, N, (int)p->D,
                            (int)p->adj.k_pad, (int)p->C, (int)p->adj.n_pad, true, ACT_NONE, s);
   if (e != hipErrorNotSupported) return e;
   const int cfg = pick_cfg(p->tune, p->C);
