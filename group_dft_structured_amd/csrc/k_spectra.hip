@@ -1,6 +1,6 @@
 // Weight-spectrum precompute: the group DFT of every W[d,c,:] (length 4),
 // written once per weight update in the two operand layouts the matrix-core
-// kernels read.
+// kernels read (binary16 p4 plans: each also in fragment order).
 //
 // Flash EQ-Linear ("Approccio Algoritmico", "Specializzazione per il Gruppo di
 // Rotazione p4"): after the DFT along the group axis the convolution becomes a
@@ -17,10 +17,23 @@
 
 namespace eql {
 
+// Position of plane element (row, col) of an [n_pad][k_pad] plane in
+// matrix-core fragment order: for 16-row block b and 32-column step s the
+// 1 KB fragment (b * k_pad / 32 + s) holds lane l = (i, g) = (l % 16, l / 16)
+// at 16 l bytes: row 16 b + i, columns 32 s + 8 g .. + 7.  A wave then loads
+// a whole fragment as 1 KB of consecutive 16-byte lanes; in the row-major
+// planes its lanes walk 16 rows, which costs the address unit about four
+// times as many cycles.
+__device__ __forceinline__ int64_t frag_index(int row, int col, int k_pad) {
+  const int b = row >> 4, i = row & 15, s = col >> 5, g = (col >> 3) & 3, e = col & 7;
+  return ((int64_t)b * (k_pad >> 5) + s) * 512 + (g * 16 + i) * 8 + e;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_weight_spectra(
     const T* __restrict__ W, const T* __restrict__ bias, T* __restrict__ spec_fwd,
-    T* __restrict__ spec_adj, float* __restrict__ bias_f32, float* __restrict__ zeros_f32,
+    T* __restrict__ spec_adj, T* __restrict__ frag_fwd, T* __restrict__ frag_adj,
+    float* __restrict__ bias_f32, float* __restrict__ zeros_f32,
     int C, int D, int fwd_n, int fwd_k, int adj_n, int adj_k) {
   const int64_t fwd_elems = (int64_t)fwd_n * fwd_k;
   const int64_t adj_elems = (int64_t)adj_n * adj_k;
@@ -36,6 +49,13 @@ __global__ __launch_bounds__(256) void k_weight_spectra(
     spec_fwd[1 * fwd_elems + i] = Elem<T>::from_f(s.f2);
     spec_fwd[2 * fwd_elems + i] = Elem<T>::from_f(s.fr);
     spec_fwd[3 * fwd_elems + i] = Elem<T>::from_f(s.fi);
+    if (frag_fwd != nullptr) {
+      const int64_t f = frag_index(d, c, fwd_k);
+      frag_fwd[0 * fwd_elems + f] = Elem<T>::from_f(s.f0);
+      frag_fwd[1 * fwd_elems + f] = Elem<T>::from_f(s.f2);
+      frag_fwd[2 * fwd_elems + f] = Elem<T>::from_f(s.fr);
+      frag_fwd[3 * fwd_elems + f] = Elem<T>::from_f(s.fi);
+    }
     return;
   }
   const int64_t j = i - fwd_elems;
@@ -50,6 +70,13 @@ __global__ __launch_bounds__(256) void k_weight_spectra(
     spec_adj[1 * adj_elems + j] = Elem<T>::from_f(s.f2);
     spec_adj[2 * adj_elems + j] = Elem<T>::from_f(s.fr);
     spec_adj[3 * adj_elems + j] = Elem<T>::from_f(-s.fi);
+    if (frag_adj != nullptr) {
+      const int64_t f = frag_index(c, d, adj_k);
+      frag_adj[0 * adj_elems + f] = Elem<T>::from_f(s.f0);
+      frag_adj[1 * adj_elems + f] = Elem<T>::from_f(s.f2);
+      frag_adj[2 * adj_elems + f] = Elem<T>::from_f(s.fr);
+      frag_adj[3 * adj_elems + f] = Elem<T>::from_f(-s.fi);
+    }
     return;
   }
   const int64_t k = j - adj_elems;
@@ -62,29 +89,6 @@ __global__ __launch_bounds__(256) void k_weight_spectra(
   if (z < adj_n) zeros_f32[z] = 0.f;
 }
 
-// One operand (four planes [n_pad][k_pad]) rewritten in matrix-core fragment
-// order: for plane p, 16-row block b and 32-column step s, the 1 KB fragment
-// ((p * n_pad / 16 + b) * k_pad / 32 + s) holds lane l = (i, g) = (l % 16, l / 16)
-// at 16 l bytes: row 16 b + i, columns 32 s + 8 g .. + 7.  A wave then loads
-// a whole fragment as 1 KB of consecutive 16-byte lanes; in the row-major
-// planes its lanes walk 16 rows, which costs the address unit about four
-// times as many cycles.  One thread per 16-byte slot.
-__global__ __launch_bounds__(256) void k_spectra_frag(const _Float16* __restrict__ spec,
-                                                      _Float16* __restrict__ frag, int n_pad, int k_pad) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t plane = (int64_t)n_pad * k_pad;
-  if (t >= 4 * plane / 8) return;
-  const int l = (int)(t & 63);
-  const int64_t f = t >> 6;
-  const int ks = k_pad / 32, nblk = n_pad / 16;
-  const int s = (int)(f % ks);
-  const int b = (int)((f / ks) % nblk);
-  const int p = (int)(f / ((int64_t)ks * nblk));
-  const _Float16* src = spec + p * plane + (int64_t)(16 * b + (l & 15)) * k_pad + 32 * s + 8 * (l >> 4);
-  *reinterpret_cast<u32x4*>(frag + 8 * t) = *reinterpret_cast<const u32x4*>(src);
-}
-
 hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bias, hipStream_t s) {
   if (p->cyclic) return cyc::launch_spectra(p, W, bias, s);
   const int64_t total = (int64_t)p->fwd.plane_elems() + (int64_t)p->adj.plane_elems() +
@@ -94,21 +98,13 @@ hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bia
   if (p->dtype == EQL_F16) {
     hipLaunchKernelGGL(k_weight_spectra<_Float16>, dim3((unsigned)blocks), dim3(threads), 0, s,
                        (const _Float16*)W, (const _Float16*)bias, (_Float16*)p->spec_fwd,
-                       (_Float16*)p->spec_adj, p->bias_f32, p->zeros_f32, (int)p->C, (int)p->D,
-                       (int)p->fwd.n_pad, (int)p->fwd.k_pad, (int)p->adj.n_pad, (int)p->adj.k_pad);
-    if (p->frag_fwd != nullptr) {
-      const int64_t nf = 4 * (int64_t)p->fwd.plane_elems() / 8, na = 4 * (int64_t)p->adj.plane_elems() / 8;
-      hipLaunchKernelGGL(k_spectra_frag, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, s,
-                         (const _Float16*)p->spec_fwd, (_Float16*)p->frag_fwd, (int)p->fwd.n_pad,
-                         (int)p->fwd.k_pad);
-      hipLaunchKernelGGL(k_spectra_frag, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, s,
-                         (const _Float16*)p->spec_adj, (_Float16*)p->frag_adj, (int)p->adj.n_pad,
-                         (int)p->adj.k_pad);
-    }
+                       (_Float16*)p->spec_adj, (_Float16*)p->frag_fwd, (_Float16*)p->frag_adj, p->bias_f32,
+                       p->zeros_f32, (int)p->C, (int)p->D, (int)p->fwd.n_pad, (int)p->fwd.k_pad,
+                       (int)p->adj.n_pad, (int)p->adj.k_pad);
   } else {
     hipLaunchKernelGGL(k_weight_spectra<float>, dim3((unsigned)blocks), dim3(threads), 0, s,
                        (const float*)W, (const float*)bias, (float*)p->spec_fwd,
-                       (float*)p->spec_adj, p->bias_f32, p->zeros_f32, (int)p->C, (int)p->D,
+                       (float*)p->spec_adj, nullptr, nullptr, p->bias_f32, p->zeros_f32, (int)p->C, (int)p->D,
                        (int)p->fwd.n_pad, (int)p->fwd.k_pad, (int)p->adj.n_pad, (int)p->adj.k_pad);
   }
   return hipGetLastError();
