@@ -72,8 +72,13 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 // LDS fragment layout (per buffer): plane p (X0, X2, Xr, Xi) and k-step s
 // hold one 1 KB fragment at (p*KS + s)*512 halves; lane (i16, g) of the B
-// operand reads the 16 bytes at (g*16 + i16)*16, i.e. row i16, reduction
-// channels 32s + 8g .. 32s + 8g + 7.
+// operand reads the 16 bytes of slot g*16 + (i16 ^ 4g): row i16 and k-slice g.
+// The row index is swizzled by 4g so that a producer wave whose sixteen
+// lanes hold four rows x four slices writes sixteen distinct banks groups.
+// Reduction order inside a 32-channel step: slice g holds the channel pairs
+// g, g + 4, g + 8, g + 12 (two channels each, in that order), so that the
+// four lanes of a producer quad read 64 contiguous bytes of a row; the
+// weight fragments (k_spectra.hip) use the same order.
 template <int NC, int NP, int NB, int KS, int YP, bool G8, bool STAGGER, bool PST, bool PIPE,
           bool SPLIT, bool ACT = false>
 __device__ __forceinline__ void ws_body(
@@ -151,22 +156,17 @@ __device__ __forceinline__ void ws_body(
     // =========================== producer waves ===========================
     const int ptid = tid - NC * 64;
     const int64_t row_elems = (int64_t)K * 4;
-    // unit u -> (row, channel group).  A wave's 64 units cover 16 rows and
-    // 4 consecutive groups, so its loads touch 16 row segments of 64 bytes
-    // either way; the lane order is chosen for the LDS writes.  With 8-channel
-    // units, rows fastest: lane l writes the 16-byte fragment slot l, so a
-    // wave writes 1 KB contiguously.  With 2-channel units, groups fastest:
-    // lane l writes the l-th 4-byte word of a 256-byte run, where rows
-    // fastest would put rows r and r + 8 on the same LDS bank (measured on
-    // gfx950: 2-way conflicts, half of the write cycles).
+    // unit u -> (row, channels).  The four lanes of a quad share a row and
+    // read 64 contiguous bytes per load instruction (lanes walking rows
+    // would cost the address unit four times the cycles).  With 2-channel
+    // units, lane l of a wave takes row (l / 4) % 16 and channel pair
+    // 4 (u / 64) + l % 4.  With 8-channel units, lane l takes row (l / 4) % 16,
+    // 32-channel step u / 64 and slice g = l % 4: load e reads pair 4e + g of
+    // the step, and the four pairs fill the slot of slice g.
     auto unit_pos = [](int u, int& row, int& grp) {
-      if (G8) {
-        row = u % 16;
-        grp = u / 16;
-      } else {
-        row = (u >> 2) & 15;
-        grp = ((u >> 6) << 2) | (u & 3);
-      }
+      row = (u >> 2) & 15;
+      grp = G8 ? (u >> 6) * 4 + (u & 3)        // (step, slice) = (grp / 4, grp % 4)
+               : ((u >> 6) << 2) | (u & 3);    // channel pair
     };
     auto load_tile = [&](half8 (&raw)[LPT], int i) {
       const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
@@ -178,11 +178,13 @@ __device__ __forceinline__ void ws_body(
         int row, grp;
         unit_pos(u, row, grp);
         const bool real = UNITS % PT == 0 || u < UNITS;
-        const uint32_t off = (uint32_t)(row * row_elems + 4 * CPU * grp) * 2;
+        // G8: pair 4e + g of step grp / 4 is at byte 256 (grp / 4) + 64 e + 16 g
+        const uint32_t off = G8 ? (uint32_t)(row * row_elems * 2 + 256 * (grp >> 2) + 16 * (grp & 3))
+                                : (uint32_t)(row * row_elems + 4 * CPU * grp) * 2;
 #pragma unroll
         for (int e = 0; e < LPU; ++e)
           raw[k * LPU + e] = __builtin_bit_cast(
-              half8, __builtin_amdgcn_raw_buffer_load_b128(rx, real ? off + 16 * e : 0x7FFFFFF0u, 0, 0));
+              half8, __builtin_amdgcn_raw_buffer_load_b128(rx, real ? off + 64 * e : 0x7FFFFFF0u, 0, 0));
       }
     };
     // butterfly of one 16-byte word (channels c, c + 1, four group values
@@ -216,12 +218,22 @@ __device__ __forceinline__ void ws_body(
         const int u = k * PT + ptid;
         int row, grp;
         unit_pos(u, row, grp);
-        const int c = CPU * grp;  // first channel of the unit
-        const int s = c >> 5, gg = (c & 31) >> 3, jj = c & 7;
+        // fragment slot (step s, slice gg, row) and the word of the pair in it
+        int s, gg, jj;
+        if (G8) {
+          s = grp >> 2;
+          gg = grp & 3;
+          jj = 0;
+        } else {
+          const int qp = (grp & 15);  // channel pair within the 32-channel step
+          s = grp >> 4;
+          gg = qp & 3;
+          jj = (qp >> 2) * 2;
+        }
         const bool real = UNITS % PT == 0 || u < UNITS;
         // units past the tile send their words to this thread's dummy slot
         _Float16* const dummy = xs + 2 * BUF + ptid * (G8 ? 8 : 2);
-        _Float16* const dst = buf + s * FRAG + (gg * 16 + row) * 8 + jj;
+        _Float16* const dst = buf + s * FRAG + (gg * 16 + (row ^ (gg << 2))) * 8 + jj;
         if (G8) {
           u32x4 v0, v2, vr, vi;
 #pragma unroll
@@ -343,6 +355,7 @@ __device__ __forceinline__ void ws_body(
   } else {
     // =========================== consumer waves ===========================
     const int i16 = lane & 15, g = lane >> 4;
+    const int xslot = lane ^ (g << 2);      // LDS slot of row i16, slice g
     const int d0 = j * BN + wave * NB * 16;  // this wave's first output channel
     // weight fragments (A operand): channel d0 + 16nb + i16, reduction
     // channels 32s + 8g .. 32s + 8g + 7, from the operand in fragment order
@@ -391,7 +404,7 @@ __device__ __forceinline__ void ws_body(
       }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const _Float16* f = buf + s * FRAG + lane * 8;
+        const _Float16* f = buf + s * FRAG + xslot * 8;
         const half8 x0 = *reinterpret_cast<const half8*>(f + 0 * PS);
         const half8 x2 = *reinterpret_cast<const half8*>(f + 1 * PS);
         const half8 xr = *reinterpret_cast<const half8*>(f + 2 * PS);

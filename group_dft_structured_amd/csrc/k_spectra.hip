@@ -20,12 +20,16 @@ namespace eql {
 // Position of plane element (row, col) of an [n_pad][k_pad] plane in
 // matrix-core fragment order: for 16-row block b and 32-column step s the
 // 1 KB fragment (b * k_pad / 32 + s) holds lane l = (i, g) = (l % 16, l / 16)
-// at 16 l bytes: row 16 b + i, columns 32 s + 8 g .. + 7.  A wave then loads
-// a whole fragment as 1 KB of consecutive 16-byte lanes; in the row-major
+// at 16 l bytes: row 16 b + i and k-slice g of the step, which holds the
+// column pairs g, g + 4, g + 8, g + 12 (the reduction order the
+// producer/consumer kernels stage x in; k_fwd_ws.hip).  A wave then loads a
+// whole fragment as 1 KB of consecutive 16-byte lanes; in the row-major
 // planes its lanes walk 16 rows, which costs the address unit about four
 // times as many cycles.
 __device__ __forceinline__ int64_t frag_index(int row, int col, int k_pad) {
-  const int b = row >> 4, i = row & 15, s = col >> 5, g = (col >> 3) & 3, e = col & 7;
+  const int b = row >> 4, i = row & 15, s = col >> 5;
+  const int q = (col & 31) >> 1;           // column pair within the step
+  const int g = q & 3, e = ((q >> 2) << 1) | (col & 1);
   return ((int64_t)b * (k_pad >> 5) + s) * 512 + (g * 16 + i) * 8 + e;
 }
 
