@@ -529,19 +529,24 @@ __device__ __forceinline__ void ws_body(
       // Software pipeline: between barriers i+1 and i+2 the products of tile
       // i+1 (buffer (i+1) % 2) are issued before the epilogue of tile i, so
       // the matrix cores work while the same wave runs the epilogue's VALU
-      // instructions.  Two accumulator sets alternate (loop unrolled twice).
-      // The last iteration of an even tile count multiplies a buffer that
-      // holds no further tile into A; A is not used again.
+      // instructions.  Two accumulator sets alternate (loop unrolled twice);
+      // the last one or two tiles leave the loop, so no products are issued
+      // for a tile past the worker's last.
       Acc A, B;
       products(A, xs);
       int i = 0;
-      for (; i + 1 < n_my; i += 2) {
+      for (; i + 2 < n_my; i += 2) {
         __syncthreads();  // barrier i+1
         pipe_step(B, xs + BUF, i, A);
         __syncthreads();  // barrier i+2
         pipe_step(A, xs, i + 1, B);
       }
-      if (i < n_my) {
+      if (i + 1 < n_my) {  // two tiles left: i (products in A) and i + 1
+        __syncthreads();  // barrier i+1
+        pipe_step(B, xs + BUF, i, A);
+        __syncthreads();  // barrier i+2 = n_my
+        epilogue_any(i + 1, B);
+      } else {  // one tile left
         __syncthreads();  // barrier n_my
         epilogue_any(i, A);
       }
@@ -641,20 +646,22 @@ static hipError_t launch_ws_t(const Tuning& tn, const void* x, const void* spec,
   // memory-side cache and reductions of up to six steps (the second
   // accumulator set fits the register budget there).
   if constexpr (KS <= 6) {
-    const bool pipe = !adjoint && small && pick(tn.ws_pipe, 1) != 0;
+    // With a fused activation the second accumulator set and the
+    // activation's registers fit the budget of twelve waves only up to three
+    // reduction steps (beyond, the compiler spills); consumer-side stores
+    // (EQL_WS_OUT=1) run unpipelined.
+    const bool pipe = !adjoint && small && pick(tn.ws_pipe, 1) != 0 && pick(tn.ws_out, 0) != 1 &&
+                      (act == ACT_NONE || KS <= 3);
     if (pipe) {
 #define EQL_WS_PIPE_LAUNCH(YP_, G8_, PST_, ACT_)                                                       \
   hipLaunchKernelGGL((k_fwd_ws_f16<NC, NP, NB, KS, YP_, G8_, PST_, true, false, ACT_>), grid, block, 0, s, \
                      (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K, n_out,     \
                      n_pad, n_ct, qx, act, wfirst)
-      // consumer stores (EQL_WS_OUT=1) or the producers' whole-row stores
-      const bool cst = pick(tn.ws_out, 0) == 1;
       if (act != ACT_NONE) {
-        if (g8) EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, true, true, true);
-        else EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, false, true, true);
-      } else if (cst) {
-        if (g8) EQL_WS_PIPE_LAUNCH(POLICY_STREAM, true, false, false);
-        else EQL_WS_PIPE_LAUNCH(POLICY_STREAM, false, false, false);
+        if constexpr (KS <= 3) {
+          if (g8) EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, true, true, true);
+          else EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, false, true, true);
+        }
       } else {
         if (g8) EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, true, true, false);
         else EQL_WS_PIPE_LAUNCH(POLICY_THROUGH, false, true, false);
