@@ -156,17 +156,23 @@ __device__ __forceinline__ void ws_body(
     // =========================== producer waves ===========================
     const int ptid = tid - NC * 64;
     const int64_t row_elems = (int64_t)K * 4;
-    // unit u -> (row, channels).  The four lanes of a quad share a row and
-    // read 64 contiguous bytes per load instruction (lanes walking rows
-    // would cost the address unit four times the cycles).  With 2-channel
-    // units, lane l of a wave takes row (l / 4) % 16 and channel pair
-    // 4 (u / 64) + l % 4.  With 8-channel units, lane l takes row (l / 4) % 16,
-    // 32-channel step u / 64 and slice g = l % 4: load e reads pair 4e + g of
-    // the step, and the four pairs fill the slot of slice g.
+    // unit u -> (row, channels).  Lanes that share a row read contiguous
+    // bytes (lanes walking rows would cost the address unit four times the
+    // cycles).  With 2-channel units, sixteen lanes take the sixteen channel
+    // pairs of one 32-channel step of one row (256 contiguous bytes), so a
+    // wave covers four rows; its 4-byte LDS writes (four slices x four words
+    // of four swizzled rows) then meet 64 distinct banks.  With 8-channel
+    // units, lane l takes row (l / 4) % 16, step u / 64 and slice g = l % 4:
+    // load e reads pair 4e + g of the step (four lanes, 64 contiguous
+    // bytes), and the four pairs fill the slot of slice g.
     auto unit_pos = [](int u, int& row, int& grp) {
-      row = (u >> 2) & 15;
-      grp = G8 ? (u >> 6) * 4 + (u & 3)        // (step, slice) = (grp / 4, grp % 4)
-               : ((u >> 6) << 2) | (u & 3);    // channel pair
+      if (G8) {
+        row = (u >> 2) & 15;
+        grp = (u >> 6) * 4 + (u & 3);             // (step, slice) = (grp / 4, grp % 4)
+      } else {
+        row = (u >> 4) & 15;
+        grp = ((u >> 8) << 4) | (u & 15);         // channel pair
+      }
     };
     auto load_tile = [&](half8 (&raw)[LPT], int i) {
       const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
