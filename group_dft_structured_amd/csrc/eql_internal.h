@@ -98,8 +98,9 @@ struct eqlinear_plan {
   eql::SpectraLayout adj;
   void* spec_fwd;     // device, plan dtype
   void* spec_adj;     // device, plan dtype
-  // Binary16 p4 plans: the same two operands in matrix-core fragment order
-  // (k_spectra.hip), read by the producer/consumer kernels; nullptr otherwise.
+  // p4 plans: the operands of the producer/consumer kernels again in their
+  // matrix-core fragment order (k_spectra.hip): both in binary16, the forward
+  // one in binary32 (frag_adj nullptr); nullptr for the generic groups.
   void* frag_fwd;
   void* frag_adj;
   float* bias_f32;    // device, [fwd.n_pad], zeros where no bias
@@ -134,7 +135,8 @@ hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bia
 hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,
                      const float* bias, void* y, int64_t N, int K, int k_pad, int n_out, int n_pad,
                      bool adjoint, int act, hipStream_t s);
-// Producer/consumer forward kernel, binary32 (reduction width a multiple of 16, <= 192).
+// Producer/consumer forward kernel, binary32 (reduction width a multiple of 16, <= 192);
+// `spec` is the forward operand in its fragment order (frag_fwd).
 hipError_t launch_ws32(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,
                        const float* bias, void* y, int64_t N, int K, int k_pad, int n_out, int n_pad,
                        int act, hipStream_t s);

@@ -303,9 +303,11 @@ eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t p, const void* W, const vo
     const size_t adj_bytes = (size_t)p->T * p->adj.plane_elems() * p->esize;
     const size_t bias_bytes = (size_t)p->fwd.n_pad * sizeof(float);
     const size_t zero_bytes = (size_t)p->adj.n_pad * sizeof(float);
-    // binary16 p4 plans keep both operands a second time in fragment order
-    const bool frag = p->dtype == EQL_F16 && !p->cyclic;
-    const size_t frag_bytes = frag ? fwd_bytes + adj_bytes : 0;
+    // p4 plans keep the operands of the producer/consumer kernels a second
+    // time in fragment order: both in binary16, the forward one in binary32
+    const bool frag = !p->cyclic;
+    const bool frag_adj = frag && p->dtype == EQL_F16;
+    const size_t frag_bytes = frag ? fwd_bytes + (frag_adj ? adj_bytes : 0) : 0;
     void* mem = nullptr;
     hipError_t e = hipMalloc(&mem, fwd_bytes + adj_bytes + bias_bytes + zero_bytes + frag_bytes);
     if (e != hipSuccess) {
@@ -321,7 +323,7 @@ eqlinear_status_t eqlinear_set_weight(eqlinear_plan_t p, const void* W, const vo
     p->zeros_f32 = (float*)(base + fwd_bytes + adj_bytes + bias_bytes);
     if (frag) {
       p->frag_fwd = base + fwd_bytes + adj_bytes + bias_bytes + zero_bytes;
-      p->frag_adj = (char*)p->frag_fwd + fwd_bytes;
+      p->frag_adj = frag_adj ? (char*)p->frag_fwd + fwd_bytes : nullptr;
     }
     p->device = dev;
   }

@@ -18,10 +18,12 @@
 //    (four output channels of one row), or leave the tile in LDS for the
 //    producers to store (PST, below).
 // The reduction index is permuted identically for both operands so that a
-// lane's four consecutive k-steps read 16 contiguous bytes: within a block
-// of 16 channels, lane group g at k-step e handles channel 4g + e.  Its
-// weights are then one 16-byte load per plane and block, and its x values
-// one 16-byte LDS read per plane and block.
+// lane's four k-steps read 16 contiguous bytes: within a block of 16
+// channels, lane group g at k-step e handles channel 4e + g.  Its weights
+// are then one 16-byte load per plane and block from the fragment-order
+// copy (1 KB contiguous per wave), its x values one 16-byte LDS read per
+// plane and block, and four producer lanes that share a row load 64
+// contiguous bytes (channels 4e .. 4e + 3 at load e).
 #include "eql_device.h"
 #include "eql_internal.h"
 
@@ -49,8 +51,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc32(const void* base, uint3
 }  // namespace
 
 // LDS per buffer: plane p, channel block j (16 channels): 1 KB at
-// (p*KB + j)*256 floats; lane (i16, g) reads the 16 bytes at (g*16 + i16)*4
-// floats = row i16, channels 16j + 4g .. 16j + 4g + 3.
+// (p*KB + j)*256 floats; lane (i16, g) reads the 16 bytes of slot
+// g*16 + (i16 ^ 4g) = row i16, channels 16j + g, +4, +8, +12 (the row is
+// swizzled by 4g so that sixteen producer lanes, four rows x four slots,
+// write sixteen distinct bank groups).
 //
 // PST: the consumers leave each output tile in LDS (rows of BN channels x 16
 // bytes, a 16-byte pad per row so that 8 consecutive lanes' 16-byte writes
@@ -89,8 +93,9 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     // =========================== producer waves ===========================
     const int ptid = tid - NC * 64;
     const int64_t row_elems = (int64_t)K * 4;
-    // unit u -> (row = u % 16, 4-channel group c4 = u / 16): four 16-byte
-    // loads (one channel's four group values each), contiguous in the row
+    // unit u -> (16-channel block u / 64, row (u / 4) % 16, slot g = u % 4):
+    // load e reads channel 16 (u / 64) + 4e + g, so the four lanes of a quad
+    // read 64 contiguous bytes of their row
     auto load_tile = [&](f32x4 (&raw)[LPT], int i) {
       const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
       const int64_t rows = r0 < N ? (N - r0 < 16 ? N - r0 : 16) : 0;
@@ -98,25 +103,24 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const int u = k * PT + ptid;
-        const int row = u % 16, c4 = u / 16;
+        const int row = (u >> 2) & 15, jb = u >> 6, g = u & 3;
         const bool real = UNITS % PT == 0 || u < UNITS;
-        const uint32_t off = (uint32_t)(row * row_elems + 16 * c4) * 4;
+        const uint32_t off = (uint32_t)(row * row_elems * 4 + 256 * jb + 16 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           raw[4 * k + e] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, real ? off + 16 * e : 0x7FFFFFF0u, 0, 0));
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, real ? off + 64 * e : 0x7FFFFFF0u, 0, 0));
       }
     };
     auto store_tile = [&](const f32x4 (&raw)[LPT], float* buf) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const int u = k * PT + ptid;
-        const int row = u % 16, c4 = u / 16;
-        const int jb = c4 >> 2, g = c4 & 3;
+        const int row = (u >> 2) & 15, jb = u >> 6, g = u & 3;
         const bool real = UNITS % PT == 0 || u < UNITS;
         f32x4 p0, p2, pr, pi;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {  // channel 4*c4 + e: values t = 0..3
+        for (int e = 0; e < 4; ++e) {  // channel 16 jb + 4e + g: values t = 0..3
           const f32x4 v = raw[4 * k + e];
           const Spec4 sp = dft4(v[0], v[1], v[2], v[3]);  // scaled planes
           p0[e] = sp.f0;
@@ -125,7 +129,7 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
           pi[e] = sp.fi;
         }
         float* const dummy = xs + 2 * BUF + ptid * 4;
-        float* const dst = buf + jb * FRAG + (g * 16 + row) * 4;
+        float* const dst = buf + jb * FRAG + (g * 16 + (row ^ (g << 2))) * 4;
         *reinterpret_cast<f32x4*>(real ? dst + 0 * PS : dummy) = p0;
         *reinterpret_cast<f32x4*>(real ? dst + 1 * PS : dummy) = p2;
         *reinterpret_cast<f32x4*>(real ? dst + 2 * PS : dummy) = pr;
@@ -217,7 +221,7 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     const int i16 = lane & 15, g = lane >> 4;
     const int d0 = j * BN + wave * 16;  // this wave's first output channel
     // weight fragments (A operand): channel d0 + i16, reduction channels
-    // 16jb + 4g .. 16jb + 4g + 3 (one per k-step e of block jb)
+    // 16jb + 4e + g (k-step e of block jb), from the fragment-order copy
     f32x4 w0[KB], w2[KB], wr[KB], wi[KB];
     float bc[4];
     {
@@ -227,13 +231,13 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
       const __amdgpu_buffer_rsrc_t rr = rsrc32(spec + 2 * plane, plane_bytes);
       const __amdgpu_buffer_rsrc_t ri = rsrc32(spec + 3 * plane, plane_bytes);
       const __amdgpu_buffer_rsrc_t rb = rsrc32(bias, (uint32_t)n_pad * 4);
-      const uint32_t off = (uint32_t)((d0 + i16) * KP + 4 * g) * 4;
+      const uint32_t off = (uint32_t)((d0 / 16) * KB * 1024 + lane * 16);
 #pragma unroll
       for (int jb = 0; jb < KB; ++jb) {
-        w0[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, off + jb * 64, 0, 0));
-        w2[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, off + jb * 64, 0, 0));
-        wr[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off + jb * 64, 0, 0));
-        wi[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off + jb * 64, 0, 0));
+        w0[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, off + jb * 1024, 0, 0));
+        w2[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, off + jb * 1024, 0, 0));
+        wr[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off + jb * 1024, 0, 0));
+        wi[jb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off + jb * 1024, 0, 0));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -246,7 +250,7 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
       a.c0 = a.c2 = a.cr = a.ci = f32x4{};
 #pragma unroll
       for (int jb = 0; jb < KB; ++jb) {
-        const float* f = buf + jb * FRAG + lane * 4;
+        const float* f = buf + jb * FRAG + (lane ^ (g << 2)) * 4;
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(f + 0 * PS);
         const f32x4 x2 = *reinterpret_cast<const f32x4*>(f + 1 * PS);
         const f32x4 xr = *reinterpret_cast<const f32x4*>(f + 2 * PS);

@@ -1,6 +1,8 @@
 // Weight-spectrum precompute: the group DFT of every W[d,c,:] (length 4),
 // written once per weight update in the two operand layouts the matrix-core
-// kernels read (binary16 p4 plans: each also in fragment order).
+// kernels read, and for p4 plans also in the fragment order of the
+// producer/consumer kernels (binary16: both operands; binary32: the forward
+// operand).
 //
 // Flash EQ-Linear ("Approccio Algoritmico", "Specializzazione per il Gruppo di
 // Rotazione p4"): after the DFT along the group axis the convolution becomes a
@@ -33,6 +35,21 @@ __device__ __forceinline__ int64_t frag_index(int row, int col, int k_pad) {
   return ((int64_t)b * (k_pad >> 5) + s) * 512 + (g * 16 + i) * 8 + e;
 }
 
+// The binary32 operand of k_fwd_ws32.hip in fragment order: for 16-row block
+// b and 16-column block jb, the 1 KB fragment (b * k_pad / 16 + jb) holds lane
+// l = (i, g) at 16 l bytes: row 16 b + i and the columns g, g + 4, g + 8,
+// g + 12 of the block (the reduction order that kernel stages x in).
+__device__ __forceinline__ int64_t frag_index32(int row, int col, int k_pad) {
+  const int b = row >> 4, i = row & 15, jb = col >> 4, c = col & 15;
+  return ((int64_t)b * (k_pad >> 4) + jb) * 256 + ((c & 3) * 16 + i) * 4 + (c >> 2);
+}
+
+template <typename T>
+__device__ __forceinline__ int64_t frag_pos(int row, int col, int k_pad) {
+  if constexpr (sizeof(T) == 2) return frag_index(row, col, k_pad);
+  else return frag_index32(row, col, k_pad);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_weight_spectra(
     const T* __restrict__ W, const T* __restrict__ bias, T* __restrict__ spec_fwd,
@@ -54,7 +71,7 @@ __global__ __launch_bounds__(256) void k_weight_spectra(
     spec_fwd[2 * fwd_elems + i] = Elem<T>::from_f(s.fr);
     spec_fwd[3 * fwd_elems + i] = Elem<T>::from_f(s.fi);
     if (frag_fwd != nullptr) {
-      const int64_t f = frag_index(d, c, fwd_k);
+      const int64_t f = frag_pos<T>(d, c, fwd_k);
       frag_fwd[0 * fwd_elems + f] = Elem<T>::from_f(s.f0);
       frag_fwd[1 * fwd_elems + f] = Elem<T>::from_f(s.f2);
       frag_fwd[2 * fwd_elems + f] = Elem<T>::from_f(s.fr);
@@ -75,7 +92,7 @@ __global__ __launch_bounds__(256) void k_weight_spectra(
     spec_adj[2 * adj_elems + j] = Elem<T>::from_f(s.fr);
     spec_adj[3 * adj_elems + j] = Elem<T>::from_f(-s.fi);
     if (frag_adj != nullptr) {
-      const int64_t f = frag_index(c, d, adj_k);
+      const int64_t f = frag_pos<T>(c, d, adj_k);
       frag_adj[0 * adj_elems + f] = Elem<T>::from_f(s.f0);
       frag_adj[1 * adj_elems + f] = Elem<T>::from_f(s.f2);
       frag_adj[2 * adj_elems + f] = Elem<T>::from_f(s.fr);
@@ -108,7 +125,8 @@ hipError_t launch_spectra(const eqlinear_plan* p, const void* W, const void* bia
   } else {
     hipLaunchKernelGGL(k_weight_spectra<float>, dim3((unsigned)blocks), dim3(threads), 0, s,
                        (const float*)W, (const float*)bias, (float*)p->spec_fwd,
-                       (float*)p->spec_adj, nullptr, nullptr, p->bias_f32, p->zeros_f32, (int)p->C, (int)p->D,
+                       (float*)p->spec_adj, (float*)p->frag_fwd, (float*)p->frag_adj, p->bias_f32, p->zeros_f32,
+                       (int)p->C, (int)p->D,
                        (int)p->fwd.n_pad, (int)p->fwd.k_pad, (int)p->adj.n_pad, (int)p->adj.k_pad);
   }
   return hipGetLastError();

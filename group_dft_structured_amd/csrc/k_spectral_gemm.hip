@@ -248,7 +248,7 @@ hipError_t launch_forward(const eqlinear_plan* p, const void* x, void* y, int64_
   hipError_t e = launch_ws(p->tune, p->dtype, x, p->frag_fwd, p->bias_f32, y, N, (int)p->C,
                            (int)p->fwd.k_pad, (int)p->D, (int)p->fwd.n_pad, false, act, s);
   if (e != hipErrorNotSupported) return e;
-  e = launch_ws32(p->tune, p->dtype, x, p->spec_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
+  e = launch_ws32(p->tune, p->dtype, x, p->frag_fwd, p->bias_f32, y, N, (int)p->C, (int)p->fwd.k_pad,
                   (int)p->D, (int)p->fwd.n_pad, act, s);
   if (e != hipErrorNotSupported) return e;
   // the fallbacks store the linear output; a second pass applies the activation
