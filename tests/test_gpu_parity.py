@@ -213,12 +213,16 @@ def test_forward_ws32_cases(nc, np_, kb, monkeypatch):
         check_forward_full(16 * kb, 264, 1234 + kb, "f32", seed=nc * 100 + kb)
 
 
-F32_PATHS = {"ws32": {}, "tiled": {"EQL_NO_WS32": "1"}}
+F32_PATHS = {"ws32": {}, "tiled": {"EQL_NO_WS32": "1"},
+             # one consumer wave per output block over the whole reduction
+             "ws32_whole": {"EQL_WS32_NC": "6"},
+             # two consumer waves per output block over the reduction halves
+             "ws32_split": {"EQL_WS32_NC": "12"}}
 
 
 @pytest.mark.parametrize("path", sorted(F32_PATHS))
 @pytest.mark.parametrize("C,D,N", [(16, 4, 3), (96, 96, 12608), (48, 100, 999), (192, 768, 2049),
-                                   (64, 36, 257)])
+                                   (64, 36, 257), (96, 40, 1001), (96, 96, 17)])
 def test_forward_f32_paths(C, D, N, path, monkeypatch):
     for k, v in F32_PATHS[path].items():
         monkeypatch.setenv(k, v)
@@ -376,6 +380,7 @@ def _forward_act_case(C, D, N, dtype, act, T=4, seed=0):
     (96, 384, 3001, "f16", {"EQL_WS_NC": "4", "EQL_WS_NB": "2"}),  # 4 consumers of 32 channels
     (256, 96, 700, "f16", {}),                          # 8-channel producer units (long reduction)
     (96, 384, 3001, "f32", {}),                         # producer/consumer binary32
+    (96, 96, 1000, "f32", {"EQL_WS32_NC": "12"}),       # binary32, reduction split over wave pairs
     (33, 130, 65, "f16", {}),                           # fallback kernel + activation pass
     (33, 130, 65, "f32", {}),
     (96, 96, 1000, "f16", {"EQL_NO_WS": "1"}),          # tiled fallback + activation pass
