@@ -277,6 +277,41 @@ def test_backward_weight_paths(C, D, N, path, monkeypatch):
     assert max(e) <= TOL["f16"], e
 
 
+def test_backward_weight_calls_in_a_row():
+    """Weight-gradient calls of one plan in a row, with split counts that
+    change from call to call, each match the
+    oracle, and a repeated shape repeats its bits; a plan that never had a
+    set_weight gives the same gradient."""
+    torch = torch_mod()
+    C, D = 96, 384
+    bare = Plan(C, D, "f16")
+    inp = make_inputs(C, D, 777, dtype="f16", seed=70, bias=True, dy=True)
+    dW, db = bare.backward_weight(to_dev(inp["x"]), to_dev(inp["dy"]))
+    _sync()
+    ref_dW, ref_db = oracle.backward_weight(inp["x"], inp["dy"])
+    assert max(rel_err(to_np64(dW), ref_dW), rel_err(to_np64(db), ref_db)) <= TOL["f16"]
+    bare.close()
+    plan = Plan(C, D, "f16")
+    w = make_inputs(C, D, 1, dtype="f16", seed=71, bias=True)
+    plan.set_weight(to_dev(w["W"]), to_dev(w["bias"]))
+    first = None
+    for i, N in enumerate((3001, 12608, 95, 1, 3001)):
+        inp = make_inputs(C, D, N, dtype="f16", seed=72 if N == 3001 else 73 + i,
+                          bias=True, dy=True)
+        dW, db = plan.backward_weight(to_dev(inp["x"]), to_dev(inp["dy"]))
+        _sync()
+        ref_dW, ref_db = oracle.backward_weight(inp["x"], inp["dy"])
+        e = (rel_err(to_np64(dW), ref_dW), rel_err(to_np64(db), ref_db))
+        print(f"backward_weight call {i} N={N}: dW {e[0]:.3e} dbias {e[1]:.3e}", flush=True)
+        assert max(e) <= TOL["f16"], (N, e)
+        if N == 3001:
+            if first is None:
+                first = (dW.clone(), db.clone())
+            else:
+                assert torch.equal(first[0], dW) and torch.equal(first[1], db)
+    plan.close()
+
+
 def test_no_bias_equals_zero_bias():
     inp = make_inputs(24, 40, 100, dtype="f32", seed=3, bias=True)
     plan = Plan(24, 40, "f32")
