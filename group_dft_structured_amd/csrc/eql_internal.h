@@ -59,6 +59,7 @@ struct Tuning {
   int64_t ws_small_bytes;  // outputs up to this size take the write-through producer stores
   // producer/consumer binary32 forward
   int ws32_off, ws32_nc, ws32_np, ws32_qx, ws32_stream, ws32_pst;
+  int ws32_tail;  // split last round of tiles into (tile, block) units (0/1)
   // general tiled kernel: tile shape
   int gemm_tile;
   // backward_weight: producer/consumer kernel off, tiled kernel forced,

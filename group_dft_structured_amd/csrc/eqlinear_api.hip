@@ -101,6 +101,7 @@ eql::Tuning eql::read_tuning() {
   t.ws32_qx = knob("EQL_WS32_QX", 1, 1 << 20);
   t.ws32_stream = knob("EQL_WS32_STREAM", 0, 1);
   t.ws32_pst = knob("EQL_WS32_PST", 0, 1);
+  t.ws32_tail = knob("EQL_WS32_TAIL", 0, 1);
   t.gemm_tile = knob("EQL_GEMM_TILE", 0, 4);
   t.bws_off = knob("EQL_NO_BWS", 0, 1);
   t.bw_tiled = knob("EQL_BW_TILED", 0, 1);

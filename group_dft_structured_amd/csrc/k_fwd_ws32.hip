@@ -68,10 +68,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc32(const void* base, uint3
 // leaves its four accumulators in LDS; in the next tile's phase the first
 // half's wave adds them to its own, in a fixed order, and runs the epilogue
 // of the previous tile, so the producers store each tile one phase later.
+//
+// tail_split (KSPLIT only): the last, partial round of tiles is cut into
+// (tile, output block) units, one per worker, so that no worker runs a whole
+// extra tile while the others idle: worker q takes the full tiles
+// q + i*Q (i < n_rt / Q) and then, if q < (n_rt mod Q) * NBLK, block
+// q mod NBLK of tile (n_rt / Q)*Q + q / NBLK.  In that unit only the two
+// waves of that block run products, and the producers store its 16
+// channels.
 template <int NC, int NP, int KB, int YP, bool ACT = false, bool PST = false, bool KSPLIT = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     const float* __restrict__ x, const float* __restrict__ spec, const float* __restrict__ bias,
-    float* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act) {
+    float* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act, int tail_split) {
   static_assert(!KSPLIT || (PST && NC % 2 == 0 && KB % 2 == 0), "split reduction: paired waves, staged output");
   constexpr int NBLK = KSPLIT ? NC / 2 : NC;  // 16-channel output blocks
   constexpr int KBW = KSPLIT ? KB / 2 : KB;   // reduction blocks per consumer wave
@@ -99,8 +107,27 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
   const int j = slot % n_ct;
   const int q = (slot / n_ct) * 8 + xcd, Q = Qx * 8;
   const int n_rt = (N + 15) / 16;
-  const int n_my = q < n_rt ? (n_rt - 1 - q) / Q + 1 : 0;  // tiles of this worker
+  int n_full, n_my, tail_tile = 0, tail_blk = -1;
+  if (KSPLIT && tail_split) {
+    n_full = n_rt / Q;
+    const int units = (n_rt - n_full * Q) * NBLK;
+    n_my = n_full + (q < units ? 1 : 0);
+    if (q < units) {
+      tail_tile = n_full * Q + q / NBLK;
+      tail_blk = q % NBLK;
+    }
+  } else {
+    n_my = q < n_rt ? (n_rt - 1 - q) / Q + 1 : 0;  // tiles of this worker
+    n_full = n_my;
+  }
   if (n_my == 0) return;  // whole work-group
+  // first row of this worker's tile i (past its last tile: beyond the rows,
+  // which load as zeros)
+  auto row0 = [&](int i) -> int64_t {
+    if (i < n_full) return (int64_t)(q + (int64_t)i * Q) * 16;
+    if (i == n_full && tail_blk >= 0) return (int64_t)tail_tile * 16;
+    return (int64_t)n_rt * 16;
+  };
 
   if (wave >= NC) {
     // =========================== producer waves ===========================
@@ -110,7 +137,7 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     // load e reads channel 16 (u / 64) + 4e + g, so the four lanes of a quad
     // read 64 contiguous bytes of their row
     auto load_tile = [&](f32x4 (&raw)[LPT], int i) {
-      const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
+      const int64_t r0 = row0(i);
       const int64_t rows = r0 < N ? (N - r0 < 16 ? N - r0 : 16) : 0;
       const __amdgpu_buffer_rsrc_t rx = rsrc32(x + (r0 < N ? r0 : 0) * row_elems, (uint32_t)(rows * row_elems * 4));
 #pragma unroll
@@ -152,7 +179,8 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     // PST: write staged output tile t (16 rows x BN channels, 16 bytes = one
     // channel's four group values per lane, whole rows per wave instruction)
     auto store_out = [&](int t) {
-      const int64_t r0 = (int64_t)(q + (int64_t)t * Q) * 16;
+      const int64_t r0 = row0(t);
+      const int only_blk = t == n_full ? tail_blk : -1;  // a tail unit: its block only
       const int64_t rows = N - r0 < 16 ? N - r0 : 16;
       const __amdgpu_buffer_rsrc_t ry = rsrc32(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 16));
       const float* const sb = obuf + (t & 1) * OBUF;
@@ -166,7 +194,8 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
         const int row = u / BN, ch = u % BN;
         const u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * OPITCH + 4 * ch);
         const int col = j * BN + ch;
-        const uint32_t off = (real && col < n_out) ? (uint32_t)((row * n_out + col) * 16) : 0x7FFFFFF0u;
+        const bool mine = only_blk < 0 || ch / 16 == only_blk;
+        const uint32_t off = (real && mine && col < n_out) ? (uint32_t)((row * n_out + col) * 16) : 0x7FFFFFF0u;
         __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, YP);
       }
     };
@@ -331,7 +360,7 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
     };
     // lane holds channels d0 + 4g + r of row r0 + i16: 64 contiguous bytes
     auto epilogue = [&](int i, const Acc& a) {
-      const int64_t r0 = (int64_t)(q + (int64_t)i * Q) * 16;
+      const int64_t r0 = row0(i);
       const int64_t rows = N - r0 < 16 ? N - r0 : 16;
       const __amdgpu_buffer_rsrc_t ry = rsrc32(y + r0 * n_out * 4, (uint32_t)(rows * n_out * 16));
       const int col = d0 + 4 * g;
@@ -357,7 +386,13 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
       // half; the second half parks them in partial buffer i % 2, the first
       // half adds the parked partial of tile i - 1 to its own and runs that
       // tile's epilogue (barrier n_my + 1 follows the last one)
+      // in a tail unit only the waves of its block work
+      auto idle = [&](int i) { return i == n_full && tail_blk >= 0 && blk != tail_blk; };
+      auto products_i = [&](Acc& a, const float* buf, int i) {
+        if (!idle(i)) products(a, buf);
+      };
       auto park = [&](int i, const Acc& a) {
+        if (idle(i)) return;
         f32x4* pp = reinterpret_cast<f32x4*>(pbuf + (i & 1) * PBUF) + blk * 4 * 64 + lane;
         pp[0 * 64] = a.c0;
         pp[1 * 64] = a.c2;
@@ -365,6 +400,7 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
         pp[3 * 64] = a.ci;
       };
       auto finish = [&](int i, Acc& a) {
+        if (idle(i)) return;
         const f32x4* pp = reinterpret_cast<const f32x4*>(pbuf + (i & 1) * PBUF) + blk * 4 * 64 + lane;
         a.c0 += pp[0 * 64];
         a.c2 += pp[1 * 64];
@@ -375,17 +411,17 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f32(
       Acc A, B;
       int i = 0;
       for (; i + 1 < n_my; i += 2) {
-        products(A, xs);
+        products_i(A, xs, i);
         if (half) park(i, A);
         else if (i > 0) finish(i - 1, B);
         __syncthreads();  // barrier i+1
-        products(B, xs + BUF);
+        products_i(B, xs + BUF, i + 1);
         if (half) park(i + 1, B);
         else finish(i, A);
         __syncthreads();  // barrier i+2
       }
       if (i < n_my) {  // odd tile count: the last tile is in buffer 0
-        products(A, xs);
+        products_i(A, xs, i);
         if (half) park(i, A);
         else if (i > 0) finish(i - 1, B);
         __syncthreads();  // barrier n_my
@@ -433,10 +469,15 @@ static hipError_t launch_ws32_t(const Tuning& tn, const void* x, const void* spe
   // larger ones by the consumers (C=192, D=768: producer stores measured
   // 4038 us against 3690).
   const bool pst = KSPLIT || pick32(tn.ws32_pst, y_bytes <= (128LL << 20) ? 1 : 0) != 0;
+  // the last round of tiles cut into (tile, output block) units when they
+  // fit one per worker (split reduction only)
+  const int64_t Qw = (int64_t)qx * 8, tail = n_rt % Qw;
+  const int tail_split =
+      (KSPLIT && tail > 0 && tail * (BN / 16) <= Qw && pick32(tn.ws32_tail, 1) != 0) ? 1 : 0;
   const dim3 grid(blocks), block((NC + NP) * 64);
 #define EQL_WS32_LAUNCH(YP_, ACT_, PST_)                                                              \
   hipLaunchKernelGGL((k_fwd_ws_f32<NC, NP, KB, YP_, ACT_, PST_ || KSPLIT, KSPLIT>), grid, block, 0, s, (const float*)x, \
-                     (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx, act)
+                     (const float*)spec, bias, (float*)y, (int)N, K, n_out, n_pad, n_ct, qx, act, tail_split)
 #define EQL_WS32_MODES(YP_, ACT_)                      \
   do {                                                 \
     if (pst) EQL_WS32_LAUNCH(YP_, ACT_, true);         \

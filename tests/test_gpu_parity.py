@@ -216,13 +216,16 @@ def test_forward_ws32_cases(nc, np_, kb, monkeypatch):
 F32_PATHS = {"ws32": {}, "tiled": {"EQL_NO_WS32": "1"},
              # one consumer wave per output block over the whole reduction
              "ws32_whole": {"EQL_WS32_NC": "6"},
-             # two consumer waves per output block over the reduction halves
-             "ws32_split": {"EQL_WS32_NC": "12"}}
+             # two consumer waves per output block over the reduction halves;
+             # the last round of tiles cut into (tile, output block) units
+             # where they fit one per worker, or run as whole tiles
+             "ws32_split": {"EQL_WS32_NC": "12"},
+             "ws32_split_whole_tiles": {"EQL_WS32_NC": "12", "EQL_WS32_TAIL": "0"}}
 
 
 @pytest.mark.parametrize("path", sorted(F32_PATHS))
 @pytest.mark.parametrize("C,D,N", [(16, 4, 3), (96, 96, 12608), (48, 100, 999), (192, 768, 2049),
-                                   (64, 36, 257), (96, 40, 1001), (96, 96, 17)])
+                                   (64, 36, 257), (96, 40, 1001), (96, 96, 17), (96, 96, 4097)])
 def test_forward_f32_paths(C, D, N, path, monkeypatch):
     for k, v in F32_PATHS[path].items():
         monkeypatch.setenv(k, v)
