@@ -228,10 +228,11 @@ def main():
 
         # ---- cold timing: the memory-side cache evicted before every launch ----
         evict = torch.empty((EVICT_BYTES,), dtype=torch.uint8, device=dev)
-        cold_us = {}
+        cold_us, clean_us = {}, {}
         for name, fn in (() if args.no_graph else passes.items()):
             if name != "set_weight":
                 cold_us[name] = time_cold(fn, stream, args.cold_reps, evict)
+                clean_us[name] = time_cold(fn, stream, args.cold_reps, evict, clean=True)
 
     if args.no_graph:  # counter-collection run: no per-kernel timing, no JSON line
         print(f"eager steps done: {gpu_ms:.4f} ms/step", flush=True)
@@ -264,6 +265,11 @@ def main():
             kinfo[name].update({"cold_us": round(cus, 3), "cold_hbm_gbps": round(cg, 1),
                                 "cold_hbm_frac": round(cg / PEAK_HBM_GBPS, 4),
                                 "cold_tflops_actual": round(flops_pass[name] / (cus * 1e-6) / 1e12, 2)})
+        if name in clean_us:
+            kus = clean_us[name]
+            kg = bytes_alg[name] / (kus * 1e-6) / 1e9
+            kinfo[name].update({"cold_clean_us": round(kus, 3), "cold_clean_hbm_gbps": round(kg, 1),
+                                "cold_clean_hbm_frac": round(kg / PEAK_HBM_GBPS, 4)})
 
     fwd_us = per_pass_us["forward"]
     value = flops / (fwd_us * 1e-6) / 1e12
@@ -284,6 +290,9 @@ def main():
     roof["cold_us"] = kinfo[dominant].get("cold_us")
     roof["cold_achieved"] = kinfo[dominant].get("cold_hbm_gbps")
     roof["cold_frac"] = kinfo[dominant].get("cold_hbm_frac")
+    # the same with the cache evicted by reads (no dirty lines to write back)
+    roof["cold_clean_us"] = kinfo[dominant].get("cold_clean_us")
+    roof["cold_clean_frac"] = kinfo[dominant].get("cold_clean_hbm_frac")
     roof["traffic"] = read_traffic(f"{args.workload}.{dtype}.{dominant}", src_hash)
 
     out = {
@@ -364,20 +373,28 @@ def time_graph(fn, stream, reps, replays):
 EVICT_BYTES = 512 << 20
 
 
-def time_cold(fn, stream, reps, evict):
+def time_cold(fn, stream, reps, evict, clean=False):
     """Mean launch duration (us) of fn with the memory-side cache evicted
     before every launch: a 512 MiB fill of `evict` runs first on the same
     stream, then HIP events bracket fn alone.  The 256 MB memory-side cache
     and the L2s then hold none of fn's inputs, so each launch reads them from
-    HBM (the cold figure; the graph replays of time_graph are warm)."""
+    HBM (the cold figure; the graph replays of time_graph are warm).  The
+    fill leaves the cache full of dirty lines, whose write-back fn then pays
+    as it allocates; with clean=True the eviction is a 512 MiB read (a sum)
+    instead, which leaves clean lines: inputs in HBM, nothing to write back."""
     import torch
     tot = 0.0
+    ev64 = evict.view(torch.int64)
+    acc = torch.empty((), dtype=torch.int64, device=evict.device)
     with torch.cuda.stream(stream):
         fn()
         torch.cuda.synchronize()
         pairs = []
         for r in range(reps):
-            evict.fill_(r & 0x7F)
+            if clean:
+                torch.sum(ev64, dim=(0,), out=acc)
+            else:
+                evict.fill_(r & 0x7F)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()
@@ -428,9 +445,11 @@ def extra_forward_configs(stream, evict, reps):
         if cold:
             cus = time_cold(fn, stream, reps, evict)
             ctf = flops / (cus * 1e-6) / 1e12
+            kus = time_cold(fn, stream, reps, evict, clean=True)
             rec.update({"cold_us": round(cus, 3), "cold_tflops_actual": round(ctf, 2),
                         "cold_mfma_peak_frac": round(ctf / PEAK_MFMA_TFLOPS[dtype], 4),
-                        "cold_hbm_gbps": round(nbytes / (cus * 1e-6) / 1e9, 1)})
+                        "cold_hbm_gbps": round(nbytes / (cus * 1e-6) / 1e9, 1),
+                        "cold_clean_us": round(kus, 3)})
         out[f"{name}_{dtype}_forward"] = rec
         plan.close()
         del x, W, b, y
