@@ -62,6 +62,8 @@ def parse_args():
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="print per-kernel matrix-core utilisation from a rocprofv3 --pmc run "
                          "of MFMA_COUNTERS under DIR, then exit")
+    ap.add_argument("--summarize-clock", metavar="DIR",
+                    help="per-dispatch shader clock from a rocprofv3 --pmc GRBM_GUI_ACTIVE run")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run found under DIR")
     return ap.parse_args()
@@ -114,6 +116,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
+        return
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
@@ -722,6 +727,26 @@ def summarize_mfma(root):
         bpi = busy / insts if insts > 0 else 0.0
         print(f"{util:9.4f} {futil:9.4f} {bpi:9.2f} {insts:10.0f} {(m16 + m32) * 512 / 1e9:7.3f} "
               f"{d:8.2f} {len(dur[k]):5d}  {k[:90]}")
+
+
+def summarize_clock(root):
+    """Per dispatch of the layer's kernels: duration, GRBM_GUI_ACTIVE cycles
+    per XCD (the counter sums the eight XCDs) and their ratio, the shader
+    clock the dispatch ran at.  Constant cycles with a varying duration mean
+    a pass bound by on-chip work at the shader clock, not by memory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {root}")
+    print(f"{'dispatch':>8} {'dur_us':>9} {'Mcyc/XCD':>9} {'GHz':>6}  kernel")
+    for r in csv.DictReader(open(files[0])):
+        if r["Counter_Name"] != "GRBM_GUI_ACTIVE" or "eql" not in r["Kernel_Name"]:
+            continue
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        cyc = float(r["Counter_Value"]) / 8
+        print(f"{r['Dispatch_Id']:>8} {dur:9.1f} {cyc / 1e6:9.3f} {cyc / (dur * 1e3):6.2f}  "
+              f"{r['Kernel_Name'][:90]}")
 
 
 def summarize_trace(root):
