@@ -743,8 +743,6 @@ hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const
   EQL_WS_CASE(8, 4, 1, 1)
   EQL_WS_CASE(8, 4, 1, 2)
   EQL_WS_CASE(8, 4, 1, 3)
-  EQL_WS_CASE(8, 2, 1, 3)
-  EQL_WS_CASE(4, 4, 1, 3)
   EQL_WS_CASE(4, 4, 1, 8)
   EQL_WS_CASE(4, 4, 1, 12)
   EQL_WS_CASE(3, 4, 1, 8)
