@@ -166,10 +166,14 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
         }
       };
       // Ring of four steps in registers.  Between barriers i and i+1 the
-      // producers first request step i+4 into the slot that step i left
-      // (so the vector-memory queue works while they transform), then
-      // transform step i+1 into buffer (i+1) % 2; the loads have three
-      // intervals to arrive.  Steps past the split load as zeros.
+      // producers first transform step i+1 into buffer (i+1) % 2, then
+      // request step i+4 into the slot that step i left; the loads have
+      // about three intervals to arrive.  Requests issued before the
+      // transform held it back while the address unit took them (the
+      // pass ran about 1 us slower at 12608 x 96 x 384), so they follow it
+      // in program order, with no scheduling fence between the two (a fence
+      // there gave back half of the gain).  Steps past the split load as
+      // zeros.
       half8 ra[NBK], rb[NBK], rc[NBK], rd[NBK];
       load_step(ra, 0);
       __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
@@ -181,20 +185,20 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
       __builtin_amdgcn_sched_barrier(0);
       int i = 0;
       for (; i + 4 <= nsteps - 1; i += 4) {
-        load_step(ra, i + 4);
         store_step(rb, lds + BUF);
+        load_step(ra, i + 4);
         __syncthreads();  // barrier i+1
         __builtin_amdgcn_sched_barrier(0);
-        load_step(rb, i + 5);
         store_step(rc, lds);
+        load_step(rb, i + 5);
         __syncthreads();  // barrier i+2
         __builtin_amdgcn_sched_barrier(0);
-        load_step(rc, i + 6);
         store_step(rd, lds + BUF);
+        load_step(rc, i + 6);
         __syncthreads();  // barrier i+3
         __builtin_amdgcn_sched_barrier(0);
-        load_step(rd, i + 7);
         store_step(ra, lds);
+        load_step(rd, i + 7);
         __syncthreads();  // barrier i+4
         __builtin_amdgcn_sched_barrier(0);
       }
