@@ -762,6 +762,21 @@ def summarize_trace(root):
             continue
         print(f"{float(r['AverageNs']) / 1e3:10.3f} {float(r['MinNs']) / 1e3:10.3f} "
               f"{float(r['MaxNs']) / 1e3:10.3f} {r['Calls']:>6}  {r['Name'][:110]}")
+    # medians from the per-dispatch trace: a run that also times cold launches
+    # has them in its average and maximum, while the median is a warm launch
+    traces = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        durs = {}
+        for r in csv.DictReader(open(traces[0])):
+            name = r.get("Kernel_Name", "")
+            if "at::" in name or "rocclr" in name:
+                continue
+            durs.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print("#\n# medians over all launches of the traced run")
+        print(f"# {'median_us':>9} {'calls':>6}  kernel")
+        for name, v in sorted(durs.items(), key=lambda kv: -sorted(kv[1])[len(kv[1]) // 2]):
+            v = sorted(v)
+            print(f"# {v[len(v) // 2]:9.3f} {len(v):>6}  {name[:110]}")
 
 
 WORKLOAD_DTYPE = {"vit_s_mlp": "f16", "vit_s_proj": "f16", "swin_stage": "f16", "tiny": "f32",
