@@ -18,7 +18,7 @@
 //
 // Roles inside a work-group, one barrier per 32-row step:
 //  * NP producer waves load each step's dy and x rows (range-checked 16-byte
-//    buffer loads, three steps ahead in a register ring), apply the length-4
+//    buffer loads, one step ahead of the transform), apply the length-4
 //    butterfly on the matrix cores (below) into the scaled planes X0/4, X2/4,
 //    Xr/2, Xi/2 (eql_device.h) and write them to LDS in matrix-core fragment
 //    order with the rows along the fragments' k; dbias is summed in fp32 from
@@ -165,56 +165,38 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
           }
         }
       };
-      // Ring of four steps in registers.  Between barriers i and i+1 the
-      // producers first transform step i+1 into buffer (i+1) % 2, then
-      // request step i+4 into the slot that step i left; the loads have
-      // about three intervals to arrive.  Requests issued before the
-      // transform held it back while the address unit took them (the
-      // pass ran about 1 us slower at 12608 x 96 x 384), so they follow it
-      // in program order, with no scheduling fence between the two (a fence
-      // there gave back half of the gain).  Steps past the split load as
-      // zeros.
-      half8 ra[NBK], rb[NBK], rc[NBK], rd[NBK];
+      // Two steps in registers.  Between barriers i and i+1 the producers
+      // transform step i+1 (loaded in the previous interval) into buffer
+      // (i+1) % 2, then request step i+2 into the slot step i left, so each
+      // load has one interval to arrive.  Measured at 12608 x 96 x 384
+      // (partials kernel, back-to-back launches): requests issued before the
+      // transform instead of after it held the transform back (+0.9 us), and
+      // prefetching two or three steps ahead was slower (+0.3 and +1.0 us):
+      // the address unit then holds more requests, and a wave's next request
+      // waits behind them.  No scheduling fence separates the transform and
+      // the requests (one there cost half of the load-order gain).  Steps
+      // past the split load as zeros.
+      half8 ra[NBK], rb[NBK];
       load_step(ra, 0);
       __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
       load_step(rb, 1);
-      load_step(rc, 2);
-      load_step(rd, 3);
       store_step(ra, lds);
       __syncthreads();  // barrier 0: step 0 is in buffer 0
       __builtin_amdgcn_sched_barrier(0);
       int i = 0;
-      for (; i + 4 <= nsteps - 1; i += 4) {
+      for (; i + 2 <= nsteps - 1; i += 2) {
         store_step(rb, lds + BUF);
-        load_step(ra, i + 4);
+        load_step(ra, i + 2);
         __syncthreads();  // barrier i+1
         __builtin_amdgcn_sched_barrier(0);
-        store_step(rc, lds);
-        load_step(rb, i + 5);
+        store_step(ra, lds);
+        load_step(rb, i + 3);
         __syncthreads();  // barrier i+2
         __builtin_amdgcn_sched_barrier(0);
-        store_step(rd, lds + BUF);
-        load_step(rc, i + 6);
-        __syncthreads();  // barrier i+3
-        __builtin_amdgcn_sched_barrier(0);
-        store_step(ra, lds);
-        load_step(rd, i + 7);
-        __syncthreads();  // barrier i+4
-        __builtin_amdgcn_sched_barrier(0);
       }
-      // at most three steps left, already in rb, rc, rd; step i+1 goes to buffer 1
-      const int rest = nsteps - 1 - i;
-      if (rest > 0) {
+      if (nsteps - 1 - i > 0) {  // one step left, in rb, for buffer 1
         store_step(rb, lds + BUF);
         __syncthreads();
-        if (rest > 1) {
-          store_step(rc, lds);
-          __syncthreads();
-          if (rest > 2) {
-            store_step(rd, lds + BUF);
-            __syncthreads();
-          }
-        }
       }
       if constexpr (IS_DY) {
         // bias partial of this split: lane (j, 0) holds channels 2j, 2j + 1
