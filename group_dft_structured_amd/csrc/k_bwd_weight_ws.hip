@@ -171,9 +171,9 @@ __global__ __launch_bounds__((NWD * NWC + NP) * 64) void k_bwd_weight_ws(
       // load has one interval to arrive.  Measured at 12608 x 96 x 384
       // (partials kernel, back-to-back launches): requests issued before the
       // transform instead of after it held the transform back (+0.9 us), and
-      // prefetching two or three steps ahead was slower (+0.3 and +1.0 us):
-      // the address unit then holds more requests, and a wave's next request
-      // waits behind them.  No scheduling fence separates the transform and
+      // prefetching two or three steps ahead was slower (+0.3 and +1.0 us;
+      // more requests in flight per CU, with the transform waiting behind
+      // them).  No scheduling fence separates the transform and
       // the requests (one there cost half of the load-order gain).  Steps
       // past the split load as zeros.
       half8 ra[NBK], rb[NBK];
