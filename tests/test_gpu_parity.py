@@ -428,3 +428,35 @@ def test_forward_act(C, D, N, dtype, env, act, monkeypatch):
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     _forward_act_case(C, D, N, dtype, act, seed=21)
+
+
+# ---- seeded random shapes for the weight gradient ---------------------------
+
+def _random_bw_shapes(n, seed=11):
+    """(C, D, N, splits) with even channel counts (the producer/consumer
+    kernel's domain), row counts that leave ragged 32-row steps and splits
+    of odd and even step counts; splits 0 keeps the library's choice."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        C = 2 * int(rng.integers(1, 97))
+        D = 2 * int(rng.integers(1, 129))
+        N = int(rng.integers(1, 4000))
+        out.append((C, D, N, int(rng.choice([0, 1, 2, 3, 5, 9]))))
+    return out
+
+
+@pytest.mark.parametrize("C,D,N,splits", _random_bw_shapes(16))
+def test_backward_weight_random_shapes(C, D, N, splits, monkeypatch):
+    if splits:
+        monkeypatch.setenv("EQL_BWS_S", str(splits))
+    inp = make_inputs(C, D, N, dtype="f16", seed=C * 7 + D + N, bias=True, dy=True)
+    plan = Plan(C, D, "f16")
+    dW, db = plan.backward_weight(to_dev(inp["x"]), to_dev(inp["dy"]))
+    _sync()
+    ref_dW, ref_db = oracle.backward_weight(inp["x"], inp["dy"])
+    e = (rel_err(to_np64(dW), ref_dW), rel_err(to_np64(db), ref_db))
+    print(f"backward_weight random C={C} D={D} N={N} splits={splits}: dW {e[0]:.3e} dbias {e[1]:.3e}",
+          flush=True)
+    assert max(e) <= TOL["f16"], e
+    plan.close()
