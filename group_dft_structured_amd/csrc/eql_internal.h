@@ -56,6 +56,7 @@ struct Tuning {
   int ws_out;       // 1: consumers store their fragments (streaming)
   int ws_split;     // split producer/consumer stores beyond the cache (0/1)
   int ws_wfirst;    // consumers' weight fragments before the second and third tiles (0/1)
+  int ws_ksplit;    // 0: backward_input over 384 channels without split-reduction consumers
   int64_t ws_small_bytes;  // outputs up to this size take the write-through producer stores
   // producer/consumer binary32 forward
   int ws32_off, ws32_nc, ws32_np, ws32_qx, ws32_stream, ws32_pst;

@@ -93,6 +93,7 @@ eql::Tuning eql::read_tuning() {
   t.ws_out = knob("EQL_WS_OUT", 0, 1);
   t.ws_split = knob("EQL_WS_SPLIT", 0, 1);
   t.ws_wfirst = knob("EQL_WS_WFIRST", 0, 1);
+  t.ws_ksplit = knob("EQL_WS_KSPLIT", 0, 1);
   const int small_mb = knob("EQL_WS_SMALL_MB", 0, 1 << 20);
   t.ws_small_bytes = small_mb >= 0 ? (int64_t)small_mb << 20 : (int64_t)128 << 20;
   t.ws32_off = knob("EQL_NO_WS32", 0, 1);

@@ -26,6 +26,15 @@
 // so memory back-pressure never stalls the matrix cores.  Work-groups that
 // read the same x tiles (different channel ranges) sit on the same XCD and
 // share its L2.
+//
+// Split reduction (KSPLIT, backward_input over 384 channels): two consumer
+// waves per 16-channel output block, each holding the weight fragments of
+// half of the reduction steps, so the weights take half the VGPRs, twelve
+// waves fit (six producers instead of four) and each producer transforms
+// two units per tile instead of three.  The second wave of a pair parks its
+// accumulators in LDS; the first adds them in a fixed order one tile later
+// and runs the epilogue, so the producers store each tile two phases after
+// its products.
 #include <type_traits>
 
 #include "eql_device.h"
@@ -80,12 +89,20 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // four lanes of a producer quad read 64 contiguous bytes of a row; the
 // weight fragments (k_spectra.hip) use the same order.
 template <int NC, int NP, int NB, int KS, int YP, bool G8, bool STAGGER, bool PST, bool PIPE,
-          bool SPLIT, bool ACT = false>
+          bool SPLIT, bool ACT = false, bool KSPLIT = false>
 __device__ __forceinline__ void ws_body(
     const _Float16* __restrict__ x, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ y, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int act,
     int wfirst) {
-  constexpr int BN = NC * NB * 16;
+  // KSPLIT: two consumer waves per output block, each over half of the
+  // reduction steps (wave 2b + h: block b, half h); the second half leaves
+  // its accumulators in LDS and the first adds them, in a fixed order, one
+  // tile later, before the epilogue
+  static_assert(!KSPLIT || (!PIPE && PST && !SPLIT && !ACT && NB == 1 && NC % 2 == 0 && KS % 2 == 0),
+                "split reduction: paired waves, staged output, no pipelining");
+  constexpr int NCB = KSPLIT ? NC / 2 : NC;  // consumer output blocks of NB x 16 channels
+  constexpr int KSH = KSPLIT ? KS / 2 : KS;  // reduction steps per consumer wave
+  constexpr int BN = NCB * NB * 16;
   constexpr int KP = KS * 32;
   constexpr int FRAG = 512;                   // halves per fragment
   constexpr int PS = KS * FRAG;               // plane stride (halves)
@@ -109,6 +126,8 @@ __device__ __forceinline__ void ws_body(
   constexpr int OBUF = 16 * OPITCH;   // halves per staged output tile
   __shared__ __attribute__((aligned(16))) _Float16 xs[2 * BUF + DUMMY + (PST ? 2 * OBUF : 0)];
   _Float16* const obuf = xs + 2 * BUF + DUMMY;  // PST staging (two tiles)
+  // KSPLIT: parked accumulators of the second halves, [2][NCB][6][64] f32x4
+  __shared__ __attribute__((aligned(16))) f32x4 park[KSPLIT ? 2 * NCB * 6 * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
@@ -272,7 +291,7 @@ __device__ __forceinline__ void ws_body(
     // phase p (between barriers p and p + 1) first writes out the tile the
     // consumers staged in phase p - 1: tile p - 1, or p - 2 when their
     // epilogue lags their products by one tile (PIPE)
-    constexpr int LAG = PIPE ? 2 : 1;
+    constexpr int LAG = (PIPE || KSPLIT) ? 2 : 1;
     auto out_step = [&](int p) {
       if (PST && p >= LAG) store_out(p - LAG);
     };
@@ -342,7 +361,7 @@ __device__ __forceinline__ void ws_body(
         __syncthreads();
       }
     }
-    if (PIPE) {
+    if (PIPE || KSPLIT) {
       // phase n_my - 1, barrier n_my (the consumers' last products are done),
       // and with PST phase n_my and barrier n_my + 1 (their last epilogue)
       out_step(n_my - 1);
@@ -362,11 +381,13 @@ __device__ __forceinline__ void ws_body(
     // =========================== consumer waves ===========================
     const int i16 = lane & 15, g = lane >> 4;
     const int xslot = lane ^ (g << 2);      // LDS slot of row i16, slice g
-    const int d0 = j * BN + wave * NB * 16;  // this wave's first output channel
+    const int cw = KSPLIT ? wave >> 1 : wave;  // this wave's output block
+    const int kh = KSPLIT ? wave & 1 : 0;      // its half of the reduction (KSPLIT)
+    const int d0 = j * BN + cw * NB * 16;      // its first output channel
     // weight fragments (A operand): channel d0 + 16nb + i16, reduction
     // channels 32s + 8g .. 32s + 8g + 7, from the operand in fragment order
     // (1 KB per fragment, lane l at 16 l bytes: one contiguous wave load)
-    half8 w0[NB][KS], w2[NB][KS], wr[NB][KS], wi[NB][KS];
+    half8 w0[NB][KSH], w2[NB][KSH], wr[NB][KSH], wi[NB][KSH];
     float bc[NB][4];
     {
       const uint32_t plane_bytes = (uint32_t)n_pad * KP * 2;
@@ -377,9 +398,9 @@ __device__ __forceinline__ void ws_body(
       const __amdgpu_buffer_rsrc_t rb = rsrc(bias, (uint32_t)n_pad * 4);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const uint32_t off = (uint32_t)(((d0 / 16 + nb) * KS) * 1024 + lane * 16);
+        const uint32_t off = (uint32_t)(((d0 / 16 + nb) * KS + kh * KSH) * 1024 + lane * 16);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KSH; ++s) {
           w0[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r0, off + s * 1024, 0, 0));
           w2[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r2, off + s * 1024, 0, 0));
           wr[nb][s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rr, off + s * 1024, 0, 0));
@@ -409,8 +430,8 @@ __device__ __forceinline__ void ws_body(
         if constexpr (!ACC4) a.cq[nb] = a.cn[nb] = f32x4{};
       }
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const _Float16* f = buf + s * FRAG + xslot * 8;
+      for (int s = 0; s < KSH; ++s) {
+        const _Float16* f = buf + (kh * KSH + s) * FRAG + xslot * 8;
         const half8 x0 = *reinterpret_cast<const half8*>(f + 0 * PS);
         const half8 x2 = *reinterpret_cast<const half8*>(f + 1 * PS);
         const half8 xr = *reinterpret_cast<const half8*>(f + 2 * PS);
@@ -467,7 +488,7 @@ __device__ __forceinline__ void ws_body(
         const u32x4 lo = {o[0], o[1], o[2], o[3]}, hi = {o[4], o[5], o[6], o[7]};
         if (PST) {
           // row i16, work-group channels wave*16NB + 16nb + 4g .. + 3
-          _Float16* const sp = obuf + (i & 1) * OBUF + i16 * OPITCH + (wave * NB * 16 + nb * 16 + 4 * g) * 4;
+          _Float16* const sp = obuf + (i & 1) * OBUF + i16 * OPITCH + (cw * NB * 16 + nb * 16 + 4 * g) * 4;
           *reinterpret_cast<u32x4*>(sp) = lo;
           *reinterpret_cast<u32x4*>(sp + 8) = hi;
         } else {
@@ -531,7 +552,38 @@ __device__ __forceinline__ void ws_body(
       __syncthreads();  // barrier W
     }
     __syncthreads();  // barrier 0
-    if (PIPE) {
+    if constexpr (KSPLIT) {
+      // Between barriers i and i+1: the first half of each pair adds the
+      // second half's parked accumulators of tile i-1 to its own and runs
+      // that tile's epilogue (staged, stored by the producers one phase
+      // later), then both halves run the products of tile i over their
+      // steps, and the second half parks them (buffer i % 2).
+      Acc A;
+      f32x4* const pk = park + cw * 6 * 64 + lane;
+      auto add_parked = [&](int i) {
+        const f32x4* p = pk + (i & 1) * (NCB * 6 * 64);
+        A.c0[0] += p[0]; A.c2[0] += p[64]; A.cr[0] += p[128];
+        A.ci[0] += p[192]; A.cq[0] += p[256]; A.cn[0] += p[320];
+      };
+      for (int i = 0; i < n_my; ++i) {
+        if (kh == 0 && i > 0) {
+          add_parked(i - 1);
+          epilogue_any(i - 1, A);
+        }
+        products(A, xs + (i & 1) * BUF);
+        if (kh == 1) {
+          f32x4* p = pk + (i & 1) * (NCB * 6 * 64);
+          p[0] = A.c0[0]; p[64] = A.c2[0]; p[128] = A.cr[0];
+          p[192] = A.ci[0]; p[256] = A.cq[0]; p[320] = A.cn[0];
+        }
+        __syncthreads();  // barrier i+1
+      }
+      if (kh == 0) {
+        add_parked(n_my - 1);
+        epilogue_any(n_my - 1, A);
+      }
+      __syncthreads();  // barrier n_my + 1: the last tile is staged
+    } else if (PIPE) {
       // Software pipeline: between barriers i+1 and i+2 the products of tile
       // i+1 (buffer (i+1) % 2) are issued before the epilogue of tile i, so
       // the matrix cores work while the same wave runs the epilogue's VALU
@@ -593,11 +645,12 @@ __global__ __launch_bounds__((NC + NP) * 64) void k_fwd_ws_f16(
                                                                n_ct, Qx, act, wfirst);
 }
 
-template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE, bool SPLIT>
+template <int NC, int NP, int NB, int KS, int YP, bool G8, bool PST, bool PIPE, bool SPLIT,
+          bool KSPLIT = false>
 __global__ __launch_bounds__((NC + NP) * 64) void k_bwd_input_ws_f16(
     const _Float16* __restrict__ dy, const _Float16* __restrict__ spec, const float* __restrict__ bias,
     _Float16* __restrict__ dx, int N, int K, int n_out, int n_pad, int n_ct, int Qx, int wfirst) {
-  ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE, SPLIT>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct,
+  ws_body<NC, NP, NB, KS, YP, G8, true, PST, PIPE, SPLIT, false, KSPLIT>(dy, spec, bias, dx, N, K, n_out, n_pad, n_ct,
                                                           Qx, ACT_NONE, wfirst);
 }
 
@@ -703,6 +756,36 @@ static hipError_t launch_ws_t(const Tuning& tn, const void* x, const void* spec,
   return hipGetLastError();
 }
 
+// backward_input with split-reduction consumers: NC / 2 output blocks of 16
+// channels per work-group, two consumer waves per block over the halves of
+// the KS reduction steps, NP producer waves, producer-staged output.
+template <int NC, int NP, int KS>
+static hipError_t launch_bwi_ksplit(const Tuning& tn, const void* x, const void* spec, const float* bias,
+                                    void* y, int64_t N, int K, int n_out, int n_pad, hipStream_t s) {
+  constexpr int BN = NC / 2 * 16;
+  const int n_ct = (n_out + BN - 1) / BN;
+  if ((int64_t)n_ct * BN > n_pad) return hipErrorNotSupported;  // weight reads stay in the planes
+  const int64_t n_rt = (N + 15) / 16;
+  int qx = 256 / (8 * n_ct);
+  if (qx < 1) qx = 1;
+  const int64_t max_qx = (n_rt + 7) / 8;
+  if (qx > max_qx) qx = (int)(max_qx < 1 ? 1 : max_qx);
+  qx = pick(tn.ws_qx, qx);
+  const unsigned blocks = (unsigned)(8 * n_ct * qx);
+  const int wfirst = pick(tn.ws_wfirst, 0);
+  const bool small = N * (int64_t)n_out * 8 <= tn.ws_small_bytes;
+  const dim3 grid(blocks), block((NC + NP) * 64);
+  if (small)
+    hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, 1, KS, POLICY_THROUGH, true, true, false, false, true>), grid,
+                       block, 0, s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K,
+                       n_out, n_pad, n_ct, qx, wfirst);
+  else
+    hipLaunchKernelGGL((k_bwd_input_ws_f16<NC, NP, 1, KS, POLICY_STREAM, true, true, false, false, true>), grid,
+                       block, 0, s, (const _Float16*)x, (const _Float16*)spec, bias, (_Float16*)y, (int)N, K,
+                       n_out, n_pad, n_ct, qx, wfirst);
+  return hipGetLastError();
+}
+
 // hipErrorNotSupported when outside this kernel's limits.
 hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const void* spec,
                      const float* bias, void* y, int64_t N, int K, int k_pad, int n_out, int n_pad,
@@ -715,6 +798,11 @@ hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const
   if ((int64_t)n_pad * k_pad * 2 >= (1LL << 31) || (int64_t)16 * n_out * 8 >= (1LL << 31))
     return hipErrorNotSupported;
   const int ks = k_pad / 32;
+  // backward_input over 384 channels: split-reduction consumers (six
+  // producer waves instead of four; measured at 12608 x 384 -> 96, five
+  // alternating runs on one box: 15.0-16.0 against 15.3-16.9 us)
+  if (adjoint && ks == 12 && pick(tn.ws_ksplit, 1) == 1)
+    return launch_bwi_ksplit<6, 6, 12>(tn, x, spec, bias, y, N, K, n_out, n_pad, s);
   // measured on MI355X: 4 consumer waves of 32 channels for short reductions,
   // 8 consumer waves of 16 channels (fewer VGPRs per wave) up to 192
   // channels, and 4 consumer waves of 16 channels beyond (the weight

@@ -235,13 +235,14 @@ def test_forward_f32_paths(C, D, N, path, monkeypatch):
 # backward-input paths forced one at a time (binary16)
 BI_PATHS = {
     "ws": {},
+    "ws_no_ksplit": {"EQL_WS_KSPLIT": "0"},
     "tiled": {"EQL_NO_WS": "1"},
 }
 
 
 @pytest.mark.parametrize("path", sorted(BI_PATHS))
 @pytest.mark.parametrize("C,D,N", [(96, 384, 12608), (96, 384, 1001), (32, 256, 333), (100, 96, 777),
-                                   (64, 288, 65), (96, 384, 2063)])
+                                   (64, 288, 65), (96, 384, 2063), (48, 384, 17), (144, 384, 700)])
 def test_backward_input_paths(C, D, N, path, monkeypatch):
     for k, v in BI_PATHS[path].items():
         monkeypatch.setenv(k, v)
