@@ -487,7 +487,7 @@ __device__ __forceinline__ void ws_body(
         }
         const u32x4 lo = {o[0], o[1], o[2], o[3]}, hi = {o[4], o[5], o[6], o[7]};
         if (PST) {
-          // row i16, work-group channels wave*16NB + 16nb + 4g .. + 3
+          // row i16, work-group channels cw*16NB + 16nb + 4g .. + 3 (cw: the wave's block)
           _Float16* const sp = obuf + (i & 1) * OBUF + i16 * OPITCH + (cw * NB * 16 + nb * 16 + 4 * g) * 4;
           *reinterpret_cast<u32x4*>(sp) = lo;
           *reinterpret_cast<u32x4*>(sp + 8) = hi;
