@@ -798,19 +798,23 @@ hipError_t launch_ws(const Tuning& tn, eqlinear_dtype_t dt, const void* x, const
   if ((int64_t)n_pad * k_pad * 2 >= (1LL << 31) || (int64_t)16 * n_out * 8 >= (1LL << 31))
     return hipErrorNotSupported;
   const int ks = k_pad / 32;
-  // backward_input over 384 channels: split-reduction consumers (six
-  // producer waves instead of four; measured at 12608 x 384 -> 96, five
-  // alternating runs on one box: 15.0-16.0 against 15.3-16.9 us)
-  if (adjoint && ks == 12 && pick(tn.ws_ksplit, 1) == 1)
-    return launch_bwi_ksplit<6, 6, 12>(tn, x, spec, bias, y, N, K, n_out, n_pad, s);
+  // long reductions: 3 or 4 consumer waves, whichever pads the output
+  // channels less (ties go to 4)
+  const int pad3 = (n_out + 47) / 48 * 48 - n_out, pad4 = (n_out + 63) / 64 * 64 - n_out;
+  // backward_input over 384 channels where 48-channel work-groups pad the
+  // output least: split-reduction consumers (six producer waves instead of
+  // four; measured at 12608 x 384 -> 96, five alternating runs on one box:
+  // 15.0-16.0 against 15.3-16.9 us); shapes it does not take run the
+  // organisation below
+  if (adjoint && ks == 12 && pad3 < pad4 && pick(tn.ws_ksplit, 1) == 1) {
+    const hipError_t e = launch_bwi_ksplit<6, 6, 12>(tn, x, spec, bias, y, N, K, n_out, n_pad, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   // measured on MI355X: 4 consumer waves of 32 channels for short reductions,
   // 8 consumer waves of 16 channels (fewer VGPRs per wave) up to 192
   // channels, and 4 consumer waves of 16 channels beyond (the weight
   // fragments of a wave grow with the reduction width)
   const bool wide = ks <= 3, deep = ks > 6;
-  // long reductions: 3 or 4 consumer waves, whichever pads the output
-  // channels less (ties go to 4)
-  const int pad3 = (n_out + 47) / 48 * 48 - n_out, pad4 = (n_out + 63) / 64 * 64 - n_out;
   // with a fused activation the epilogue carries most of the consumers' work:
   // short reductions then take 8 consumer waves of 16 channels (measured at
   // C = 96, D = 384 with GELU: 26.6 us against 37.6 us with 4 waves of 32)

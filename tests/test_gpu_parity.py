@@ -242,7 +242,8 @@ BI_PATHS = {
 
 @pytest.mark.parametrize("path", sorted(BI_PATHS))
 @pytest.mark.parametrize("C,D,N", [(96, 384, 12608), (96, 384, 1001), (32, 256, 333), (100, 96, 777),
-                                   (64, 288, 65), (96, 384, 2063), (48, 384, 17), (144, 384, 700)])
+                                   (64, 288, 65), (96, 384, 2063), (48, 384, 17), (144, 384, 700),
+                                   (100, 384, 300)])
 def test_backward_input_paths(C, D, N, path, monkeypatch):
     for k, v in BI_PATHS[path].items():
         monkeypatch.setenv(k, v)
